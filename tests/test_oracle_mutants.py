@@ -1,0 +1,82 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pins catch every one of them.
+
+Each mutant is the oracle's own source with one textual change, executed as a
+fresh module; the pins of test_oracle are then run against it and at least one
+must fail.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle.attention as attn_mod
+import test_oracle as pins
+
+MUTANTS = {
+    "online_drops_rescale_of_u": ("u = a[:, None] * u + p @ v[b, hk, start:stop]",
+                                  "u = u + p @ v[b, hk, start:stop]"),
+    "online_drops_rescale_of_l": ("l = a * l + p.sum(axis=1)", "l = l + p.sum(axis=1)"),
+    "online_forgets_final_division": ("o[b, h, ok] = u[ok] / l[ok, None]", "o[b, h, ok] = u[ok]"),
+    "forward_mask_not_applied": ("            s = np.where(vis, s, -np.inf)\n            m = s.max(axis=1, initial=-np.inf)          # row max",
+                                 "            m = s.max(axis=1, initial=-np.inf)          # row max"),
+    "forward_lse_without_log": ("            lse[b, h, ok] = m[ok] + np.log(l[ok])\n    return o, lse\n\n\ndef attention_backward",
+                                "            lse[b, h, ok] = m[ok] + l[ok]\n    return o, lse\n\n\ndef attention_backward"),
+    "bottom_right_offset_sign": ("(i[:, None] + (Sk - Sq))", "(i[:, None] + (Sq - Sk))"),
+    "top_left_strict_inequality": ("return j[None, :] <= i[:, None]", "return j[None, :] < i[:, None]"),
+    "gqa_interleaved_heads": ("            hk = h // g\n            s = c * (q[b, h] @ k[b, hk].T)              # [n, Sk]",
+                              "            hk = h % Hkv\n            s = c * (q[b, h] @ k[b, hk].T)              # [n, Sk]"),
+    "backward_jacobian_sign": ("ds = p * (dp - D[:, None])", "ds = p * (dp + D[:, None])"),
+    "backward_dq_missing_scale": ("dq[b, h] = c * (ds @ k[b, hk])", "dq[b, h] = ds @ k[b, hk]"),
+    "backward_dk_transposed_operand": ("dk[b, hk] += c * (ds.T @ q[b, h])", "dk[b, hk] += c * (p.T @ q[b, h])"),
+    "backward_dv_drops_probabilities": ("dv[b, hk] += p.T @ do[b, h]", "dv[b, hk] += vis.T @ do[b, h]"),
+    "merge_wrong_weight": ("wb[live] = np.exp(lse_b[live] - M[live])", "wb[live] = np.exp(lse_a[live] - M[live])"),
+}
+
+# (pin function, kwargs) pairs run against each mutant
+PIN_CALLS = [
+    (pins.test_worked_example_states_and_output, {}),
+    (pins.test_tile_invariance, {"causal": 1, "tile": 3}),
+    (pins.test_tile_invariance, {"causal": 2, "tile": 8}),
+    (pins.test_single_visible_key, {"causal": 1}),
+    (pins.test_zero_keys_give_mean_of_visible_values, {"causal": 2}),
+    (pins.test_forward_matches_torch_sdpa_fp64, {"causal": 1, "gqa": True}),
+    (pins.test_forward_matches_torch_sdpa_fp64, {"causal": 2, "gqa": False}),
+    (pins.test_fully_masked_rows_strict_and_defined, {}),
+    (pins.test_merge_states_equals_single_pass, {}),
+    (pins.test_central_differences_masked_2x3x2, {}),
+    (pins.test_backward_matches_torch_autograd_fp64, {"causal": 1, "shape": (2, 4, 2, 5, 9, 8)}),
+]
+
+_NAMES = ["attention_forward", "attention_backward", "online_softmax_forward",
+          "merge_states", "visible_mask", "FullyMaskedRowError"]
+
+
+def _mutant_module(old, new):
+    src = inspect.getsource(attn_mod)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "<oracle_mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    mod = _mutant_module(*MUTANTS[name])
+    for n in _NAMES:
+        monkeypatch.setattr(pins, n, getattr(mod, n))
+    failures = 0
+    for fn, kw in PIN_CALLS:
+        try:
+            fn(**kw)
+        except (Exception, pytest.fail.Exception):   # an assertion, pytest.raises, or a crash
+            failures += 1
+    assert failures > 0, f"no pin caught mutant {name}"
+
+
+def test_unmutated_copy_passes_all_pins(monkeypatch):
+    mod = _mutant_module("import math", "import math")
+    for n in _NAMES:
+        monkeypatch.setattr(pins, n, getattr(mod, n))
+    for fn, kw in PIN_CALLS:
+        fn(**kw)
