@@ -1,0 +1,187 @@
+"""Exact IO-aware attention for MI355X (gfx950): Python binding of libattn.so.
+
+This module only marshals arguments: it passes device pointers of PyTorch
+tensors and the current HIP stream to the C ABI declared in
+``include/attn.h``. Every step of the computation runs in the library's HIP
+kernels. If the library has not been built, every call raises; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "ATTN_F32", "ATTN_BF16", "AttnError", "lib", "library_path", "fwd", "bwd",
+    "fwd_workspace_bytes", "bwd_workspace_bytes", "strerror", "last_dispatch",
+]
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn.so")
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+_SHAPE = [_I] * 7                      # B, Hq, Hkv, Sq, Sk, d, causal
+
+
+class AttnError(RuntimeError):
+    """A negative status returned by the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m exact_io_aware_38_amd.build` "
+                "(the HIP library is required; there is no fallback)")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.attn_fwd_workspace_bytes.argtypes = _SHAPE + [_I]
+        L.attn_fwd_workspace_bytes.restype = _Z
+        L.attn_bwd_workspace_bytes.argtypes = _SHAPE + [_I]
+        L.attn_bwd_workspace_bytes.restype = _Z
+        L.attn_fwd.argtypes = [_P, _P, _P, _P, _P] + _SHAPE + [_F, _I, _P, _Z, _P]
+        L.attn_fwd.restype = _I
+        L.attn_bwd.argtypes = [_P] * 9 + _SHAPE + [_F, _I, _P, _Z, _P]
+        L.attn_bwd.restype = _I
+        L.attn_strerror.argtypes = [_I]
+        L.attn_strerror.restype = ctypes.c_char_p
+        L.attn_last_dispatch.argtypes = [ctypes.c_char_p, _Z]
+        L.attn_last_dispatch.restype = _I
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().attn_strerror(int(status)).decode()
+
+
+def last_dispatch() -> str:
+    """What the calling thread's last successful call launched."""
+    n = lib().attn_last_dispatch(None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().attn_last_dispatch(buf, n + 1)
+    return buf.value.decode()
+
+
+def fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype) -> int:
+    return int(lib().attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype))
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name: str):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _want(t, shape, dtype, name: str):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must have shape {tuple(shape)} and dtype {dtype}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def fwd(q, k, v, *, causal: int = 0, scale: Optional[float] = None, out=None, lse=None,
+        need_lse: bool = True, workspace=None, stream=None) -> Tuple["object", "object"]:
+    """O (and lse) for q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] on the GPU.
+
+    Returns (o, lse); lse is None when ``need_lse`` is False and no buffer was
+    given. ``causal``: 0 none, 1 top-left, 2 bottom-right.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse"), (workspace, "workspace")):
+        _check(t, n)
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    dt = _dtype_code(q)
+    _want(k, (B, Hkv, Sk, d), q.dtype, "k")
+    _want(v, (B, Hkv, Sk, d), q.dtype, "v")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Sq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and need_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    ws_n = fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dt)
+    if workspace is None and ws_n > 0:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                        causal, sc, dt, _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: int = 0, scale: Optional[float] = None, dq=None, dk=None,
+        dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) for the forward that produced o and lse (bf16 only)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace")):
+        _check(t, n)
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    dt = _dtype_code(q)
+    for t, n, shp in ((k, "k", k.shape), (v, "v", k.shape), (o, "o", q.shape), (dout, "dout", q.shape),
+                      (dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        _want(t, shp, q.dtype, n)
+    _want(v, (B, Hkv, Sk, d), q.dtype, "v")
+    _want(lse, (B, Hq, Sq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_n = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dt)
+    if workspace is None and ws_n > 0:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                        _ptr(dv), B, Hq, Hkv, Sq, Sk, d, causal, sc, dt, _ptr(workspace), ws_bytes,
+                        _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,84 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Lane layouts used throughout (checked on the hardware with an in-bounds
+// probe of the builtins):
+//  * v_mfma_f32_32x32x16_bf16: A operand lane l holds row (l % 32) and the 8
+//    reduction slots 8*(l/32) .. 8*(l/32)+7; B operand lane l holds column
+//    (l % 32) and the same 8 slots; accumulator register i of lane l holds
+//    row 8*(i/4) + 4*(l/32) + (i%4), column (l % 32).
+//  * ds_read_b64_tr_b16: within each 16-lane group, lane L supplies the
+//    address of 4 consecutive 16-bit elements of row r0 + L/4, columns
+//    c0 + 4*(L%4) .. +3 of a row-major LDS matrix; lane j of the group then
+//    receives the 4 elements of rows r0 .. r0+3 in column c0 + j.
+//  * permlane32_swap(x, x) returns {x[l % 32], x[l % 32 + 32]} in every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit; 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max of x over lanes l and l^32.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum of x over lanes l and l^32.
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Transposed 8-byte LDS read (see the layout note at the top of this file).
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round-to-nearest-even float -> bf16 of 8 values.
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
+                                            float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+  return r;
+}
+
+// Workgroup order: the hardware hands consecutive workgroup ids to the 8 XCDs
+// in turn, each with its own L2. Renumber so that each XCD receives a
+// contiguous range of logical ids, i.e. all tiles of a few heads, which then
+// share K/V lines in that XCD's L2.
+__device__ __forceinline__ int xcd_logical_id(int linear, int total) {
+  if ((total & 7) != 0) return linear;
+  return (linear & 7) * (total >> 3) + (linear >> 3);
+}
+
+}  // namespace attn

@@ -1,0 +1,116 @@
+/*
+ * attn.h -- C ABI of the exact IO-aware attention library for MI355X (gfx950).
+ *
+ * What it computes. For every batch b, query head h (KV head h / (Hq/Hkv)),
+ * query row i and key j:
+ *     s_ij  = scale * q_i . k_j                      (masked keys: s_ij = -inf)
+ *     O_i   = sum_j softmax_j(s_i.) v_j,   lse_i = ln sum_j exp(s_ij)
+ * exactly as the plain definition (Attention = softmax(QK^T/sqrt(d_k))V of
+ * "Flash Attention FA1->FA4 / pre-training practice", §1.1), but computed
+ * tile by tile with the online-softmax recurrence of the same page, §1.2, in
+ * the unnormalised (m, l, u) form of "AI 大模型之 FlashAttention_01",
+ * §4.1 and section "瓦片状态如何保持精确语义". The score matrix never
+ * reaches device memory; the forward keeps only O and the per-row lse, and
+ * the backward rebuilds the probabilities tile by tile from them (same page,
+ * section "反向传播为什么可以重算").
+ *
+ * Layout. Every tensor is contiguous, row-major [B, H, S, d]:
+ *   q, o, dout, dq : [B, Hq,  Sq, d]      k, v, dk, dv : [B, Hkv, Sk, d]
+ *   lse            : [B, Hq,  Sq] float32, natural log
+ * Element type is given by `dtype` (ATTN_F32 or ATTN_BF16) for q, k, v, o,
+ * dout, dq, dk, dv; lse is always float32. All pointers are device pointers
+ * (memory from hipMalloc or a PyTorch CUDA/HIP tensor) except `buf` of
+ * attn_last_dispatch, which is host memory.
+ *
+ * Masks (`causal`): 0 = none; 1 = top-left, key j visible to query i iff
+ * j <= i; 2 = bottom-right, j <= i + Sk - Sq. The two coincide when Sq == Sk.
+ * A query row that sees no key (Sk == 0, or causal == 2 with i < Sq - Sk)
+ * gets O = 0, lse = -inf, dq = 0, and adds nothing to dk or dv. This is the
+ * explicit rule for fully masked rows that "AI 大模型之 FlashAttention_01"
+ * (section "工程实操") asks an interface to define.
+ *
+ * Restrictions (the kernels are specialised, as that page's limitations
+ * section notes for high-performance attention kernels): d in {64, 128};
+ * Hq a multiple of Hkv (grouped heads are contiguous); scale finite and > 0;
+ * backward in ATTN_BF16 only; gfx950 only.
+ *
+ * Ownership and errors. The caller allocates every buffer, including the
+ * workspace (size from the *_workspace_bytes queries); the library allocates
+ * no device memory and keeps no pointer after a call returns. Arguments are
+ * validated on the host before anything is launched: on error the function
+ * returns a negative status, launches nothing and leaves every output
+ * untouched. Work is enqueued asynchronously on `stream` (a hipStream_t; NULL
+ * means the default stream); the library never synchronises, so a device
+ * fault surfaces at the caller's next synchronisation. A failed launch returns
+ * ATTN_ERR_HIP. No C++ exception crosses this interface. Calls may come from
+ * several host threads; the dispatch record is per thread.
+ */
+#ifndef EXACT_ATTN_MI355X_H
+#define EXACT_ATTN_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,       /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,      /* B, Hq, Hkv, Sq < 1, or Sk < 0, or a size overflows */
+  ATTN_ERR_GQA = -3,        /* Hq is not a multiple of Hkv */
+  ATTN_ERR_HEADDIM = -4,    /* d not in {64, 128} */
+  ATTN_ERR_DTYPE = -5,      /* unknown dtype, or not supported by this entry point */
+  ATTN_ERR_CAUSAL = -6,     /* causal not in {0, 1, 2} */
+  ATTN_ERR_WORKSPACE = -7,  /* workspace smaller than the query says, or NULL when needed */
+  ATTN_ERR_HIP = -8,        /* a HIP runtime call or kernel launch failed */
+  ATTN_ERR_SCALE = -9       /* scale not finite or not > 0 */
+};
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Bytes of device workspace attn_fwd needs for these arguments (0 if none).
+ * The split-key decode path (few query rows per KV head, e.g. Sq = 1) keeps
+ * per-split partial results there. Returns 0 for invalid arguments too; the
+ * call itself then reports the error. */
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                                int causal, int dtype);
+
+/* Forward: o (and lse, if non-NULL) from q, k, v. lse may be NULL when no
+ * backward follows (inference keeps no state). k and v may be NULL only when
+ * Sk == 0. workspace may be NULL only if attn_fwd_workspace_bytes returns 0. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace attn_bwd needs (the per-row term D_i = dO_i . O_i,
+ * float32 [B, Hq, Sq]). */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                                int causal, int dtype);
+
+/* Backward of the forward above, given its o and lse and the upstream
+ * gradient dout (all required). Writes dq, dk, dv (dk/dv summed over the query
+ * heads that share a KV head). Must be called with the same mask, scale and
+ * shapes as the forward that produced o and lse. k, v, dk and dv may be NULL
+ * only when Sk == 0 (then dq = 0). ATTN_BF16 only. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* Copies into buf (host memory, n bytes, NUL-terminated) a description of
+ * the kernels the calling thread's last successful attn_fwd/attn_bwd
+ * launched: kernel names, grid and tile shapes. Returns the full length of
+ * the description (like snprintf), or a negative status if buf is NULL with
+ * n > 0. When the environment variable ATTN_LOG is set to 1 the same line is
+ * also printed to stderr on every call. */
+int attn_last_dispatch(char* buf, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_MI355X_H */

@@ -1,0 +1,109 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects invalid arguments before touching any device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_38_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+FAKE = 0x1000          # non-NULL pointer value that is never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = attn.lib()
+    names = _declared()
+    assert {"attn_fwd", "attn_bwd", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes",
+            "attn_strerror", "attn_last_dispatch"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libattn.so does not export {n}"
+
+
+def test_strerror_covers_every_status():
+    codes = {0: "success", -1: "NULL", -2: "shape", -3: "multiple", -4: "head dim", -5: "dtype",
+             -6: "causal", -7: "workspace", -8: "HIP", -9: "scale"}
+    for c, word in codes.items():
+        assert word.lower() in attn.strerror(c).lower()
+    assert "unknown" in attn.strerror(-99)
+
+
+def _fwd(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=16, Sk=16, d=64,
+             causal=0, scale=0.125, dtype=attn.ATTN_BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return attn.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                               a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["dtype"], a["ws"],
+                               a["ws_bytes"], a["stream"])
+
+
+def _bwd(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4,
+             Hkv=2, Sq=16, Sk=16, d=64, causal=0, scale=0.125, dtype=attn.ATTN_BF16, ws=None,
+             ws_bytes=0, stream=None)
+    a.update(over)
+    return attn.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                               a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["causal"],
+                               a["scale"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, -1), ({"k": None}, -1), ({"v": None}, -1), ({"o": None}, -1),
+    ({"B": 0}, -2), ({"Hq": 0}, -2), ({"Hkv": 0}, -2), ({"Sq": 0}, -2), ({"Sk": -1}, -2),
+    ({"B": 1 << 20, "Hq": 1 << 10, "Hkv": 1 << 10}, -2),
+    ({"Hq": 6, "Hkv": 4}, -3), ({"d": 96}, -4), ({"d": 256}, -4), ({"dtype": 7}, -5),
+    ({"causal": 3}, -6), ({"causal": -1}, -6), ({"scale": 0.0}, -9), ({"scale": -1.0}, -9),
+    ({"scale": float("nan")}, -9), ({"scale": float("inf")}, -9),
+    # decode shape needs a workspace for the per-split partials
+    ({"Sq": 1, "Sk": 4096}, -7),
+])
+def test_fwd_validation(over, code):
+    assert _fwd(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"lse": None}, -1), ({"do": None}, -1), ({"dq": None}, -1), ({"dk": None}, -1), ({"dv": None}, -1),
+    ({"o": None}, -1), ({"Sq": 0}, -2), ({"Hq": 3, "Hkv": 2}, -3), ({"d": 32}, -4),
+    ({"dtype": attn.ATTN_F32}, -5), ({"causal": 5}, -6), ({"scale": 0.0}, -9),
+    ({}, -7),                                   # no workspace
+    ({"ws": FAKE, "ws_bytes": 8}, -7),          # too small
+])
+def test_bwd_validation(over, code):
+    assert _bwd(**over) == code
+
+
+def test_workspace_queries():
+    # prefill needs none; decode (4 query rows per KV head) needs the split partials
+    assert attn.fwd_workspace_bytes(2, 32, 32, 8192, 8192, 128, 1, attn.ATTN_BF16) == 0
+    n = attn.fwd_workspace_bytes(16, 32, 8, 1, 32768, 128, 0, attn.ATTN_BF16)
+    assert n >= 16 * 32 * 129 * 4
+    assert attn.fwd_workspace_bytes(1, 1, 1, 1, 100, 64, 0, attn.ATTN_F32) == 0
+    assert attn.fwd_workspace_bytes(0, 1, 1, 1, 1, 64, 0, attn.ATTN_BF16) == 0     # invalid -> 0
+    rows = 1 * 32 * 8192
+    assert attn.bwd_workspace_bytes(1, 32, 32, 8192, 8192, 128, 1, attn.ATTN_BF16) >= 2 * 4 * rows
+    assert attn.bwd_workspace_bytes(1, 32, 32, 8192, 8192, 128, 1, attn.ATTN_F32) == 0
+
+
+def test_dispatch_record_is_empty_before_any_call():
+    import threading
+    out = {}
+    th = threading.Thread(target=lambda: out.setdefault("d", attn.last_dispatch()))
+    th.start()
+    th.join()
+    assert out["d"] == ""
+    assert attn.lib().attn_last_dispatch(None, 8) == -1
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(attn, "_lib", None)
+    monkeypatch.setattr(attn, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        attn.lib()

@@ -1,0 +1,223 @@
+"""Forward parity on the GPU: the HIP path (through the C ABI) against the
+FP64 oracle on the same seeded inputs."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import check_lse, check_o, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def attn():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_38_amd as m
+    m.lib()
+    return m
+
+
+def _inputs(w):
+    x = synth.make_inputs(w)
+    dev = {n: to_device(x[n], w.dtype) for n in ("q", "k", "v")}
+    f64 = {n: synth.to_f64(x[n], w.dtype) for n in ("q", "k", "v")}
+    return x, dev, f64
+
+
+def _run(attn, w, dev):
+    import torch
+    o, lse = attn.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return to_host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+SMALL = [
+    # B, Hq, Hkv, Sq, Sk, d, causal          several tiles with ragged tails
+    (1, 2, 2, 300, 300, 64, 0),
+    (1, 2, 2, 300, 300, 64, 1),
+    (2, 4, 2, 257, 333, 128, 2),
+    (2, 8, 2, 200, 77, 128, 2),      # Sq > Sk, bottom-right: first 123 rows see no key
+    (1, 4, 1, 130, 520, 128, 1),     # top-left with Sk > Sq: keys >= 130 are never visible
+    (1, 6, 2, 100, 100, 64, 0),      # 3 query heads per KV head
+    (1, 2, 1, 17, 50, 128, 1),       # 2 query heads per KV head, one partial tile
+    (1, 8, 8, 64, 64, 128, 0),       # exactly one tile
+]
+SPLIT = [
+    (2, 8, 2, 1, 1000, 128, 0),      # decode: 4 query heads per KV head, one row each
+    (1, 4, 4, 3, 700, 64, 2),        # 3 rows per head, bottom-right mask
+    (1, 32, 1, 1, 5000, 128, 0),     # 32 query heads share one KV head
+    (3, 2, 1, 16, 2049, 64, 1),      # 32 packed rows, top-left mask
+    (1, 4, 1, 2, 64, 128, 0),        # a single key tile
+]
+
+
+@pytest.mark.parametrize("shape", SMALL + SPLIT, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_small_all_outputs(attn, shape):
+    B, Hq, Hkv, Sq, Sk, d, causal = shape
+    w = synth.Workload("small", B, Hq, Hkv, Sq, Sk, d, "bf16", causal, seed=1000 + sum(shape))
+    _say("case", shape)
+    x, dev, f = _inputs(w)
+    o, lse = _run(attn, w, dev)
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal=causal, scale=w.scale)
+    check_o(o, o_ref, "bf16")
+    check_lse(lse, lse_ref)
+    is_split = Hq // Hkv * Sq <= 32
+    assert ("fwd_split_bf16" in attn.last_dispatch()) == is_split
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1, 2])
+def test_f32_small_all_outputs(attn, d, causal):
+    w = synth.Workload("small_f32", 2, 4, 2, 150, 190, d, "f32", causal, seed=77 + d + causal)
+    x, dev, f = _inputs(w)
+    o, lse = _run(attn, w, dev)
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal=causal, scale=w.scale)
+    check_o(o, o_ref, "f32")
+    check_lse(lse, lse_ref, tol=1e-5)
+    assert "fwd_f32" in attn.last_dispatch()
+
+
+def test_single_head_f32_workload(attn):
+    w = synth.get_workload("single_head_f32")
+    x, dev, f = _inputs(w)
+    o, lse = _run(attn, w, dev)
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal=0, scale=w.scale)
+    err = check_o(o, o_ref, "f32")
+    check_lse(lse, lse_ref, tol=1e-5)
+    _say(f"single_head_f32 max abs err {err:.3e}")
+
+
+def test_worked_example_embedded_f32(attn):
+    """Scores 1000, 1001, 999 with values 1, 3, 7 (the worked example of the
+    large-score section): one query, three keys, head dim 64, scale 1."""
+    import json
+    import os
+    import torch
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json"),
+                       encoding="utf-8"))
+    d = 64
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, 3, d), np.float32)
+    v = np.zeros((1, 1, 3, d), np.float32)
+    k[0, 0, :, 0] = g["scores"]
+    v[0, 0, :, 0] = g["values"]
+    o, lse = attn.fwd(to_device(q, "f32"), to_device(k, "f32"), to_device(v, "f32"), causal=0, scale=1.0)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    assert abs(o[0, 0, 0, 0] - g["output"]) <= 1e-5
+    assert (o[0, 0, 0, 1:] == 0).all()
+    assert abs(lse.item() - 1001.4076059644) <= 1e-3
+
+
+def _sample_rows(rng, Sq, extra=()):
+    base = {0, 1, 63, 64, 127, 128, 255, 256, Sq // 2, Sq - 2, Sq - 1}
+    base |= set(int(r) for r in rng.choice(Sq, size=min(Sq, 24), replace=False))
+    base |= set(int(r) for r in extra)
+    return np.array(sorted(r for r in base if 0 <= r < Sq))
+
+
+FULL = ["multihead_d64", "multihead_d64_causal", "multihead_d64_ragged", "multihead_d64_ragged_causal",
+        "long_causal_d128", "gqa_prefill", "gqa_decode"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads_sampled(attn, name):
+    """Full-size run in the benchmark's launch configuration; the oracle checks
+    sampled rows of every head (plus all outlier rows) one by one."""
+    import torch
+    w = synth.get_workload(name)
+    _say("workload", name)
+    x = synth.make_inputs(w)
+    dev = {n: to_device(x[n], w.dtype) for n in ("q", "k", "v")}
+    o_t, lse_t = attn.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o = o_t.float().cpu().numpy()
+    lse = lse_t.cpu().numpy()
+    assert np.isfinite(o).all(), "non-finite output"
+    assert not np.isnan(lse).any() and not np.isposinf(lse).any()
+    del o_t, dev
+    rng = np.random.default_rng(5)
+    g = w.Hq // w.Hkv
+    kf = synth.to_f64(x["k"], w.dtype)
+    vf = synth.to_f64(x["v"], w.dtype)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            extra = x["outlier_rows"][b, h] if "outlier_rows" in x else ()
+            rows = _sample_rows(rng, w.Sq, extra)
+            qf = synth.to_f64(x["q"][b:b + 1, h:h + 1, rows], w.dtype)
+            hk = h // g
+            o_ref, lse_ref = oracle.attention_forward(qf, kf[b:b + 1, hk:hk + 1], vf[b:b + 1, hk:hk + 1],
+                                                      causal=w.causal, scale=w.scale, rows=rows, Sq=w.Sq)
+            check_o(o[b, h, rows][None, None].astype(np.float64), o_ref, "bf16", what=f"O[{b},{h}]")
+            check_lse(lse[b, h, rows][None, None].astype(np.float64), lse_ref)
+
+
+def test_forward_is_deterministic(attn):
+    import torch
+    w = synth.Workload("det", 1, 8, 2, 700, 900, 128, "bf16", 1, seed=3)
+    x, dev, _ = _inputs(w)
+    o1, l1 = attn.fwd(dev["q"], dev["k"], dev["v"], causal=1)
+    o2, l2 = attn.fwd(dev["q"], dev["k"], dev["v"], causal=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_batched_equals_single_head_runs(attn):
+    import torch
+    w = synth.Workload("batch", 2, 4, 2, 190, 260, 64, "bf16", 2, seed=9)
+    x, dev, _ = _inputs(w)
+    o, lse = attn.fwd(dev["q"], dev["k"], dev["v"], causal=2)
+    for b in range(2):
+        for h in range(4):
+            q1 = dev["q"][b:b + 1, h:h + 1].contiguous()
+            k1 = dev["k"][b:b + 1, h // 2:h // 2 + 1].contiguous()
+            v1 = dev["v"][b:b + 1, h // 2:h // 2 + 1].contiguous()
+            o1, l1 = attn.fwd(q1, k1, v1, causal=2)
+            torch.cuda.synchronize()
+            assert torch.equal(o1[0, 0], o[b, h]) and torch.equal(l1[0, 0], lse[b, h])
+
+
+def test_no_keys_and_fully_masked_rows(attn):
+    import torch
+    # Sk = 0: every row is empty
+    for Sq in (1, 100):
+        q = torch.randn(1, 4, Sq, 128, device="cuda").to(torch.bfloat16)
+        kv = torch.empty(1, 2, 0, 128, device="cuda", dtype=torch.bfloat16)
+        o, lse = attn.fwd(q, kv, kv, causal=0)
+        torch.cuda.synchronize()
+        assert (o.float() == 0).all() and torch.isneginf(lse).all()
+    # bottom-right with Sq > Sk: rows i < Sq - Sk see nothing
+    w = synth.Workload("masked", 1, 2, 2, 160, 40, 64, "bf16", 2, seed=4)
+    x, dev, f = _inputs(w)
+    o, lse = _run(attn, w, dev)
+    assert (o[:, :, :120] == 0).all() and np.isneginf(lse[:, :, :120]).all()
+    assert np.isfinite(lse[:, :, 120:]).all()
+
+
+def test_single_visible_key_is_exact(attn):
+    w = synth.Workload("one_key", 1, 2, 2, 70, 70, 128, "bf16", 1, seed=6)
+    x, dev, f = _inputs(w)
+    o, lse = _run(attn, w, dev)
+    assert np.array_equal(o[:, :, 0], f["v"][:, :, 0])       # row 0 sees only key 0: P = 1 exactly
+    s00 = w.scale * (f["q"][:, :, 0] * f["k"][:, :, 0]).sum(-1)
+    assert np.abs(lse[:, :, 0] - s00).max() <= 1e-3
+
+
+def test_bf16_output_bounds_invariant(attn):
+    w = synth.Workload("bounds", 1, 4, 4, 512, 512, 128, "bf16", 0, seed=8)
+    x, dev, f = _inputs(w)
+    o, _ = _run(attn, w, dev)
+    vmin = f["v"].min(axis=2, keepdims=True)
+    vmax = f["v"].max(axis=2, keepdims=True)
+    assert (o >= vmin - 1e-2).all() and (o <= vmax + 1e-2).all()
