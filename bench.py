@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step is one pass of the whole training path over one batch of synthetic
+input: attn_fwd then attn_bwd on B=1, H=32, S=8192, d=128, causal, bf16 (the
+training workload). The same run also times the long-context causal forward
+(B=2, H=32, S=8192, d=128, 1% of query rows x30) and the grouped-query decode
+(B=16, Hq=32, Hkv=8, one query row against 32768 keys), which report as their
+own sub-objects. Inputs are resident in device memory before timing starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration          (a plain copy of known size,
+                                                    for counter calibration)
+       python bench.py --summarize-counters DIR    (turn rocprofv3 --pmc output
+                                                    into profiles/ summaries)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s fwd & fwd+bwd, bf16 d=128 causal S=8K; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+CSRC = os.path.join(ROOT, "exact_io_aware_38_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# kernel name -> source files whose content defines it (for counter staleness)
+KERNEL_SOURCES = {
+    "fwd_prefill_bf16": ["fwd_bf16.hip", "common.h"],
+    "fwd_split_bf16": ["fwd_bf16.hip", "common.h"],
+    "bwd_dkdv": ["bwd_bf16.hip", "common.h"],
+    "bwd_dq": ["bwd_bf16.hip", "common.h"],
+    "bwd_pre": ["bwd_bf16.hip"],
+}
+# substrings of the mangled device symbols, as rocprofv3 reports them
+KERNEL_SYMBOLS = {
+    "fwd_prefill_bf16": "fwd_bf16_kernelILi128ELi4ELi2ELb0E",
+    "fwd_split_bf16": "fwd_bf16_kernelILi128ELi1ELi1ELb1E",
+    "bwd_dkdv": "bwd_dkdv_kernelILi128E",
+    "bwd_dq": "bwd_dq_kernelILi128E",
+    "bwd_pre": "bwd_pre_kernelILi128E",
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def nominal_fwd_flops(B, Hq, Sq, Sk, d, causal) -> float:
+    f = 4.0 * B * Hq * Sq * Sk * d
+    return f / 2 if causal else f
+
+
+def kernel_work(kernel: str, w) -> dict:
+    """Algorithmic work one launch of `kernel` does on workload w.
+
+    Forward: 4*d FLOP per visible (query, key) pair, causal counted as half of
+    the pairs. Backward: 10*d per pair over five GEMMs (S recompute, dV, dP, dK,
+    dQ); the dK/dV kernel does four of them (8*d), the dQ kernel is credited
+    only with dQ (2*d) since its S and dP are a second recomputation. Decode
+    and the preprocess pass are bound by bytes: each tensor crosses HBM once.
+    """
+    fwd = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
+    e = 2  # bf16 bytes
+    if kernel == "fwd_prefill_bf16":
+        return {"bound": "mfma", "flops": fwd}
+    if kernel == "bwd_dkdv":
+        return {"bound": "mfma", "flops": 2.0 * fwd}
+    if kernel == "bwd_dq":
+        return {"bound": "mfma", "flops": 0.5 * fwd}
+    if kernel == "bwd_pre":
+        rows = w.B * w.Hq * w.Sq
+        return {"bound": "hbm", "bytes": 2.0 * rows * w.d * e + 3.0 * rows * 4}
+    if kernel == "fwd_split_bf16":
+        kv = 2.0 * w.B * w.Hkv * w.Sk * w.d * e
+        return {"bound": "hbm", "bytes": kv + w.B * w.Hq * w.Sq * w.d * e}
+    if kernel == "combine_split":
+        return {"bound": "hbm", "bytes": w.B * w.Hq * w.Sq * (w.d * e + 4)}
+    return {"bound": "mfma", "flops": 0.0}
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from stored counters, or None if absent or stale."""
+    path = os.path.join(PROFILES, f"counters_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_sha") != source_hash(kernel):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def roofline(kernel: str, w, avg_ms: float) -> dict:
+    work = kernel_work(kernel, w)
+    if work["bound"] == "mfma":
+        ach = work["flops"] / (avg_ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        ach = work["bytes"] / (avg_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    return {"kernel": kernel, "bound": work["bound"], "achieved": round(ach, 2), "peak": peak,
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic_for(kernel),
+            "avg_launch_ms": round(avg_ms, 4)}
+
+
+def _device_inputs(w):
+    import numpy as np
+    import torch
+    import synth
+    x = synth.make_inputs(w)
+    out = {}
+    for n in ("q", "k", "v", "do"):
+        if n in x:
+            out[n] = torch.from_numpy(x[n].view(np.int16)).cuda().view(torch.bfloat16)
+    del x
+    return out
+
+
+def _time(fn, steps: int, warmup: int, attn):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    attn.timing_start()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    kern = attn.timing_stop()
+    ms = start.elapsed_time(end) / steps
+    return ms, {k: v[1] / v[0] for k, v in kern.items()}
+
+
+def bench_step(attn, steps, warmup):
+    import torch
+    import synth
+    w = synth.get_workload("train_causal_d128")
+    t = _device_inputs(w)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws = torch.empty(max(1, attn.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal,
+                                                     attn.ATTN_BF16)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o, lse=lse)
+        attn.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal, scale=w.scale,
+                 dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms, kern = _time(step, steps, warmup, attn)
+    fwd = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
+    total = 3.5 * fwd
+    dom = max(kern, key=kern.get)
+    return w, ms, total, kern, dom
+
+
+def bench_fwd(attn, steps, warmup):
+    import torch
+    import synth
+    w = synth.get_workload("long_causal_d128")
+    t = _device_inputs(w)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
+    ms, kern = _time(lambda: attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o,
+                                      lse=lse), steps, warmup, attn)
+    flops = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
+    return {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d, "causal": w.causal,
+            "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+            "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline("fwd_prefill_bf16", w, kern["fwd_prefill_bf16"]),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
+
+
+def bench_decode(attn, steps, warmup):
+    import torch
+    import synth
+    w = synth.get_workload("gqa_decode")
+    t = _device_inputs(w)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
+    ws = torch.empty(attn.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, attn.ATTN_BF16),
+                     dtype=torch.uint8, device="cuda")
+    ms, kern = _time(lambda: attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o,
+                                      lse=lse, workspace=ws), steps, warmup, attn)
+    e = 2
+    alg = 2 * w.B * w.Hkv * w.Sk * w.d * e + 2 * w.B * w.Hq * w.Sq * w.d * e + w.B * w.Hq * w.Sq * 4
+    return {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
+            "ms": round(ms, 4), "algorithmic_bytes": alg, "gbs": round(alg / ms / 1e6, 1),
+            "frac_of_peak": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "roofline": roofline("fwd_split_bf16", w, kern["fwd_split_bf16"]),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
+
+
+def cpu_baseline(w, heads: int = 4) -> dict:
+    """The FP64 oracle as it stands, on a few heads of the training workload."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = synth.make_inputs(w)
+    f = {n: synth.to_f64(x[n][:, :heads], "bf16") for n in ("q", "k", "v", "do")}
+    t0 = time.perf_counter()
+    oracle.attention_forward(f["q"], f["k"], f["v"], causal=w.causal, scale=w.scale)
+    oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], causal=w.causal, scale=w.scale)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * nominal_fwd_flops(w.B, heads, w.Sq, w.Sk, w.d, w.causal)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{heads} of {w.Hq} heads of {w.name} (S={w.Sq}, d={w.d}, causal), "
+                      "attention_forward + attention_backward in float64 NumPy"}
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def _read_counter_csv(d: str):
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        with open(p) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                       command: str) -> None:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel by the
+    ratio a plain 1 GiB copy reads for the same counters, and store per-kernel
+    HBM bytes per launch under profiles/."""
+    def per_kernel(rows, counter):
+        acc = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        return acc
+
+    def copy_factor(rows, counter, nbytes=1 << 30):
+        vals = [v for k, vs in per_kernel(rows, counter).items() for v in vs
+                if "copy" in k.lower() or "elementwise" in k.lower()]
+        vals = [v for v in vals if v > 0.25 * nbytes / 1024]
+        if not vals:
+            return None, None
+        med = sorted(vals)[len(vals) // 2]
+        return nbytes / (med * 1024.0), med
+
+    fetch = per_kernel(_read_counter_csv(fetch_dir), "FETCH_SIZE")
+    write = per_kernel(_read_counter_csv(write_dir), "WRITE_SIZE")
+    ff, fcopy = copy_factor(_read_counter_csv(copy_fetch_dir), "FETCH_SIZE")
+    wf, wcopy = copy_factor(_read_counter_csv(copy_write_dir), "WRITE_SIZE")
+    for kern, sym in KERNEL_SYMBOLS.items():
+        fk = [v for k, vs in fetch.items() if sym in k for v in vs]
+        wk = [v for k, vs in write.items() if sym in k for v in vs]
+        if not fk or not wk or ff is None or wf is None:
+            continue
+        f_kib = sorted(fk)[len(fk) // 2]
+        w_kib = sorted(wk)[len(wk) // 2]
+        out = {"kernel": kern, "source_sha": source_hash(kern),
+               "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+               "copy_calibration": {"bytes": 1 << 30, "fetch_kib": fcopy, "write_kib": wcopy,
+                                    "fetch_factor": ff, "write_factor": wf},
+               "hbm_bytes_per_launch": int(f_kib * 1024 * ff + w_kib * 1024 * wf),
+               "command": command}
+        with open(os.path.join(PROFILES, f"counters_{kern}.json"), "w") as f:
+            json.dump(out, f, indent=1)
+        print(kern, out["hbm_bytes_per_launch"])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "step", "fwd", "decode"], default="all")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--command", default="")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, command=args.command)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import torch
+    import exact_io_aware_38_amd as attn
+    attn.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    result = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic"}
+    if args.only in ("all", "step"):
+        w, ms, total, kern, dom = bench_step(attn, args.steps, args.warmup)
+        print(f"# step: {ms:.3f} ms, kernels {kern}", file=sys.stderr, flush=True)
+        result.update({"value": round(total / ms / 1e9, 2), "ms_per_step": round(ms, 4),
+                       "frac_of_peak": round(total / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                       "config": {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d,
+                                  "causal": w.causal, "step": "attn_fwd + attn_bwd",
+                                  "nominal_tflop_per_step": round(total / 1e12, 4)},
+                       "roofline": roofline(dom, w, kern[dom]),
+                       "kernels_ms": {k: round(v, 4) for k, v in kern.items()}})
+        torch.cuda.empty_cache()
+    if args.only in ("all", "fwd"):
+        result["fwd"] = bench_fwd(attn, args.steps, args.warmup)
+        print(f"# fwd: {result['fwd']['ms']} ms", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if args.only in ("all", "decode"):
+        result["decode"] = bench_decode(attn, max(args.steps, 20), args.warmup)
+        print(f"# decode: {result['decode']['ms']} ms", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if args.only == "fwd":
+        result.update({"value": result["fwd"]["tflops"], "ms_per_step": result["fwd"]["ms"],
+                       "config": {"workload": result["fwd"]["workload"]}, "roofline": result["fwd"]["roofline"]})
+    if args.only == "decode":
+        result.update({"value": result["decode"]["gbs"], "unit": "GB/s", "ms_per_step": result["decode"]["ms"],
+                       "config": {"workload": result["decode"]["workload"]},
+                       "roofline": result["decode"]["roofline"]})
+    if not args.no_cpu_baseline and args.only in ("all", "step"):
+        import synth
+        print("# cpu baseline (oracle, one head) ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(synth.get_workload("train_causal_d128"))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

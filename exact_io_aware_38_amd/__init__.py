@@ -15,6 +15,7 @@ from typing import Optional, Tuple
 __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "lib", "library_path", "fwd", "bwd",
     "fwd_workspace_bytes", "bwd_workspace_bytes", "strerror", "last_dispatch",
+    "timing_start", "timing_stop",
 ]
 
 ATTN_F32 = 0
@@ -63,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_dispatch.argtypes = [ctypes.c_char_p, _Z]
         L.attn_last_dispatch.restype = _I
+        L.attn_timing_start.argtypes = []
+        L.attn_timing_start.restype = _I
+        L.attn_timing_stop.argtypes = [ctypes.c_char_p, _Z]
+        L.attn_timing_stop.restype = _I
         _lib = L
     return _lib
 
@@ -77,6 +82,24 @@ def last_dispatch() -> str:
     buf = ctypes.create_string_buffer(n + 1)
     lib().attn_last_dispatch(buf, n + 1)
     return buf.value.decode()
+
+
+def timing_start() -> None:
+    """Start recording per-kernel device time for this thread's calls."""
+    lib().attn_timing_start()
+
+
+def timing_stop() -> dict:
+    """Stop recording; returns {kernel: (launches, total_ms)} (waits for the events)."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().attn_timing_stop(buf, len(buf))
+    if n < 0:
+        raise AttnError(n, "attn_timing_stop")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
 
 
 def fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype) -> int:

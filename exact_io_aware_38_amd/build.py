@@ -24,6 +24,8 @@ ARCH = "gfx950"
 # Packed fp32 arithmetic is switched off for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA results in ordinary VGPRs instead of shuttling them through AGPRs
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

@@ -8,10 +8,41 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <string>
+#include <vector>
 
 #include "kernels.h"
 
 namespace {
+
+// Per-thread kernel timing records (diagnostics).
+struct TimedLaunch {
+  const char* kernel;
+  hipEvent_t begin, end;
+};
+struct TimingState {
+  bool on = false;
+  bool failed = false;
+  std::vector<hipEvent_t> pool;   // events owned by this thread, reused across sessions
+  size_t used = 0;
+  std::vector<TimedLaunch> launches;
+  const char* pending = nullptr;
+  hipEvent_t pending_begin = nullptr;
+};
+thread_local TimingState g_timing;
+
+hipEvent_t next_event() {
+  TimingState& t = g_timing;
+  if (t.used == t.pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+      t.failed = true;
+      return nullptr;
+    }
+    t.pool.push_back(e);
+  }
+  return t.pool[t.used++];
+}
 
 thread_local char g_dispatch[512] = "";
 
@@ -50,7 +81,78 @@ attn::Problem make_problem(int B, int Hq, int Hkv, int Sq, int Sk, int d, int ca
 
 }  // namespace
 
+namespace attn {
+
+void timing_begin(hipStream_t s, const char* kernel) {
+  TimingState& t = g_timing;
+  if (!t.on) return;
+  t.pending = kernel;
+  t.pending_begin = next_event();
+  if (t.pending_begin != nullptr && hipEventRecord(t.pending_begin, s) != hipSuccess) t.failed = true;
+}
+
+void timing_end(hipStream_t s) {
+  TimingState& t = g_timing;
+  if (!t.on || t.pending == nullptr || t.pending_begin == nullptr) return;
+  hipEvent_t e = next_event();
+  if (e == nullptr || hipEventRecord(e, s) != hipSuccess) {
+    t.failed = true;
+  } else {
+    t.launches.push_back(TimedLaunch{t.pending, t.pending_begin, e});
+  }
+  t.pending = nullptr;
+  t.pending_begin = nullptr;
+}
+
+}  // namespace attn
+
 extern "C" {
+
+int attn_timing_start(void) {
+  TimingState& t = g_timing;
+  t.on = true;
+  t.failed = false;
+  t.used = 0;
+  t.launches.clear();
+  return ATTN_OK;
+}
+
+int attn_timing_stop(char* buf, size_t n) {
+  TimingState& t = g_timing;
+  t.on = false;
+  if (t.failed) return ATTN_ERR_HIP;
+  // aggregate per kernel name, in order of first appearance
+  std::vector<std::string> names;
+  std::vector<double> total;
+  std::vector<int> count;
+  for (const TimedLaunch& l : t.launches) {
+    if (hipEventSynchronize(l.end) != hipSuccess) return ATTN_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, l.begin, l.end) != hipSuccess) return ATTN_ERR_HIP;
+    size_t i = 0;
+    while (i < names.size() && names[i] != l.kernel) ++i;
+    if (i == names.size()) {
+      names.emplace_back(l.kernel);
+      total.push_back(0.0);
+      count.push_back(0);
+    }
+    total[i] += ms;
+    count[i] += 1;
+  }
+  std::string out;
+  for (size_t i = 0; i < names.size(); ++i) {
+    char line[160];
+    std::snprintf(line, sizeof(line), "%s %d %.6f\n", names[i].c_str(), count[i], total[i]);
+    out += line;
+  }
+  t.launches.clear();
+  t.used = 0;
+  if (n > 0) {
+    if (buf == nullptr) return ATTN_ERR_NULL;
+    std::snprintf(buf, n, "%s", out.c_str());
+  }
+  return (int)out.size();
+}
 
 const char* attn_strerror(int status) {
   switch (status) {

@@ -439,17 +439,23 @@ template <int D>
 hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   const size_t rows = (size_t)a.B * a.Hq * a.Sq;
   constexpr int RPB = 256 / (D / 8);
+  timing_begin(s, "bwd_pre");
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a, rows);
   hipError_t e = hipGetLastError();
+  timing_end(s);
   if (e != hipSuccess) return e;
   if (a.total_kv > 0) {
+    timing_begin(s, "bwd_dkdv");
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.total_kv), dim3(256), 0, s, a);
     e = hipGetLastError();
+    timing_end(s);
     if (e != hipSuccess) return e;
   }
   if (a.total_q > 0) {
+    timing_begin(s, "bwd_dq");
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.total_q), dim3(256), 0, s, a);
     e = hipGetLastError();
+    timing_end(s);
     if (e != hipSuccess) return e;
   }
   if (log != nullptr && log_n > 0)

@@ -101,11 +101,14 @@ hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, cons
                           float* lse, hipStream_t s) {
   F32Args a{q, k, v, o, lse, p.Hq, p.Hkv, p.Sq, p.Sk, p.Hq / p.Hkv, p.causal, p.scale};
   dim3 grid((p.Sq + 127) / 128, p.Hq, p.B);
+  timing_begin(s, "fwd_f32");
   if (p.d == 64)
     hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, dim3(128), 0, s, a);
   else
     hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, dim3(128), 0, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  timing_end(s);
+  return e;
 }
 
 }  // namespace attn

@@ -8,6 +8,12 @@
 
 namespace attn {
 
+// Optional per-kernel timing (diagnostics, off by default): while enabled on
+// the calling thread, every launch is bracketed by two HIP events recorded on
+// the launch's own stream.
+void timing_begin(hipStream_t s, const char* kernel);
+void timing_end(hipStream_t s);
+
 // Problem description shared by the launchers (already validated).
 struct Problem {
   int B, Hq, Hkv, Sq, Sk, d, causal;

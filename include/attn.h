@@ -109,6 +109,20 @@ const char* attn_strerror(int status);
  * also printed to stderr on every call. */
 int attn_last_dispatch(char* buf, size_t n);
 
+/* Diagnostics: per-kernel device timing of the calling thread's calls.
+ * attn_timing_start() clears the record and, until attn_timing_stop(), makes
+ * every kernel launch of attn_fwd/attn_bwd on this thread be bracketed by two
+ * HIP events recorded on the launch's own stream (the events are created
+ * lazily and reused; timing adds two event records per kernel and changes
+ * nothing else). attn_timing_stop() ends the record, waits for the recorded
+ * events, and writes one line per kernel name into buf (host memory, n bytes,
+ * NUL-terminated): "<kernel> <launches> <total milliseconds>". It returns the
+ * full length of the text, ATTN_ERR_NULL if buf is NULL with n > 0, or
+ * ATTN_ERR_HIP if an event could not be created, recorded or read. The record
+ * lives only in host memory; no kernel argument or output depends on it. */
+int attn_timing_start(void);
+int attn_timing_stop(char* buf, size_t n);
+
 #ifdef __cplusplus
 }
 #endif
