@@ -45,8 +45,8 @@ KERNEL_SOURCES = {
 }
 # substrings of the mangled device symbols, as rocprofv3 reports them
 KERNEL_SYMBOLS = {
-    "fwd_prefill_bf16": "fwd_bf16_kernelILi128ELi4ELi2ELb0E",
-    "fwd_split_bf16": "fwd_bf16_kernelILi128ELi1ELi1ELb1E",
+    "fwd_prefill_bf16": "fwd_prefill_kernelILi128E",
+    "fwd_split_bf16": "fwd_split_kernelILi128E",
     "bwd_dkdv": "bwd_dkdv_kernelILi128E",
     "bwd_dq": "bwd_dq_kernelILi128E",
     "bwd_pre": "bwd_pre_kernelILi128E",
@@ -132,6 +132,12 @@ def _device_inputs(w):
     return out
 
 
+def _fwd_workspace(attn, w):
+    import torch
+    n = attn.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, attn.ATTN_BF16)
+    return torch.empty(max(1, n), dtype=torch.uint8, device="cuda")
+
+
 def _time(fn, steps: int, warmup: int, attn):
     import torch
     for _ in range(warmup):
@@ -160,9 +166,10 @@ def bench_step(attn, steps, warmup):
     dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
     ws = torch.empty(max(1, attn.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal,
                                                      attn.ATTN_BF16)), dtype=torch.uint8, device="cuda")
+    fws = _fwd_workspace(attn, w)
 
     def step():
-        attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o, lse=lse)
+        attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=fws)
         attn.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal, scale=w.scale,
                  dq=dq, dk=dk, dv=dv, workspace=ws)
 
@@ -180,8 +187,9 @@ def bench_fwd(attn, steps, warmup):
     t = _device_inputs(w)
     o = torch.empty_like(t["q"])
     lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
+    fws = _fwd_workspace(attn, w)
     ms, kern = _time(lambda: attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o,
-                                      lse=lse), steps, warmup, attn)
+                                      lse=lse, workspace=fws), steps, warmup, attn)
     flops = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
     return {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d, "causal": w.causal,
             "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),

@@ -36,9 +36,16 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
+# Kernel sources only: the kernels never produce NaN (masked scores are -inf and
+# every -inf - -inf case is guarded), so NaN-preserving max sequences are not
+# needed. Host code (argument validation) keeps full IEEE semantics.
+KERNEL_ONLY = ["-fno-honor-nans"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = KERNEL_ONLY if src.endswith(".hip") else []
+    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

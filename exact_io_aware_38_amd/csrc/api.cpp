@@ -183,7 +183,7 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d, i
   if (dtype != ATTN_BF16) return 0;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, 1.f);
   const attn::SplitPlan sp = attn::plan_split(p);
-  return sp.use ? sp.ws_bytes : 0;
+  return sp.use ? sp.ws_bytes : attn::plan_prefill(p).ws_bytes;
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -211,10 +211,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                     d, sp.nsplit * B * Hkv, sp.nsplit, sp.split_keys, d, B * Hq * Sq);
     } else {
       const attn::PrefillPlan pl = attn::plan_prefill(p);
-      e = attn::launch_fwd_prefill_bf16(p, pl, q, k, v, o, lse, s);
+      if (pl.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < pl.ws_bytes)) return ATTN_ERR_WORKSPACE;
+      e = attn::launch_fwd_prefill_bf16(p, pl, q, k, v, o, lse, workspace, s);
       std::snprintf(text, sizeof(text),
-                    "attn_fwd: fwd_prefill_bf16<d=%d> grid=%d block=256 heads/wg=%d rows/wg=%d key_tile=64 causal=%d",
-                    d, pl.total_wgs, pl.hw, pl.rows_per_wg, causal);
+                    "attn_fwd: transpose_v<d=%d> grid=(%d,%d,%d); fwd_prefill_bf16<d=%d> grid=%d block=512 "
+                    "heads/wg=%d rows/wg=%d key_tile=64 causal=%d",
+                    d, (Sk + 63) / 64, Hkv, B, d, pl.total_wgs, pl.hw, pl.rows_per_wg, causal);
     }
   }
   if (e != hipSuccess) return ATTN_ERR_HIP;

@@ -30,13 +30,12 @@ namespace attn {
 namespace {
 
 // Element offset in a row-major [rows][D] bf16 LDS tile whose 16-byte chunks
-// are XOR-swizzled per row, so that both 16-byte row reads (8 rows at one
-// column) and transposed 8-byte reads (4 rows, 32 bytes each) spread over
-// distinct banks. col must be a multiple of 4.
+// are XOR-swizzled per row (chunk_swizzle), so that both 16-byte row reads
+// and transposed 8-byte reads are free of bank conflicts. col must be a
+// multiple of 4.
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
-  const int h = ((row & 3) << 1) | ((row >> 2) & 1);
-  return row * D + (((col >> 3) ^ h) << 3) + (col & 7);
+  return row * D + (((col >> 3) ^ chunk_swizzle<D>(row)) << 3) + (col & 7);
 }
 
 struct BwdArgs {
@@ -281,11 +280,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int MB = D / 32;
   constexpr int CH_ROW = D / 8;
   constexpr int CH_THR = BK * CH_ROW / NT;
-  constexpr int VS = D + 8;        // padded V row stride (only 16-byte row reads)
   static_assert((BK * CH_ROW) % NT == 0, "tile must split evenly");
 
   __shared__ __attribute__((aligned(16))) bf16 sk[2][BK * D];
-  __shared__ __attribute__((aligned(16))) bf16 sv[2][BK * VS];
+  __shared__ __attribute__((aligned(16))) bf16 sv[2][BK * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -356,7 +354,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       const int row = c / CH_ROW;
       const int col = c % CH_ROW;
       *(u32x4*)(&sk[buf][swz<D>(row, col * 8)]) = kreg[i];
-      *(u32x4*)(&sv[buf][row * VS + col * 8]) = vreg[i];
+      *(u32x4*)(&sv[buf][swz<D>(row, col * 8)]) = vreg[i];
     }
   };
 
@@ -386,7 +384,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 ak = *(const bf16x8*)(tk + swz<D>(32 * kb + l32, 16 * dc + 8 * hi));
-          const bf16x8 av = *(const bf16x8*)(tv + (32 * kb + l32) * VS + 16 * dc + 8 * hi);
+          const bf16x8 av = *(const bf16x8*)(tv + swz<D>(32 * kb + l32, 16 * dc + 8 * hi));
           s[kb] = mfma32(ak, qf[dc], s[kb]);
           dp[kb] = mfma32(av, df[dc], dp[kb]);
         }

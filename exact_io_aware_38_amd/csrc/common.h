@@ -72,6 +72,43 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   return r;
 }
 
+// Max and sum of 32 values as balanced trees (max3 where possible), so that
+// the reductions do not form long dependency chains.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+__device__ __forceinline__ float tree_max32(const float* v) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) t[i] = max3f(v[3 * i], v[3 * i + 1], v[3 * i + 2]);
+  t[10] = fmaxf(v[30], v[31]);
+  const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]);
+  const float u2 = max3f(t[6], t[7], t[8]), u3 = fmaxf(t[9], t[10]);
+  return fmaxf(max3f(u0, u1, u2), u3);
+}
+
+__device__ __forceinline__ float tree_sum32(const float* v) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+  return t[0];
+}
+
+// LDS tiles of 64 rows x D bf16 are stored unpadded, with the 16-byte chunks
+// of each row XOR-permuted by this row function. gfx950 LDS serves 256 bytes
+// per clock over 64 banks: 16-byte row reads (16 consecutive rows, same
+// logical chunk) and transposed 8-byte reads (4 consecutive rows x 4 adjacent
+// chunks per 32 lanes) then both hit 16 distinct 16-byte bank groups, which a
+// conflict-counter probe of every read pattern used here confirmed.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // Workgroup order: the hardware hands consecutive workgroup ids to the 8 XCDs
 // in turn, each with its own L2. Renumber so that each XCD receives a
 // contiguous range of logical ids, i.e. all tiles of a few heads, which then

@@ -4,37 +4,351 @@
 // pre-training practice" §1.2, kept in the unnormalised (m, l, u) form of "AI
 // 大模型之 FlashAttention_01" §4.1 / "瓦片状态如何保持精确语义": per query row,
 // a running max m, a running denominator l and an accumulator u are rescaled
-// by exp(m_old - m_new) whenever a key tile raises the max, and O = u / l at
-// the end, with lse = m + ln l kept for the backward. Scores never leave the
-// registers (the fusion of §1.3 of the first page); the outer loop runs over
-// query tiles and the inner one over key tiles (the loop order of §4.3 of
-// the second page). Key tiles above the causal diagonal are never loaded
-// (§2.1 of the first page), and the rescale is skipped when no row of the
-// wavefront raised its max (§2.3 of the first page, with threshold 0).
+// by exp(m_old - m_new) when a key tile raises the max, and O = u / l at the
+// end, with lse = m + ln l kept for the backward. Scores never leave the
+// registers (the fused kernel of §1.3 of the first page); the outer loop runs
+// over query tiles and the inner one over key tiles (the loop order of §4.3 of
+// the second page). Key tiles above the causal diagonal are never loaded (§2.1
+// of the first page), and the rescale is skipped unless some row's max grew
+// by more than RESCALE_T (§2.3 of the first page describes the skip; with a
+// threshold the probabilities stay below 2^RESCALE_T and u / l is unchanged).
 //
 // Mapping to CDNA4:
-//  * a wavefront owns 32*NB query rows as MFMA columns and computes the
-//    transposed score tile S^T = K Q^T (rows = keys), so that every lane holds
-//    the scores of one query row: the row max and sum reduce inside the lane
-//    plus one swap between lane halves, and the probabilities sit in the
-//    exact register layout the B operand of O^T = V^T P^T expects;
-//  * K and V tiles (64 keys) are staged through LDS, double-buffered, shared by
-//    the NW wavefronts of the workgroup; V^T fragments come from
-//    ds_read_b64_tr_b16 on the row-major V tile;
+//  * a wavefront owns 32 query rows as MFMA columns and computes the transposed
+//    score tile S^T = K Q^T (rows = keys), so every lane holds the scores of one
+//    query row: the row max and sum reduce inside the lane plus one swap between
+//    lane halves, and the probabilities already sit in the B-operand layout of
+//    O^T = V^T P^T;
+//  * V is first transposed once per call into a [d][keys] workspace whose keys
+//    are permuted inside each group of 16 so that one 16-byte LDS read yields
+//    the 8 keys an MFMA lane needs (transposed LDS reads are several times
+//    slower than row reads on this chip);
+//  * K and V^T tiles (64 keys) go HBM -> LDS through the DMA path of
+//    global_load_lds into a 4-stage ring, issued two tiles ahead;
+//  * two wavefronts share each SIMD and run the per-tile steps in opposite
+//    orders so that one's softmax (vector ALU) overlaps the other's MFMAs;
 //  * exp2 with log2(e) folded into the score scale: one FMA and one v_exp_f32
 //    per score.
 #include "common.h"
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace attn {
 
 namespace {
 
+constexpr float RESCALE_T = 8.0f;   // log2 units
+constexpr int BC = 64;               // keys per tile
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// 16 bytes per lane from global memory straight into LDS at base + 16 * lane
+// (base must be wave-uniform). Issued as inline assembly: the compiler would
+// otherwise make every later LDS read wait for all outstanding DMA (it cannot
+// tell the ring stages apart), which serialises the prefetch; the kernels wait
+// for their DMA explicitly (s_waitcnt vmcnt + s_barrier) before reading a stage.
+__device__ __forceinline__ void dma16(const void* g, lds_void* base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(g)
+               : "memory", "m0");
+}
+
+// Swizzle of the 8 16-byte chunks of a 128-byte V^T row (conflict-free
+// 16-byte reads of 16 consecutive rows at one logical chunk).
+__device__ __forceinline__ int vt_swizzle(int row) { return (row >> 1) & 7; }
+
+// Position of key k inside its group of 16 in a V^T row: key 8a + 4h + e is
+// stored at 8h + 4a + e, so that lane half h finds its 8 MFMA reduction slots
+// (keys 8a + 4h + e, a in {0,1}, e in 0..3) in one contiguous 16-byte chunk.
+// The map swaps two bits, so it is its own inverse.
+__device__ __forceinline__ int vt_perm(int k) {
+  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
+}
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* vt;    // prefill: transposed V, [B, Hkv, D, skp], keys permuted by vt_perm
+  bf16* o;
+  float* lse;
+  float* part_o;     // split path: [nsplit, B, Hq, Sq, D]
+  float* part_lse;   // split path: [nsplit, B, Hq, Sq]
+  int B, Hq, Hkv, Sq, Sk, g, causal;
+  int skp;           // Sk rounded up to the key tile
+  float c;           // scale * log2(e)
+  int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
+  int nsplit, split_keys;
+};
+
+// ---------------------------------------------------------------------------
+// V [B, Hkv, Sk, D] -> V^T [B, Hkv, D, skp] with keys permuted by vt_perm
+// inside each group of 16 and zero padding past Sk. One workgroup per
+// (64-key tile, KV head, batch).
+// ---------------------------------------------------------------------------
 template <int D>
-struct FwdTile {
-  static constexpr int BC = 64;          // keys per tile
+__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16* __restrict__ v, bf16* __restrict__ vt,
+                                                          int Hkv, int Sk, int skp) {
+  constexpr int S = D + 2;                       // odd word stride: column reads spread over banks
+  __shared__ bf16 tile[BC * S];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * BC;
+  const size_t head = (size_t)blockIdx.z * Hkv + blockIdx.y;
+  const bf16* src = v + head * (size_t)Sk * D;
+  for (int c = tid; c < BC * D / 8; c += 256) {
+    const int row = c / (D / 8);
+    const int col = (c % (D / 8)) * 8;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (t0 + row < Sk) val = *(const u32x4*)(src + (size_t)(t0 + row) * D + col);
+    const bf16x8 e = __builtin_bit_cast(bf16x8, val);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[row * S + col + i] = e[i];
+  }
+  __syncthreads();
+  bf16* dst = vt + head * (size_t)D * skp + t0;
+  for (int c = tid; c < D * (BC / 8); c += 256) {
+    const int d = c / (BC / 8);
+    const int ch = c % (BC / 8);
+    bf16x8 e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = tile[vt_perm(8 * ch + j) * S + d];
+    *(bf16x8*)(dst + (size_t)d * skp + 8 * ch) = e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: 8 wavefronts (two per SIMD) x 32 query rows per workgroup.
+// Phase A wavefronts do S(j), P(j-1)V(j-1), softmax(j) per step; phase B
+// wavefronts do softmax(j-1), P(j-1)V(j-1), S(j).
+// ---------------------------------------------------------------------------
+template <int D>
+struct Ring {
+  static constexpr int TILE = BC * D * 2;       // bytes of one K or V^T tile
+  static constexpr int STAGE = 2 * TILE;        // K then V^T
+  static constexpr int NSTAGE = 4;
+  static constexpr int INSTR = D / 64;          // DMA instructions per wavefront per tensor per tile
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
+  using R = Ring<D>;
+  constexpr int MB = D / 32;
+  constexpr int DC = D / 16;
+  constexpr int CPR = D / 8;                    // 16-byte chunks per K row
+  constexpr int RB = 2 * D;                     // bytes per K row
+
+  __shared__ __attribute__((aligned(1024))) char smem[R::NSTAGE * R::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const bool phase_b = wid >= 4;
+  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
+
+  const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
+  const int ptile = a.n_ptiles - 1 - (W % a.n_ptiles);   // longest causal tiles first
+  int rest = W / a.n_ptiles;
+  const int hgrp = rest % a.n_hgroups;
+  rest /= a.n_hgroups;
+  const int hkv = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  // the two phases take alternating 32-row blocks, which keeps their causal work equal
+  const int slot = (wid & 3) * 2 + (wid >> 2);
+  const int head = hkv * a.g + hgrp * a.hw + slot % a.hw;
+  const int p0 = ptile * a.rows_per_wg + 32 * (slot / a.hw);
+  const int pos = p0 + l32;
+  const bool colv = pos < a.Sq;
+  const int wg_last = min((ptile + 1) * a.rows_per_wg, a.Sq) - 1;
+  int kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
+  if (kend < 0) kend = 0;
+  const int ntiles = (kend + BC - 1) / BC;
+  const int wave_maxpos = min(p0 + 31, a.Sq - 1);
+  int kend_w = a.causal ? min(kend, wave_maxpos + off + 1) : kend;
+  if (p0 >= a.Sq || kend_w < 0) kend_w = 0;
+  const int nt_w = (kend_w + BC - 1) / BC;       // tiles this wavefront computes (a prefix)
+  const int mask_from = a.causal ? max(0, min(kend, p0 + off + 1)) : kend;
+  const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
+
+  bf16x8 qf[DC];
+  {
+    const bf16* qp = a.q + (((size_t)b * a.Hq + head) * a.Sq + (colv ? pos : 0)) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+  const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
+  const bf16* vtg = a.vt + ((size_t)b * a.Hkv + hkv) * (size_t)D * a.skp;
+
+  // Per-lane DMA geometry: lane i of instruction n writes LDS chunk
+  // P = (wid*INSTR + n)*64 + i of a tile, i.e. K row P / CPR, physical chunk
+  // P % CPR (V^T row P / 8, physical chunk P % 8), and loads the logical chunk
+  // (physical ^ swizzle(row)) from global memory.
+  int krow[R::INSTR], koff[R::INSTR], voff[R::INSTR];
+#pragma unroll
+  for (int n = 0; n < R::INSTR; ++n) {
+    const int P = (wid * R::INSTR + n) * 64 + lane;
+    krow[n] = P / CPR;
+    koff[n] = ((P % CPR) ^ chunk_swizzle<D>(krow[n])) * 8;
+    const int vrow = P / 8;
+    voff[n] = vrow * a.skp + ((P % 8) ^ vt_swizzle(vrow)) * 8;
+  }
+  auto issue = [&](int t) {
+    const int key0 = t * BC;
+    char* stage = smem + (t % R::NSTAGE) * R::STAGE;
+    const bf16* kt = kg + (size_t)key0 * D;
+    const bool full = key0 + BC <= kend;
+#pragma unroll
+    for (int n = 0; n < R::INSTR; ++n) {
+      // rows past kend repeat row kend-1 (finite data; their probabilities are masked to 0)
+      const bf16* ks = full ? kt + krow[n] * D + koff[n]
+                            : kg + (size_t)min(key0 + krow[n], kend - 1) * D + koff[n];
+      dma16(ks, (lds_void*)(stage + (wid * R::INSTR + n) * 1024));
+      dma16(vtg + key0 + voff[n], (lds_void*)(stage + R::TILE + (wid * R::INSTR + n) * 1024));
+    }
+  };
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+  float m2 = kNegInf, lsum = 0.f;
+  bf16x8 pf[4];
+  // scores of the current tile, split over even and odd d-chunks: four
+  // independent MFMA accumulation chains instead of two (a dependent MFMA
+  // waits ~150 cycles for its predecessor)
+  f32x16 s[2][2];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) pf[kc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+
+  // One basic block of MFMAs: S(j) = K_j Q^T (16, four chains) interleaved with
+  // O^T += V_{j-1}^T P_{j-1}^T (16, MB chains), so that no chain's next MFMA
+  // issues within eight MFMAs of its previous one.
+  auto mma = [&](auto do_s, auto do_pv, int j) {
+    const char* stK = smem + (j % R::NSTAGE) * R::STAGE;
+    const char* stV = smem + ((j + R::NSTAGE - 1) % R::NSTAGE) * R::STAGE + R::TILE;
+    if constexpr (do_s.value) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb][0] = s[kb][1] = f32x16{};
+    }
+    constexpr int PV_PER_DC = (MB * 4) / DC;   // PV MFMAs issued per d-chunk step
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (do_s.value) {
+          const int r = 32 * kb + l32;
+          const bf16x8 ak = *(const bf16x8*)(stK + r * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(r)) << 4));
+          s[kb][dc & 1] = mfma32(ak, qf[dc], s[kb][dc & 1]);
+        }
+        if constexpr (do_pv.value) {
+#pragma unroll
+          for (int u = 0; u < PV_PER_DC / 2; ++u) {
+            const int p = dc * PV_PER_DC + kb * (PV_PER_DC / 2) + u;
+            const int mb = p % MB;
+            const int kc = p / MB;
+            const int d = 32 * mb + l32;
+            const bf16x8 av = *(const bf16x8*)(stV + d * (2 * BC) + (((2 * kc + hi) ^ vt_swizzle(d)) << 4));
+            acc[mb] = mfma32(av, pf[kc], acc[mb]);
+          }
+        }
+      }
+    }
+  };
+  auto softmax = [&](int j) {
+    const int key0 = j * BC;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = s[0][0][i] + s[0][1][i];
+      v[16 + i] = s[1][0][i] + s[1][1][i];
+    }
+    if (key0 + BC > mask_from) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int key = key0 + 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * hi + (i & 3);
+        if (key > lim) v[i] = kNegInf;
+      }
+    }
+    const float mx = max_halves(tree_max32(v)) * a.c;
+    // move the reference max only when the row max grew by more than RESCALE_T
+    const bool grow = mx > m2 + RESCALE_T;
+    if (wave_any(grow)) {
+      const float mnew = grow ? mx : m2;
+      const float alpha = grow ? fast_exp2(m2 - mnew) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+      m2 = mnew;
+    }
+    const float msub = (m2 == kNegInf) ? 0.f : m2;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = fast_exp2(__builtin_fmaf(v[i], a.c, -msub));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      pf[q] = to_bf16x8(v[8 * q + 0], v[8 * q + 1], v[8 * q + 2], v[8 * q + 3], v[8 * q + 4], v[8 * q + 5],
+                        v[8 * q + 6], v[8 * q + 7]);
+    lsum += tree_sum32(v);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  for (int j = 0; j <= ntiles; ++j) {
+    // tile j has landed in LDS for every wavefront (each waits for its own DMA,
+    // the barrier for all of them), and every wavefront is done with tile j-2
+    if (j + 1 < ntiles) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * R::INSTR) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (j + 2 < ntiles) issue(j + 2);
+    const bool ds = j < nt_w;                  // scores of tile j
+    const bool dp = j >= 1 && j - 1 < nt_w;    // P V of tile j-1
+    if (phase_b && dp) softmax(j - 1);
+    if (ds && dp) {
+      mma(T_{}, T_{}, j);
+    } else if (ds) {
+      mma(T_{}, F_{}, j);
+    } else if (dp) {
+      mma(F_{}, T_{}, j);
+    }
+    if (!phase_b && ds) softmax(j);
+  }
+
+  const float lt = sum_halves(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : kNegInf;
+  if (!colv) return;
+  bf16* op = a.o + (((size_t)b * a.Hq + head) * a.Sq + pos) * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 r;
+      r[0] = (bf16)(acc[mb][4 * q4 + 0] * inv);
+      r[1] = (bf16)(acc[mb][4 * q4 + 1] * inv);
+      r[2] = (bf16)(acc[mb][4 * q4 + 2] * inv);
+      r[3] = (bf16)(acc[mb][4 * q4 + 3] * inv);
+      *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi) = r;
+    }
+  if (a.lse != nullptr && hi == 0) a.lse[((size_t)b * a.Hq + head) * a.Sq + pos] = lse_v;
+}
+
+// ---------------------------------------------------------------------------
+// Split-key decode: one wavefront per (key slice, KV head, batch); its 32
+// MFMA columns pack (query head of the group, query row) pairs, so each K/V
+// byte of the slice is read once for all of them. Writes the slice's
+// normalised partial output and lse; combine_split_kernel merges the slices.
+// ---------------------------------------------------------------------------
+template <int D>
+struct SplitTile {
   static constexpr int KS = D + 8;       // K row stride in LDS (bf16), 16 B pad
   static constexpr int VS = D + 16;      // V row stride in LDS (bf16), 32 B pad
   static constexpr int K_ELEMS = BC * KS;
@@ -42,109 +356,44 @@ struct FwdTile {
   static constexpr int BUF = K_ELEMS + V_ELEMS;
 };
 
-struct FwdArgs {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  bf16* o;
-  float* lse;
-  float* part_o;     // split path: [nsplit, B, Hq, Sq, D]
-  float* part_lse;   // split path: [nsplit, B, Hq, Sq]
-  int B, Hq, Hkv, Sq, Sk, g, causal;
-  float c;           // scale * log2(e)
-  int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
-  int nsplit, split_keys;
-};
-
-template <int D, int NW, int NB, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
-  using T = FwdTile<D>;
-  constexpr int BC = T::BC;
-  constexpr int NT = NW * 64;
-  constexpr int CH_ROW = D / 8;             // 16-byte chunks per row
-  constexpr int CH_THR = BC * CH_ROW / NT;  // chunks per thread per tensor per tile
-  static_assert((BC * CH_ROW) % NT == 0, "tile must split evenly over the threads");
-  constexpr int QW = 32 * NB;
-  constexpr int MB = D / 32;                // 32-row blocks of O^T (over d)
-  constexpr int DC = D / 16;                // 16-wide reduction chunks over d
+template <int D>
+__global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
+  using T = SplitTile<D>;
+  constexpr int CH_ROW = D / 8;
+  constexpr int CH_THR = BC * CH_ROW / 64;
+  constexpr int MB = D / 32;
+  constexpr int DC = D / 16;
 
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::BUF];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int lane = threadIdx.x;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
-
-  int b, hkv, kbeg, kend, split = 0;
-  int hq[NB], pos[NB];
-  bool colv[NB];
-  int wave_minpos, wave_maxpos;
-  bool wave_rows;
-
-  if constexpr (!SPLIT) {
-    const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
-    const int ptile = a.n_ptiles - 1 - (W % a.n_ptiles);   // longest causal tiles first
-    int rest = W / a.n_ptiles;
-    const int hgrp = rest % a.n_hgroups;
-    rest /= a.n_hgroups;
-    hkv = rest % a.Hkv;
-    b = rest / a.Hkv;
-    const int head = hkv * a.g + hgrp * a.hw + (wid % a.hw);
-    const int p0 = ptile * a.rows_per_wg + QW * (wid / a.hw);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      hq[nb] = head;
-      pos[nb] = p0 + 32 * nb + l32;
-      colv[nb] = pos[nb] < a.Sq;
-    }
-    wave_rows = p0 < a.Sq;
-    wave_minpos = p0;
-    wave_maxpos = min(p0 + QW - 1, a.Sq - 1);
-    const int wg_last = min((ptile + 1) * a.rows_per_wg, a.Sq) - 1;
-    kbeg = 0;
-    kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
-  } else {
-    const int W = blockIdx.x;
-    split = W % a.nsplit;
-    const int rest = W / a.nsplit;
-    hkv = rest % a.Hkv;
-    b = rest / a.Hkv;
-    // column n packs (query head of the group, position): n = hg * Sq + position
-    const int n = l32;
-    colv[0] = n < a.g * a.Sq;
-    hq[0] = hkv * a.g + (colv[0] ? n / a.Sq : 0);
-    pos[0] = colv[0] ? n % a.Sq : 0;
-    wave_rows = true;
-    wave_minpos = 0;
-    wave_maxpos = a.Sq - 1;
-    kbeg = split * a.split_keys;
-    kend = min(a.Sk, kbeg + a.split_keys);
-    if (a.causal) kend = min(kend, a.Sq - 1 + off + 1);
-  }
+  const int W = blockIdx.x;
+  const int split = W % a.nsplit;
+  const int rest = W / a.nsplit;
+  const int hkv = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  // column n packs (query head of the group, query row): n = hg * Sq + row
+  const bool colv = l32 < a.g * a.Sq;
+  const int hq = hkv * a.g + (colv ? l32 / a.Sq : 0);
+  const int pos = colv ? l32 % a.Sq : 0;
+  const int kbeg = split * a.split_keys;
+  int kend = min(a.Sk, kbeg + a.split_keys);
+  if (a.causal) kend = min(kend, a.Sq - 1 + off + 1);
   if (kend < kbeg) kend = kbeg;
   const int ntiles = (kend - kbeg + BC - 1) / BC;
-  // keys this wavefront must process, and the first key that some of its rows cannot see
-  int kend_w = a.causal ? min(kend, wave_maxpos + off + 1) : kend;
-  if (!wave_rows) kend_w = kbeg;
-  const int mask_from = a.causal ? min(kend, wave_minpos + off + 1) : kend;
+  const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
+  const int mask_from = a.causal ? max(kbeg, min(kend, off + 1)) : kend;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds row pos, d = 16*dc + 8*hi .. +7
-  bf16x8 qf[NB][DC];
+  bf16x8 qf[DC];
+  {
+    const bf16* qp = a.q + (((size_t)b * a.Hq + hq) * a.Sq + pos) * D;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const bf16* qp = a.q + (((size_t)b * a.Hq + hq[nb]) * a.Sq + (colv[nb] ? pos[nb] : 0)) * D;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (colv[nb]) {
-        qf[nb][dc] = *(const bf16x8*)(qp + 16 * dc + 8 * hi);
-      } else {
-        qf[nb][dc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      }
-    }
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
-
   const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
   const bf16* vg = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
 
@@ -153,7 +402,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int key0 = kbeg + t * BC;
 #pragma unroll
     for (int i = 0; i < CH_THR; ++i) {
-      const int c = tid + i * NT;
+      const int c = lane + i * 64;
       const int row = c / CH_ROW;
       const int col = c % CH_ROW;
       const int key = key0 + row;
@@ -171,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     bf16* sv = sk + T::K_ELEMS;
 #pragma unroll
     for (int i = 0; i < CH_THR; ++i) {
-      const int c = tid + i * NT;
+      const int c = lane + i * 64;
       const int row = c / CH_ROW;
       const int col = c % CH_ROW;
       *(u32x4*)(sk + row * T::KS + col * 8) = kreg[i];
@@ -179,403 +428,97 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  f32x16 acc[MB][NB];
-  float m2[NB], lsum[NB];
+  f32x16 acc[MB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m2[nb] = kNegInf;
-    lsum[nb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = f32x16{};
-  }
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+  float m2 = kNegInf, lsum = 0.f;
 
   if (ntiles > 0) {
     load_tile(0);
     store_tile(0);
   }
+  const int L = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
     const int cur = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
     const int key0 = kbeg + t * BC;
-    if (key0 < kend_w) {
-      const bf16* sk = smem + cur * T::BUF;
-      const bf16* sv = sk + T::K_ELEMS;
-      // ---- scores S^T = K Q^T: rows = 64 keys (2 blocks), columns = query rows
-      f32x16 s[2][NB];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[kb][nb] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ak = *(const bf16x8*)(sk + (32 * kb + l32) * T::KS + 16 * dc + 8 * hi);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma32(ak, qf[nb][dc], s[kb][nb]);
-        }
-      }
-      // ---- mask (diagonal and ragged tiles only), before the max
-      if (key0 + BC > mask_from) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int lim = a.causal ? min(kend - 1, pos[nb] + off) : kend - 1;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-              if (key > lim) s[kb][nb][i] = kNegInf;
-            }
-          }
-      }
-      // ---- online softmax update
-      bf16x8 pf[4][NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = s[0][nb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][nb][i]);
-        mx = max_halves(mx);
-        const float mnew = fmaxf(m2[nb], mx * a.c);
-        const bool grow = mnew > m2[nb];
-        if (wave_any(grow)) {
-          const float alpha = grow ? fast_exp2(m2[nb] - mnew) : 1.f;
-          lsum[nb] *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][nb] *= alpha;
-        }
-        m2[nb] = mnew;
-        const float msub = (mnew == kNegInf) ? 0.f : mnew;
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = fast_exp2(__builtin_fmaf(s[kb][nb][8 * h + e], a.c, -msub));
-              ps += p[e];
-            }
-            pf[2 * kb + h][nb] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          }
-        lsum[nb] += ps;
-      }
-      // ---- O^T += V^T P^T: rows = d, columns = query rows, reduction over 64 keys
-      const int L = lane & 15;
-      const int dhalf = (lane >> 4) & 1;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16* vp = sv + (16 * kc + 4 * hi + (L >> 2)) * T::VS + 32 * mb + 16 * dhalf + 4 * (L & 3);
-          const bf16x8 av = cat4(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS));
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(av, pf[kc][nb], acc[mb][nb]);
-        }
-      }
-    }
-    if (t + 1 < ntiles) store_tile(cur ^ 1);
-  }
-
-  // ---- epilogue: O = u / l, lse = ln(2) * (m2 + log2 l)
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float lt = sum_halves(lsum[nb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_v = lt > 0.f ? (m2[nb] + __log2f(lt)) * kLn2 : kNegInf;
-    if (!colv[nb]) continue;
-    if constexpr (!SPLIT) {
-      bf16* op = a.o + (((size_t)b * a.Hq + hq[nb]) * a.Sq + pos[nb]) * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 r;
-          r[0] = (bf16)(acc[mb][nb][4 * q4 + 0] * inv);
-          r[1] = (bf16)(acc[mb][nb][4 * q4 + 1] * inv);
-          r[2] = (bf16)(acc[mb][nb][4 * q4 + 2] * inv);
-          r[3] = (bf16)(acc[mb][nb][4 * q4 + 3] * inv);
-          *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi) = r;
-        }
-      if (a.lse != nullptr && hi == 0) a.lse[((size_t)b * a.Hq + hq[nb]) * a.Sq + pos[nb]] = lse_v;
-    } else {
-      const size_t row = (((size_t)split * a.B + b) * a.Hq + hq[nb]) * a.Sq + pos[nb];
-      float* pp = a.part_o + row * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 r;
-          r[0] = acc[mb][nb][4 * q4 + 0] * inv;
-          r[1] = acc[mb][nb][4 * q4 + 1] * inv;
-          r[2] = acc[mb][nb][4 * q4 + 2] * inv;
-          r[3] = acc[mb][nb][4 * q4 + 3] * inv;
-          *(f32x4*)(pp + 32 * mb + 8 * q4 + 4 * hi) = r;
-        }
-      if (hi == 0) a.part_lse[row] = lse_v;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined prefill kernel.
-//
-// Workgroup = 4 wavefronts x 64 query rows (two 32-column MFMA blocks each).
-// Key/value tiles of 64 keys are copied HBM -> LDS by the DMA path of
-// global_load_lds (no staging registers) into a ring of 4 stages, issued two
-// tiles ahead. Iteration j computes S(j) = K_j Q^T, then issues the P V
-// product of tile j-1, then runs the softmax of tile j on the vector ALU while
-// those MFMAs execute; the accumulator is rescaled only when some row's max
-// grew by more than RESCALE_T (log2 units), so rescales are rare and the
-// probabilities stay below 2^RESCALE_T. u / l is unchanged by the choice of
-// reference max, so the result is the same as rescaling on every increase.
-// LDS tiles are unpadded [64][D] bf16 rows whose 16-byte chunks are XOR
-// swizzled: K by (row & 7) for conflict-free 16-byte row reads, V by
-// 2*(row & 3) for conflict-free transposed reads.
-// ---------------------------------------------------------------------------
-constexpr float RESCALE_T = 8.0f;
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-__device__ __forceinline__ void dma16(const void* g, lds_void* l) {
-  __builtin_amdgcn_global_load_lds((glb_void*)g, l, 16, 0, 0);
-}
-
-template <int D>
-struct Ring {
-  static constexpr int BC = 64;
-  static constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
-  static constexpr int STAGE = 2 * TILE;        // K then V
-  static constexpr int NSTAGE = 4;
-  static constexpr int INSTR = D / 32;          // DMA instructions per wavefront per tensor per tile
-};
-
-template <int D, int NB>
-__global__ __launch_bounds__(256) void fwd_prefill_kernel(FwdArgs a) {
-  using R = Ring<D>;
-  constexpr int BC = R::BC;
-  constexpr int QW = 32 * NB;
-  constexpr int MB = D / 32;
-  constexpr int DC = D / 16;
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int RB = 2 * D;                     // bytes per row
-
-  __shared__ __attribute__((aligned(1024))) char smem[R::NSTAGE * R::STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
-
-  const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
-  const int ptile = a.n_ptiles - 1 - (W % a.n_ptiles);   // longest causal tiles first
-  int rest = W / a.n_ptiles;
-  const int hgrp = rest % a.n_hgroups;
-  rest /= a.n_hgroups;
-  const int hkv = rest % a.Hkv;
-  const int b = rest / a.Hkv;
-  const int head = hkv * a.g + hgrp * a.hw + (wid % a.hw);
-  const int p0 = ptile * a.rows_per_wg + QW * (wid / a.hw);
-  int pos[NB];
-  bool colv[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    pos[nb] = p0 + 32 * nb + l32;
-    colv[nb] = pos[nb] < a.Sq;
-  }
-  const int wg_last = min((ptile + 1) * a.rows_per_wg, a.Sq) - 1;
-  int kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
-  if (kend < 0) kend = 0;
-  const int ntiles = (kend + BC - 1) / BC;
-  const int wave_maxpos = min(p0 + QW - 1, a.Sq - 1);
-  int kend_w = a.causal ? min(kend, wave_maxpos + off + 1) : kend;
-  if (p0 >= a.Sq || kend_w < 0) kend_w = 0;
-  const int nt_w = (kend_w + BC - 1) / BC;      // tiles this wavefront computes (a prefix)
-  const int mask_from = a.causal ? max(0, min(kend, p0 + off + 1)) : kend;
-
-  // Q fragments: B operand of S^T = K Q^T (column = query row, d = 16*dc + 8*hi .. +7)
-  bf16x8 qf[NB][DC];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const bf16* qp = a.q + (((size_t)b * a.Hq + head) * a.Sq + (colv[nb] ? pos[nb] : 0)) * D;
+    const bf16* sk = smem + cur * T::BUF;
+    const bf16* sv = sk + T::K_ELEMS;
+    f32x16 s[2];
+    s[0] = s[1] = f32x16{};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      qf[nb][dc] = colv[nb] ? *(const bf16x8*)(qp + 16 * dc + 8 * hi)
-                            : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  }
-
-  const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-  const bf16* vg = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-
-  // DMA of tile t into stage t % NSTAGE: lane i of instruction n writes LDS chunk
-  // P = (wid*INSTR + n)*64 + i, i.e. row P / CPR, physical chunk P % CPR, which
-  // holds logical chunk (physical ^ swizzle(row)). Rows past kend repeat row kend-1
-  // (finite data whose probabilities are masked to 0).
-  auto issue = [&](int t) {
-    const int key0 = t * BC;
-    char* stage = smem + (t % R::NSTAGE) * R::STAGE;
 #pragma unroll
-    for (int n = 0; n < R::INSTR; ++n) {
-      const int P = (wid * R::INSTR + n) * 64 + lane;
-      const int row = P / CPR;
-      const int phys = P % CPR;
-      const size_t key = (size_t)min(key0 + row, kend - 1);
-      dma16(kg + key * D + (phys ^ (row & 7)) * 8, (lds_void*)(stage + (wid * R::INSTR + n) * 1024));
-      dma16(vg + key * D + (phys ^ ((row & 3) << 1)) * 8,
-            (lds_void*)(stage + R::TILE + (wid * R::INSTR + n) * 1024));
-    }
-  };
-
-  f32x16 acc[MB][NB];
-  float m2[NB], lsum[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m2[nb] = kNegInf;
-    lsum[nb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = f32x16{};
-  }
-  bf16x8 pf[4][NB];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) pf[kc][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
-  const int L = lane & 15;
-  const int dhalf = (lane >> 4) & 1;
-
-  for (int j = 0; j <= ntiles; ++j) {
-    // tile j has landed in LDS for every wavefront (each waits for its own DMA,
-    // the barrier for everybody's); also, every wavefront is done with tile j-2
-    if (j + 1 < ntiles) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * R::INSTR) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if (j + 2 < ntiles) issue(j + 2);
-
-    const char* stK = smem + (j % R::NSTAGE) * R::STAGE;
-    const char* stV = smem + ((j + R::NSTAGE - 1) % R::NSTAGE) * R::STAGE + R::TILE;
-    const int key0 = j * BC;
-    const bool do_s = j < nt_w;
-    const bool do_pv = j >= 1 && j - 1 < nt_w;
-
-    f32x16 s[2][NB];
-    if (do_s) {
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32(*(const bf16x8*)(sk + (32 * kb + l32) * T::KS + 16 * dc + 8 * hi), qf[dc], s[kb]);
+    if (key0 + BC > mask_from) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[kb][nb] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int r = 32 * kb + l32;
-          const bf16x8 ak = *(const bf16x8*)(stK + r * RB + (((2 * dc + hi) ^ (r & 7)) << 4));
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma32(ak, qf[nb][dc], s[kb][nb]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (key > lim) s[kb][i] = kNegInf;
         }
-      }
     }
-    if (do_pv) {
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    mx = max_halves(mx) * a.c;
+    const bool grow = mx > m2 + RESCALE_T;
+    if (wave_any(grow)) {
+      const float mnew = grow ? mx : m2;
+      const float alpha = grow ? fast_exp2(m2 - mnew) : 1.f;
+      lsum *= alpha;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          bf16x4 h[2];
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+      m2 = mnew;
+    }
+    const float msub = (m2 == kNegInf) ? 0.f : m2;
+    bf16x8 pf[4];
+    float ps = 0.f;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int r = 16 * kc + 8 * t + 4 * hi + (L >> 2);
-            const int c = (4 * mb + 2 * dhalf + ((L & 3) >> 1)) ^ ((r & 3) << 1);
-            h[t] = lds_read_tr((const bf16*)(stV + r * RB + (c << 4) + ((L & 1) << 3)));
-          }
-          const bf16x8 av = cat4(h[0], h[1]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(av, pf[kc][nb], acc[mb][nb]);
+      for (int h = 0; h < 2; ++h) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(__builtin_fmaf(s[kb][8 * h + e], a.c, -msub));
+          ps += p[e];
         }
+        pf[2 * kb + h] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       }
-    }
-    if (do_s) {
-      if (key0 + BC > mask_from) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int lim = a.causal ? min(kend - 1, pos[nb] + off) : kend - 1;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-              if (key > lim) s[kb][nb][i] = kNegInf;
-            }
-          }
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = s[0][nb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][nb][i]);
-        mx = max_halves(mx) * a.c;
-        // move the reference max only when the row max grew by more than RESCALE_T
-        const bool grow = mx > m2[nb] + RESCALE_T;
-        if (wave_any(grow)) {
-          const float mnew = grow ? mx : m2[nb];
-          const float alpha = grow ? fast_exp2(m2[nb] - mnew) : 1.f;
-          lsum[nb] *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][nb] *= alpha;
-          m2[nb] = mnew;
-        }
-        const float msub = (m2[nb] == kNegInf) ? 0.f : m2[nb];
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = fast_exp2(__builtin_fmaf(s[kb][nb][8 * h + e], a.c, -msub));
-              ps += p[e];
-            }
-            pf[2 * kb + h][nb] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          }
-        lsum[nb] += ps;
-      }
-    }
-  }
-
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float lt = sum_halves(lsum[nb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_v = lt > 0.f ? (m2[nb] + __log2f(lt)) * kLn2 : kNegInf;
-    if (!colv[nb]) continue;
-    bf16* op = a.o + (((size_t)b * a.Hq + head) * a.Sq + pos[nb]) * D;
+    lsum += ps;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 r;
-        r[0] = (bf16)(acc[mb][nb][4 * q4 + 0] * inv);
-        r[1] = (bf16)(acc[mb][nb][4 * q4 + 1] * inv);
-        r[2] = (bf16)(acc[mb][nb][4 * q4 + 2] * inv);
-        r[3] = (bf16)(acc[mb][nb][4 * q4 + 3] * inv);
-        *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi) = r;
+      for (int kc = 0; kc < 4; ++kc) {
+        const bf16* vp = sv + (16 * kc + 4 * hi + (L >> 2)) * T::VS + 32 * mb + 16 * dhalf + 4 * (L & 3);
+        acc[mb] = mfma32(cat4(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS)), pf[kc], acc[mb]);
       }
-    if (a.lse != nullptr && hi == 0) a.lse[((size_t)b * a.Hq + head) * a.Sq + pos[nb]] = lse_v;
+    if (t + 1 < ntiles) store_tile(cur ^ 1);
   }
+
+  const float lt = sum_halves(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : kNegInf;
+  if (!colv) return;
+  const size_t row = (((size_t)split * a.B + b) * a.Hq + hq) * a.Sq + pos;
+  float* pp = a.part_o + row * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 r;
+      r[0] = acc[mb][4 * q4 + 0] * inv;
+      r[1] = acc[mb][4 * q4 + 1] * inv;
+      r[2] = acc[mb][4 * q4 + 2] * inv;
+      r[3] = acc[mb][4 * q4 + 3] * inv;
+      *(f32x4*)(pp + 32 * mb + 8 * q4 + 4 * hi) = r;
+    }
+  if (hi == 0) a.part_lse[row] = lse_v;
 }
 
 // Merge of the per-slice partial results (the update of §1.2 of the first page
@@ -614,10 +557,19 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
 }
 
 template <int D>
-hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_prefill_d(const FwdArgs& a, bf16* vt, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (a.skp > 0) {
+    timing_begin(s, "transpose_v");
+    hipLaunchKernelGGL((transpose_v_kernel<D>), dim3(a.skp / BC, a.Hkv, a.B), dim3(256), 0, s, a.v, vt,
+                       a.Hkv, a.Sk, a.skp);
+    e = hipGetLastError();
+    timing_end(s);
+    if (e != hipSuccess) return e;
+  }
   timing_begin(s, "fwd_prefill_bf16");
-  hipLaunchKernelGGL((fwd_prefill_kernel<D, 2>), dim3(a.total_wgs), dim3(256), 0, s, a);
-  const hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((fwd_prefill_kernel<D>), dim3(a.total_wgs), dim3(512), 0, s, a);
+  e = hipGetLastError();
   timing_end(s);
   return e;
 }
@@ -625,7 +577,7 @@ hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_split_d(const FwdArgs& a, int rows, hipStream_t s) {
   timing_begin(s, "fwd_split_bf16");
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 1, true>), dim3(a.nsplit * a.B * a.Hkv), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((fwd_split_kernel<D>), dim3(a.nsplit * a.B * a.Hkv), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   timing_end(s);
   if (e != hipSuccess) return e;
@@ -651,6 +603,7 @@ FwdArgs base_args(const Problem& p, const void* q, const void* k, const void* v,
   a.Sk = p.Sk;
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
+  a.skp = ((p.Sk + BC - 1) / BC) * BC;
   a.c = p.scale * kLog2e;
   return a;
 }
@@ -662,9 +615,11 @@ PrefillPlan plan_prefill(const Problem& p) {
   const int g = p.Hq / p.Hkv;
   pl.hw = (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
   pl.n_hgroups = g / pl.hw;
-  pl.rows_per_wg = 4 * 64 / pl.hw;
+  pl.rows_per_wg = 8 * 32 / pl.hw;
   pl.n_ptiles = (p.Sq + pl.rows_per_wg - 1) / pl.rows_per_wg;
   pl.total_wgs = p.B * p.Hkv * pl.n_hgroups * pl.n_ptiles;
+  const size_t skp = (size_t)((p.Sk + BC - 1) / BC) * BC;
+  pl.ws_bytes = (size_t)p.B * p.Hkv * p.d * skp * 2;
   return pl;
 }
 
@@ -673,14 +628,14 @@ SplitPlan plan_split(const Problem& p) {
   const int g = p.Hq / p.Hkv;
   sp.use = (long long)g * p.Sq <= 32;
   if (!sp.use) return sp;
-  const int tiles = (p.Sk + 63) / 64;
+  const int tiles = (p.Sk + BC - 1) / BC;
   const int units = p.B * p.Hkv;
   int ns = (2048 + units - 1) / units;
   ns = std::max(1, std::min(ns, tiles / 4));
   const int tiles_per = std::max(1, (tiles + ns - 1) / ns);
   ns = std::max(1, (tiles + tiles_per - 1) / tiles_per);
   sp.nsplit = ns;
-  sp.split_keys = tiles_per * 64;
+  sp.split_keys = tiles_per * BC;
   const size_t rows = (size_t)p.B * p.Hq * p.Sq;
   const size_t o_bytes = (size_t)ns * rows * p.d * sizeof(float);
   const size_t l_bytes = (size_t)ns * rows * sizeof(float);
@@ -688,21 +643,21 @@ SplitPlan plan_split(const Problem& p) {
   return sp;
 }
 
-hipError_t launch_fwd_prefill_bf16(const Problem& p, const PrefillPlan& pl, const void* q,
-                                   const void* k, const void* v, void* o, float* lse, hipStream_t s) {
+hipError_t launch_fwd_prefill_bf16(const Problem& p, const PrefillPlan& pl, const void* q, const void* k,
+                                   const void* v, void* o, float* lse, void* ws, hipStream_t s) {
   FwdArgs a = base_args(p, q, k, v, o, lse);
   a.hw = pl.hw;
   a.n_hgroups = pl.n_hgroups;
   a.rows_per_wg = pl.rows_per_wg;
   a.n_ptiles = pl.n_ptiles;
   a.total_wgs = pl.total_wgs;
+  a.vt = (const bf16*)ws;
   if (a.total_wgs == 0) return hipSuccess;
-  return p.d == 64 ? launch_prefill_d<64>(a, s) : launch_prefill_d<128>(a, s);
+  return p.d == 64 ? launch_prefill_d<64>(a, (bf16*)ws, s) : launch_prefill_d<128>(a, (bf16*)ws, s);
 }
 
-hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& sp, const void* q,
-                                 const void* k, const void* v, void* o, float* lse, void* ws,
-                                 hipStream_t s) {
+hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& sp, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, void* ws, hipStream_t s) {
   FwdArgs a = base_args(p, q, k, v, o, lse);
   a.nsplit = sp.nsplit;
   a.split_keys = sp.split_keys;

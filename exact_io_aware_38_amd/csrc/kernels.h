@@ -28,10 +28,11 @@ struct PrefillPlan {
   int rows_per_wg;  // query positions per workgroup
   int n_ptiles;     // ceil(Sq / rows_per_wg)
   int total_wgs;
+  size_t ws_bytes;  // workspace for the transposed copy of V
 };
 PrefillPlan plan_prefill(const Problem& p);
 hipError_t launch_fwd_prefill_bf16(const Problem& p, const PrefillPlan& plan, const void* q,
-                                   const void* k, const void* v, void* o, float* lse,
+                                   const void* k, const void* v, void* o, float* lse, void* ws,
                                    hipStream_t s);
 
 // Split-key decode: every workgroup runs the recurrence over one slice of the

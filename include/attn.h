@@ -70,9 +70,10 @@ enum attn_status {
 enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
 
 /* Bytes of device workspace attn_fwd needs for these arguments (0 if none).
- * The split-key decode path (few query rows per KV head, e.g. Sq = 1) keeps
- * per-split partial results there. Returns 0 for invalid arguments too; the
- * call itself then reports the error. */
+ * ATTN_BF16 prefill keeps a transposed copy of V there (B*Hkv*d*Sk' bf16,
+ * Sk' = Sk rounded up to 64); the split-key decode path (Hq/Hkv * Sq <= 32,
+ * e.g. one query row) keeps per-split partial results there. ATTN_F32 needs
+ * none. Returns 0 for invalid arguments too; the call then reports the error. */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                 int causal, int dtype);
 
