@@ -11,8 +11,9 @@ own sub-objects. Inputs are resident in device memory before timing starts.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration          (a plain copy of known size,
                                                     for counter calibration)
-       python bench.py --summarize-counters DIR    (turn rocprofv3 --pmc output
-                                                    into profiles/ summaries)
+       python bench.py --summarize-counters WORKLOAD FETCH_DIR WRITE_DIR
+                       COPY_FETCH_DIR COPY_WRITE_DIR   (turn rocprofv3 --pmc
+                       output into per-kernel HBM-traffic summaries in profiles/)
 """
 from __future__ import annotations
 
@@ -42,14 +43,16 @@ KERNEL_SOURCES = {
     "bwd_dkdv": ["bwd_bf16.hip", "common.h"],
     "bwd_dq": ["bwd_bf16.hip", "common.h"],
     "bwd_pre": ["bwd_bf16.hip"],
+    "transpose_v": ["fwd_bf16.hip"],
 }
-# substrings of the mangled device symbols, as rocprofv3 reports them
+# substrings of the (demangled) device kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {
-    "fwd_prefill_bf16": "fwd_prefill_kernelILi128E",
-    "fwd_split_bf16": "fwd_split_kernelILi128E",
-    "bwd_dkdv": "bwd_dkdv_kernelILi128E",
-    "bwd_dq": "bwd_dq_kernelILi128E",
-    "bwd_pre": "bwd_pre_kernelILi128E",
+    "fwd_prefill_bf16": "fwd_prefill_kernel<128>",
+    "fwd_split_bf16": "fwd_split_kernel<128>",
+    "bwd_dkdv": "bwd_dkdv_kernel<128>",
+    "bwd_dq": "bwd_dq_kernel<128>",
+    "bwd_pre": "bwd_pre_kernel<128>",
+    "transpose_v": "transpose_v_kernel<128>",
 }
 
 
@@ -94,9 +97,13 @@ def kernel_work(kernel: str, w) -> dict:
     return {"bound": "mfma", "flops": 0.0}
 
 
-def traffic_for(kernel: str):
+def counters_path(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"counters_{kernel}__{workload}.json")
+
+
+def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from stored counters, or None if absent or stale."""
-    path = os.path.join(PROFILES, f"counters_{kernel}.json")
+    path = counters_path(kernel, workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -115,7 +122,7 @@ def roofline(kernel: str, w, avg_ms: float) -> dict:
         ach = work["bytes"] / (avg_ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     return {"kernel": kernel, "bound": work["bound"], "achieved": round(ach, 2), "peak": peak,
-            "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic_for(kernel),
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic_for(kernel, w.name),
             "avg_launch_ms": round(avg_ms, 4)}
 
 
@@ -259,8 +266,8 @@ def _read_counter_csv(d: str):
     return rows
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
-                       command: str) -> None:
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                       copy_write_dir: str, command: str) -> None:
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel by the
     ratio a plain 1 GiB copy reads for the same counters, and store per-kernel
     HBM bytes per launch under profiles/."""
@@ -293,13 +300,13 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy
             continue
         f_kib = sorted(fk)[len(fk) // 2]
         w_kib = sorted(wk)[len(wk) // 2]
-        out = {"kernel": kern, "source_sha": source_hash(kern),
+        out = {"kernel": kern, "workload": workload, "source_sha": source_hash(kern),
                "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
                "copy_calibration": {"bytes": 1 << 30, "fetch_kib": fcopy, "write_kib": wcopy,
                                     "fetch_factor": ff, "write_factor": wf},
                "hbm_bytes_per_launch": int(f_kib * 1024 * ff + w_kib * 1024 * wf),
                "command": command}
-        with open(os.path.join(PROFILES, f"counters_{kern}.json"), "w") as f:
+        with open(counters_path(kern, workload), "w") as f:
             json.dump(out, f, indent=1)
         print(kern, out["hbm_bytes_per_launch"])
 
@@ -312,7 +319,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "step", "fwd", "decode"], default="all")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--summarize-counters", nargs=5,
+                    metavar=("WORKLOAD", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
