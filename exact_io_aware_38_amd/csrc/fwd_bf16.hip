@@ -182,6 +182,15 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    // Re-define the fragments after they arrived: the compiler then knows no
+    // load is pending on them inside the loop, where a wait on the memory
+    // counter would also wait for the K/V prefetch in flight.
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      u32x4 t = __builtin_bit_cast(u32x4, qf[dc]);
+      asm volatile("" : "+v"(t));
+      qf[dc] = __builtin_bit_cast(bf16x8, t);
+    }
   }
   const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
   const bf16* vtg = a.vt + ((size_t)b * a.Hkv + hkv) * (size_t)D * a.skp;
@@ -199,19 +208,23 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
     const int vrow = P / 8;
     voff[n] = vrow * a.skp + ((P % 8) ^ vt_swizzle(vrow)) * 8;
   }
-  auto issue = [&](int t) {
+  // DMA instruction q (0 .. 2*INSTR-1) of tile t: K for even q, V^T for odd q.
+  auto issue_one = [&](int t, int q) {
     const int key0 = t * BC;
     char* stage = smem + (t % R::NSTAGE) * R::STAGE;
-    const bf16* kt = kg + (size_t)key0 * D;
-    const bool full = key0 + BC <= kend;
-#pragma unroll
-    for (int n = 0; n < R::INSTR; ++n) {
+    const int n = q >> 1;
+    if ((q & 1) == 0) {
       // rows past kend repeat row kend-1 (finite data; their probabilities are masked to 0)
-      const bf16* ks = full ? kt + krow[n] * D + koff[n]
-                            : kg + (size_t)min(key0 + krow[n], kend - 1) * D + koff[n];
+      const bf16* ks = (key0 + BC <= kend) ? kg + (size_t)key0 * D + krow[n] * D + koff[n]
+                                           : kg + (size_t)min(key0 + krow[n], kend - 1) * D + koff[n];
       dma16(ks, (lds_void*)(stage + (wid * R::INSTR + n) * 1024));
+    } else {
       dma16(vtg + key0 + voff[n], (lds_void*)(stage + R::TILE + (wid * R::INSTR + n) * 1024));
     }
+  };
+  auto issue = [&](int t) {
+#pragma unroll
+    for (int q = 0; q < 2 * R::INSTR; ++q) issue_one(t, q);
   };
 
   f32x16 acc[MB];
@@ -219,45 +232,48 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
   float m2 = kNegInf, lsum = 0.f;
   bf16x8 pf[4];
-  // scores of the current tile, split over even and odd d-chunks: four
-  // independent MFMA accumulation chains instead of two (a dependent MFMA
-  // waits ~150 cycles for its predecessor)
-  f32x16 s[2][2];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) pf[kc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  f32x16 s[2];
 
-  // One basic block of MFMAs: S(j) = K_j Q^T (16, four chains) interleaved with
-  // O^T += V_{j-1}^T P_{j-1}^T (16, MB chains), so that no chain's next MFMA
-  // issues within eight MFMAs of its previous one.
-  auto mma = [&](auto do_s, auto do_pv, int j) {
+  // One basic block of MFMAs: S(j) = K_j Q^T (16 MFMAs, 2 chains) interleaved
+  // one-for-one with O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs, MB chains); with the
+  // two products alternating, a chain's next MFMA issues at least four MFMAs
+  // after its previous one (a dependent MFMA waits ~150 cycles for its
+  // predecessor). LDS operand fragments are loaded two pairs ahead so that
+  // their latency is covered by the MFMAs in between.
+  auto mma = [&](auto do_s, auto do_pv, int j, int dma_tile) {
     const char* stK = smem + (j % R::NSTAGE) * R::STAGE;
     const char* stV = smem + ((j + R::NSTAGE - 1) % R::NSTAGE) * R::STAGE + R::TILE;
+    constexpr int NP = 2 * DC;                 // MFMA pairs (= 4 * MB for the PV half)
+    auto kfrag = [&](int i) {                  // pair i: kb = i & 1, dc = i >> 1
+      const int r = 32 * (i & 1) + l32;
+      return *(const bf16x8*)(stK + r * RB + (((2 * (i >> 1) + hi) ^ chunk_swizzle<D>(r)) << 4));
+    };
+    auto vfrag = [&](int i) {                  // pair i: mb = i % MB, kc = i / MB
+      const int d = 32 * (i % MB) + l32;
+      return *(const bf16x8*)(stV + d * (2 * BC) + (((2 * (i / MB) + hi) ^ vt_swizzle(d)) << 4));
+    };
+    bf16x8 kq[3], vq[3];
     if constexpr (do_s.value) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb][0] = s[kb][1] = f32x16{};
+      s[0] = s[1] = f32x16{};
+      kq[0] = kfrag(0);
+      kq[1] = kfrag(1);
     }
-    constexpr int PV_PER_DC = (MB * 4) / DC;   // PV MFMAs issued per d-chunk step
+    if constexpr (do_pv.value) {
+      vq[0] = vfrag(0);
+      vq[1] = vfrag(1);
+    }
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if constexpr (do_s.value) {
-          const int r = 32 * kb + l32;
-          const bf16x8 ak = *(const bf16x8*)(stK + r * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(r)) << 4));
-          s[kb][dc & 1] = mfma32(ak, qf[dc], s[kb][dc & 1]);
-        }
-        if constexpr (do_pv.value) {
-#pragma unroll
-          for (int u = 0; u < PV_PER_DC / 2; ++u) {
-            const int p = dc * PV_PER_DC + kb * (PV_PER_DC / 2) + u;
-            const int mb = p % MB;
-            const int kc = p / MB;
-            const int d = 32 * mb + l32;
-            const bf16x8 av = *(const bf16x8*)(stV + d * (2 * BC) + (((2 * kc + hi) ^ vt_swizzle(d)) << 4));
-            acc[mb] = mfma32(av, pf[kc], acc[mb]);
-          }
-        }
+    for (int i = 0; i < NP; ++i) {
+      if (i + 2 < NP) {
+        if constexpr (do_s.value) kq[(i + 2) % 3] = kfrag(i + 2);
+        if constexpr (do_pv.value) vq[(i + 2) % 3] = vfrag(i + 2);
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads two pairs ahead of their MFMAs
+      if constexpr (do_s.value) s[i & 1] = mfma32(kq[i % 3], qf[i >> 1], s[i & 1]);
+      if constexpr (do_pv.value) acc[i % MB] = mfma32(vq[i % 3], pf[i / MB], acc[i % MB]);
+      // the prefetch of a later tile rides in the shadow of the MFMAs
+      constexpr int EVERY = NP / (2 * R::INSTR);
+      if (i % EVERY == EVERY - 1 && dma_tile >= 0) issue_one(dma_tile, i / EVERY);
     }
   };
   auto softmax = [&](int j) {
@@ -265,8 +281,8 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
     float v[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      v[i] = s[0][0][i] + s[0][1][i];
-      v[16 + i] = s[1][0][i] + s[1][1][i];
+      v[i] = s[0][i];
+      v[16 + i] = s[1][i];
     }
     if (key0 + BC > mask_from) {
 #pragma unroll
@@ -308,16 +324,18 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
     } else {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (j + 2 < ntiles) issue(j + 2);
+    const int dma_tile = (j + 2 < ntiles) ? j + 2 : -1;
     const bool ds = j < nt_w;                  // scores of tile j
     const bool dp = j >= 1 && j - 1 < nt_w;    // P V of tile j-1
     if (phase_b && dp) softmax(j - 1);
     if (ds && dp) {
-      mma(T_{}, T_{}, j);
+      mma(T_{}, T_{}, j, dma_tile);
     } else if (ds) {
-      mma(T_{}, F_{}, j);
+      mma(T_{}, F_{}, j, dma_tile);
     } else if (dp) {
-      mma(F_{}, T_{}, j);
+      mma(F_{}, T_{}, j, dma_tile);
+    } else if (dma_tile >= 0) {
+      issue(dma_tile);
     }
     if (!phase_b && ds) softmax(j);
   }
