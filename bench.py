@@ -38,12 +38,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # kernel name -> source files whose content defines it (for counter staleness)
 KERNEL_SOURCES = {
-    "fwd_prefill_bf16": ["fwd_bf16.hip", "common.h"],
-    "fwd_split_bf16": ["fwd_bf16.hip", "common.h"],
-    "bwd_dkdv": ["bwd_bf16.hip", "common.h"],
-    "bwd_dq": ["bwd_bf16.hip", "common.h"],
+    "fwd_prefill_bf16": ["fwd_bf16.hip", "common.h", "tiles.h"],
+    "fwd_split_bf16": ["fwd_bf16.hip", "common.h", "tiles.h"],
+    "bwd_dkdv": ["bwd_bf16.hip", "common.h", "tiles.h"],
+    "bwd_dq": ["bwd_bf16.hip", "common.h", "tiles.h"],
     "bwd_pre": ["bwd_bf16.hip"],
-    "transpose_v": ["fwd_bf16.hip"],
+    "transpose_rows": ["tiles.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {
@@ -52,7 +52,7 @@ KERNEL_SYMBOLS = {
     "bwd_dkdv": "bwd_dkdv_kernel<128>",
     "bwd_dq": "bwd_dq_kernel<128>",
     "bwd_pre": "bwd_pre_kernel<128>",
-    "transpose_v": "transpose_v_kernel<128>",
+    "transpose_rows": "transpose_rows_kernel<128>",
 }
 
 

@@ -24,9 +24,13 @@ ARCH = "gfx950"
 # Packed fp32 arithmetic is switched off for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # keep MFMA results in ordinary VGPRs instead of shuttling them through AGPRs
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+# Forward kernels: keep MFMA results in ordinary VGPRs instead of shuttling
+# them through AGPRs (everything fits in 256 VGPRs, and the softmax reads the
+# scores every tile). The backward kernels need more than 256 registers per
+# lane; there the accumulators that only MFMAs touch are best left in AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+PER_SOURCE = {"fwd_bf16.hip": VGPR_FORM, "fwd_f32.hip": VGPR_FORM}
 
 
 def _hipcc() -> str:
@@ -44,7 +48,7 @@ KERNEL_ONLY = ["-fno-honor-nans"]
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    extra = KERNEL_ONLY if src.endswith(".hip") else []
+    extra = (KERNEL_ONLY if src.endswith(".hip") else []) + PER_SOURCE.get(src, [])
     cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

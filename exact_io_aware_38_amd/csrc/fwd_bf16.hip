@@ -31,6 +31,7 @@
 //    per score.
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -41,34 +42,6 @@ namespace {
 
 constexpr float RESCALE_T = 8.0f;   // log2 units
 constexpr int BC = 64;               // keys per tile
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-// 16 bytes per lane from global memory straight into LDS at base + 16 * lane
-// (base must be wave-uniform). Issued as inline assembly: the compiler would
-// otherwise make every later LDS read wait for all outstanding DMA (it cannot
-// tell the ring stages apart), which serialises the prefetch; the kernels wait
-// for their DMA explicitly (s_waitcnt vmcnt + s_barrier) before reading a stage.
-__device__ __forceinline__ void dma16(const void* g, lds_void* base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(g)
-               : "memory", "m0");
-}
-
-// Swizzle of the 8 16-byte chunks of a 128-byte V^T row (conflict-free
-// 16-byte reads of 16 consecutive rows at one logical chunk).
-__device__ __forceinline__ int vt_swizzle(int row) { return (row >> 1) & 7; }
-
-// Position of key k inside its group of 16 in a V^T row: key 8a + 4h + e is
-// stored at 8h + 4a + e, so that lane half h finds its 8 MFMA reduction slots
-// (keys 8a + 4h + e, a in {0,1}, e in 0..3) in one contiguous 16-byte chunk.
-// The map swaps two bits, so it is its own inverse.
-__device__ __forceinline__ int vt_perm(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
 
 struct FwdArgs {
   const bf16* q;
@@ -85,41 +58,6 @@ struct FwdArgs {
   int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
   int nsplit, split_keys;
 };
-
-// ---------------------------------------------------------------------------
-// V [B, Hkv, Sk, D] -> V^T [B, Hkv, D, skp] with keys permuted by vt_perm
-// inside each group of 16 and zero padding past Sk. One workgroup per
-// (64-key tile, KV head, batch).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16* __restrict__ v, bf16* __restrict__ vt,
-                                                          int Hkv, int Sk, int skp) {
-  constexpr int S = D + 2;                       // odd word stride: column reads spread over banks
-  __shared__ bf16 tile[BC * S];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * BC;
-  const size_t head = (size_t)blockIdx.z * Hkv + blockIdx.y;
-  const bf16* src = v + head * (size_t)Sk * D;
-  for (int c = tid; c < BC * D / 8; c += 256) {
-    const int row = c / (D / 8);
-    const int col = (c % (D / 8)) * 8;
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (t0 + row < Sk) val = *(const u32x4*)(src + (size_t)(t0 + row) * D + col);
-    const bf16x8 e = __builtin_bit_cast(bf16x8, val);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[row * S + col + i] = e[i];
-  }
-  __syncthreads();
-  bf16* dst = vt + head * (size_t)D * skp + t0;
-  for (int c = tid; c < D * (BC / 8); c += 256) {
-    const int d = c / (BC / 8);
-    const int ch = c % (BC / 8);
-    bf16x8 e;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = tile[vt_perm(8 * ch + j) * S + d];
-    *(bf16x8*)(dst + (size_t)d * skp + 8 * ch) = e;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Prefill: 8 wavefronts (two per SIMD) x 32 query rows per workgroup.
@@ -579,7 +517,7 @@ hipError_t launch_prefill_d(const FwdArgs& a, bf16* vt, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (a.skp > 0) {
     timing_begin(s, "transpose_v");
-    hipLaunchKernelGGL((transpose_v_kernel<D>), dim3(a.skp / BC, a.Hkv, a.B), dim3(256), 0, s, a.v, vt,
+    hipLaunchKernelGGL((transpose_rows_kernel<D>), dim3(a.skp / BC, a.Hkv, a.B), dim3(256), 0, s, a.v, vt,
                        a.Hkv, a.Sk, a.skp);
     e = hipGetLastError();
     timing_end(s);
