@@ -46,7 +46,20 @@ namespace {
 
 constexpr int BT = 32;        // rows of a pipeline tile (queries for dK/dV, keys for dQ)
 constexpr int KV_WG = 128;    // keys per dK/dV workgroup (4 wavefronts x 32)
-constexpr int Q_WG = 128;     // queries per dQ workgroup
+constexpr int Q_WG = 256;     // queries per dQ workgroup (4 wavefronts x 64)
+
+// Pins where values are computed: results that are only consumed in the next
+// pipeline step would otherwise all be computed in one block just before the
+// step boundary (instruction selection places pure arithmetic next to its
+// first chained use), instead of interleaved with the MFMAs they should hide
+// behind. The empty volatile statement forces them to exist at this point.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x, float& y) { asm volatile("" : "+v"(x), "+v"(y)); }
+__device__ __forceinline__ void pin(bf16x8& x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(w));
+  x = __builtin_bit_cast(bf16x8, w);
+}
 
 struct BwdArgs {
   const bf16* q;
@@ -143,8 +156,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // dP = dO V^T (rows = 32 queries) take K and V from registers; dV^T += dO^T P
 // and dK^T += Q^T dS (rows = d) take P and dS straight from the score
 // accumulators, which already have the B-operand layout.
+//
+// LDS rings (4 slots each, so that a step's slot offsets are compile-time
+// constants once the loop is unrolled by 4): [Q | dO] row tiles of tile t are
+// loaded in step t-3 and read in step t-1, [Q^T | dO^T] in step t-2 and read
+// in step t+1, lse2/D in step t-3 and read in step t.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
@@ -152,12 +170,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;                    // 16-byte chunks per row
   constexpr int TB = BT * D * 2;                // bytes of a 32-row tile, row-major or transposed
   constexpr int INSTR = TB / 4096;              // DMA instructions per wavefront per tensor
-  constexpr int NDMA = 4 * INSTR + 1;           // ... per tile: Q, dO, Q^T, dO^T, lse2/D
-  constexpr int NQ = 3, NT = 5, NL = 4;         // ring slots
-  constexpr int T_OFF = NQ * 2 * TB;
-  constexpr int L_OFF = T_OFF + NT * 2 * TB;
+  constexpr int NDMA = 4 * INSTR + 1;           // ... per step: Q, dO, Q^T, dO^T, lse2/D
+  constexpr int RING = 4;
+  constexpr int T_OFF = RING * 2 * TB;
+  constexpr int L_OFF = 2 * T_OFF;
+  constexpr int LB = 2 * BT * 4;                // bytes of lse2/D per tile
   static_assert(NOPS >= NDMA, "one DMA per step at most");
-  __shared__ __attribute__((aligned(1024))) char smem[L_OFF + NL * 2 * BT * 4];
+  __shared__ __attribute__((aligned(1024))) char smem[L_OFF + RING * LB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,48 +220,99 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int per_head = n_qt - qt_lo;
   const int n = a.g * per_head;                 // pipeline tiles: (query head, 32-row tile)
 
-  // Per-lane DMA geometry of instruction i: LDS chunk P = (wid*INSTR + i)*64 + lane
-  // of a tile; row-major tile: row P / CPR, physical chunk P % CPR; transposed
-  // tile: row P / 4, physical chunk P % 4; each lane loads the logical chunk.
-  // Byte offsets are relative to the head's base (32-bit: a head is < 4 GiB).
-  int rrow[INSTR];
-  uint32_t rcol[INSTR], toff[INSTR];
+  // Per-lane LDS read offsets; ring slots and the constant parts of each
+  // fragment's address become immediate offsets of the reads.
+  uint32_t rb[DC], tb[2];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * (2 * D) + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+#pragma unroll
+  for (int qc = 0; qc < 2; ++qc) tb[qc] = T_OFF + l32 * 64 + (((2 * qc + hi) ^ tr_swizzle(l32)) << 4);
+  const uint32_t lb = L_OFF + 16 * hi;
+
+  // Per-lane DMA offsets of instruction i: LDS chunk P = (wid*INSTR + i)*64 +
+  // lane of a tile; row-major tile: row P / CPR, physical chunk P % CPR;
+  // transposed tile: row P / 4, physical chunk P % 4; each lane loads the
+  // logical chunk (physical ^ swizzle(row)).
+  uint32_t roff[INSTR], toff[INSTR];
 #pragma unroll
   for (int i = 0; i < INSTR; ++i) {
     const int P = (wid * INSTR + i) * 64 + lane;
-    rrow[i] = P / CPR;
-    rcol[i] = ((P % CPR) ^ chunk_swizzle<D>(rrow[i])) * 16;
+    const int rr = P / CPR;
+    roff[i] = rr * (2 * D) + (((P % CPR) ^ chunk_swizzle<D>(rr)) << 4);
     const int tr = P / 4;
     toff[i] = (uint32_t)(tr * a.sqp + ((P & 3) ^ tr_swizzle(tr)) * 8) * 2;
   }
-  auto tile_head = [&](int t) { return hkv * a.g + t / per_head; };
-  auto tile_q0 = [&](int t) { return (qt_lo + t % per_head) * BT; };
-  // DMA instruction qi (0 .. NDMA-1) of tile t into ring slots of tile ts
-  // (ts >= t: past the last tile the last one is loaded again into slots
-  // nobody reads, which keeps the per-step DMA count uniform)
-  auto issue_one = [&](int ts, int hq, int q0, int qi) {
-    const size_t hrow = (size_t)b * a.Hq + hq;
-    if (qi < 2 * INSTR) {                       // Q (qi < INSTR) or dO rows; rows past Sq repeat row Sq-1
-      const int i = qi % INSTR;
-      const bf16* src = ((qi < INSTR) ? a.q : a.dout) + hrow * a.Sq * D;
-      const uint32_t r = (uint32_t)min(q0 + rrow[i], a.Sq - 1);
-      dma16s(src, r * (2 * D) + rcol[i],
-             (lds_void*)(smem + (ts % NQ) * 2 * TB + (qi / INSTR) * TB + (wid * INSTR + i) * 1024));
-    } else if (qi < 4 * INSTR) {                // Q^T or dO^T (zero past Sq)
-      const int i = qi % INSTR;
-      const bf16* src = ((qi < 3 * INSTR) ? a.qt : a.dot) + hrow * D * a.sqp + q0;
-      dma16s(src, toff[i],
-             (lds_void*)(smem + T_OFF + (ts % NT) * 2 * TB + ((qi - 2 * INSTR) / INSTR) * TB +
-                         (wid * INSTR + i) * 1024));
-    } else {                                    // lse2 and D of the 32 rows (every wavefront, same bytes)
-      dma4s(a.ld + (hrow * (a.sqp / BT) + q0 / BT) * (2 * BT), lane * 4,
-            (lds_void*)(smem + L_OFF + (ts % NL) * 2 * BT * 4));
+
+  // Tile sequence: for each query head of the group, the 32-row tiles from
+  // the last one down to the first one that sees a key of this workgroup.
+  // Walking down keeps every workgroup of a head on the same tile at the same
+  // time (they all start at the last tile), so each tile is fetched into L2
+  // once and then served to all of them.
+  // Window over the sequence (query head hq, first row q0): entry k is tile
+  // j+k at the start of step j. Past the last tile the coordinates stay at the
+  // last one: those DMAs reload it into slots nobody reads, which keeps the
+  // per-step DMA count uniform.
+  int whq[4], wq0[4];
+  int idx3 = 2;
+  whq[1] = hkv * a.g;
+  wq0[1] = (n_qt - 1) * BT;
+  auto advance = [&](int& hq, int& q0) __attribute__((always_inline)) {
+    q0 -= BT;
+    if (q0 < qt_lo * BT) {
+      q0 = (n_qt - 1) * BT;
+      ++hq;
     }
   };
-  auto issue = [&](int t) {
-    const int hq = tile_head(t), q0 = tile_q0(t);
-#pragma unroll
-    for (int qi = 0; qi < NDMA; ++qi) issue_one(t, hq, q0, qi);
+  whq[2] = whq[1];
+  wq0[2] = wq0[1];
+  if (n > 1) advance(whq[2], wq0[2]);
+  whq[3] = whq[2];
+  wq0[3] = wq0[2];
+  if (n > 2) advance(whq[3], wq0[3]);
+  whq[0] = whq[1];
+  wq0[0] = wq0[1];
+  auto shift = [&]() __attribute__((always_inline)) {
+    whq[0] = whq[1]; wq0[0] = wq0[1];
+    whq[1] = whq[2]; wq0[1] = wq0[2];
+    whq[2] = whq[3]; wq0[2] = wq0[3];
+    if (idx3 < n - 1) advance(whq[3], wq0[3]);
+    ++idx3;
+  };
+
+  // DMA instruction qi (0 .. NDMA-1): rows (Q, dO) and lse2/D of the tile at
+  // (hq3, q03) into row slot SQ / lse slot SLD, transposed tiles of the tile
+  // at (hq2, q02) into slot STD.
+  struct Dma {
+    u32x4 rq, rd;                               // Q / dO rows from q03 on (rows past Sq read 0)
+    const bf16* tq;                             // Q^T / dO^T columns from q02 on
+    const bf16* td;
+    const float* l;                             // lse2/D block of q03
+  };
+  auto dma_setup = [&](int hq3, int q03, int hq2, int q02) __attribute__((always_inline)) {
+    Dma d;
+    const size_t h3 = (size_t)b * a.Hq + hq3;
+    const size_t h2 = (size_t)b * a.Hq + hq2;
+    const uint32_t rows_left = (uint32_t)(a.Sq - q03) * (2 * D);
+    d.rq = buffer_rsrc(a.q + (h3 * a.Sq + q03) * D, rows_left);
+    d.rd = buffer_rsrc(a.dout + (h3 * a.Sq + q03) * D, rows_left);
+    d.tq = a.qt + h2 * D * a.sqp + q02;
+    d.td = a.dot + h2 * D * a.sqp + q02;
+    d.l = a.ld + (h3 * (a.sqp / BT) + q03 / BT) * (2 * BT);
+    return d;
+  };
+  auto dma_one = [&](const Dma& d, int SQ, int STD, int SLD, int qi) __attribute__((always_inline)) {
+    const int i = qi % INSTR;
+    const int part = (wid * INSTR + i) * 1024;
+    if (qi < INSTR)
+      dma16b(d.rq, roff[i], (lds_void*)(smem + SQ * 2 * TB + part));
+    else if (qi < 2 * INSTR)
+      dma16b(d.rd, roff[i], (lds_void*)(smem + SQ * 2 * TB + TB + part));
+    else if (qi < 3 * INSTR)
+      dma16s(d.tq, toff[i], (lds_void*)(smem + T_OFF + STD * 2 * TB + part));
+    else if (qi < 4 * INSTR)
+      dma16s(d.td, toff[i], (lds_void*)(smem + T_OFF + STD * 2 * TB + TB + part));
+    else                                        // every wavefront loads the same 256 bytes
+      dma4s(d.l, lane * 4, (lds_void*)(smem + L_OFF + SLD * LB));
   };
 
   f32x16 dkt[MB], dvt[MB];
@@ -254,66 +324,61 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   f32x16 s_[2], dp_[2];                         // scores and dP of two tiles in flight
   bf16x8 pf[2][2], dsf[2][2];                   // [tile parity][16-query chunk]
 
-  // MFMA op k (0 .. NOPS-1) of the score group of the tile in ring slot sq:
-  // S (even k) or dP (odd k) over d-chunk k / 2.
-  auto g1_frag = [&](const char* sq, int k) {
-    return row_frag<D>(sq + (k & 1) * TB, l32, 2 * (k >> 1) + hi);
-  };
-  // MFMA op k of the gradient group: chain k % (2 MB) (dV^T for < MB, dK^T
-  // otherwise, d-block k % MB), 16-query chunk k / (2 MB).
-  auto g2_frag = [&](const char* st, int k) {
-    const int ch = k % (2 * MB);
-    const int qc = k / (2 * MB);
-    const int d = 32 * (ch % MB) + l32;
-    return tr_frag(st + (ch < MB ? TB : 0), d, 2 * qc + hi);   // dO^T for dV, Q^T for dK
-  };
-
-  auto step = [&](auto par, auto g1, auto g2, auto ew, int j) {
-    constexpr int P = decltype(par)::value;     // parity of tile j
-    constexpr bool G1 = decltype(g1)::value;    // scores of tile j+1
-    constexpr bool G2 = decltype(g2)::value;    // gradients of tile j-1
-    constexpr bool EW = decltype(ew)::value;    // P, dS of tile j
-    const char* sq = smem + ((j + 1) % NQ) * 2 * TB;
-    const char* st = smem + T_OFF + ((j + NT - 1) % NT) * 2 * TB;
-    const float* sl = (const float*)(smem + L_OFF + (j % NL) * 2 * BT * 4);
-    const int t3 = j + 3;
-    const int t3c = min(t3, n - 1);
-    const int hq3 = tile_head(t3c);
-    const int q03 = tile_q0(t3c);
-    const int q0 = tile_q0(j);
-    const bool need_mask = a.causal && (kw0 + 31 > q0 + off);
-
+  // One step j (slot position POS = j mod 4): score group = S, dP of tile j+1
+  // (op k: S for even k, dP for odd, d-chunk k / 2); gradient group = dV^T,
+  // dK^T of tile j-1 (op k: chain k % 2MB, 16-query chunk k / 2MB); elementwise
+  // = P, dS of tile j; and the DMA of tiles j+2 / j+3.
+  auto step = [&](auto pos_, auto g1, auto g2, auto ew, auto mask_) __attribute__((always_inline)) {
+    constexpr int POS = decltype(pos_)::value;
+    constexpr int P = POS & 1;                  // parity of tile j
+    constexpr bool G1 = decltype(g1)::value;
+    constexpr bool G2 = decltype(g2)::value;
+    constexpr bool EW = decltype(ew)::value;
+    constexpr bool MASK = decltype(mask_)::value;
+    constexpr int SQ = (POS + 1) % RING;        // rows of tile j+1
+    constexpr int ST = (POS + 3) % RING;        // transposed tiles of tile j-1
+    constexpr int SL = POS;                     // lse2/D of tile j
+    const char* lds = smem;
+    auto g1_frag = [&](int k) __attribute__((always_inline)) {
+      return *(const bf16x8*)(lds + rb[k >> 1] + SQ * 2 * TB + (k & 1) * TB);
+    };
+    auto g2_frag = [&](int k) __attribute__((always_inline)) {
+      const int ch = k % (2 * MB);
+      return *(const bf16x8*)(lds + tb[k / (2 * MB)] + ST * 2 * TB + (ch < MB ? TB : 0) + (ch % MB) * 32 * 64);
+    };
+    Dma d;
+    if constexpr (G1) d = dma_setup(whq[3], wq0[3], whq[2], wq0[2]);
+    const int q0 = wq0[0];
     f32x4 l2v[4], dlv[4];
     if constexpr (EW) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        l2v[i4] = *(const f32x4*)(sl + 8 * i4 + 4 * hi);
-        dlv[i4] = *(const f32x4*)(sl + BT + 8 * i4 + 4 * hi);
+        l2v[i4] = *(const f32x4*)(lds + lb + SL * LB + 32 * i4);
+        dlv[i4] = *(const f32x4*)(lds + lb + SL * LB + 4 * BT + 32 * i4);
       }
     }
-    if constexpr (G1) s_[P ^ 1] = dp_[P ^ 1] = f32x16{};
     bf16x8 f1[3], f2[3];
     if constexpr (G1) {
-      f1[0] = g1_frag(sq, 0);
-      f1[1] = g1_frag(sq, 1);
+      f1[0] = g1_frag(0);
+      f1[1] = g1_frag(1);
     }
     if constexpr (G2) {
-      f2[0] = g2_frag(st, 0);
-      f2[1] = g2_frag(st, 1);
+      f2[0] = g2_frag(0);
+      f2[1] = g2_frag(1);
     }
     float pt[8], dt[8];
 #pragma unroll
     for (int i = 0; i < NOPS; ++i) {
       if (i + 2 < NOPS) {
-        if constexpr (G1) f1[(i + 2) % 3] = g1_frag(sq, i + 2);
-        if constexpr (G2) f2[(i + 2) % 3] = g2_frag(st, i + 2);
+        if constexpr (G1) f1[(i + 2) % 3] = g1_frag(i + 2);
+        if constexpr (G2) f2[(i + 2) % 3] = g2_frag(i + 2);
       }
       __builtin_amdgcn_sched_barrier(0);        // keep the reads two MFMAs ahead of their use
       if constexpr (G1) {
         if (i & 1)
-          dp_[P ^ 1] = mfma32(f1[i % 3], vf[i >> 1], dp_[P ^ 1]);
+          dp_[P ^ 1] = mfma32(f1[i % 3], vf[i >> 1], i < 2 ? f32x16{} : dp_[P ^ 1]);
         else
-          s_[P ^ 1] = mfma32(f1[i % 3], kf[i >> 1], s_[P ^ 1]);
+          s_[P ^ 1] = mfma32(f1[i % 3], kf[i >> 1], i < 2 ? f32x16{} : s_[P ^ 1]);
       }
       if constexpr (G2) {
         const int ch = i % (2 * MB);
@@ -332,60 +397,89 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           const float l2 = l2v[v >> 2][v & 3];
           const float dl = dlv[v >> 2][v & 3];
           float p = fast_exp2(__builtin_fmaf(s_[P][v], a.c, -l2));
-          if (need_mask && key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) p = 0.f;
+          if constexpr (MASK) {
+            if (key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) p = 0.f;
+          }
           pt[v & 7] = p;
           dt[v & 7] = p * (dp_[P][v] - dl);
+          pin(pt[v & 7], dt[v & 7]);
           if ((v & 7) == 7) {
             pf[P][v >> 3] = to_bf16x8(pt[0], pt[1], pt[2], pt[3], pt[4], pt[5], pt[6], pt[7]);
             dsf[P][v >> 3] = to_bf16x8(dt[0], dt[1], dt[2], dt[3], dt[4], dt[5], dt[6], dt[7]);
+            pin(pf[P][v >> 3]);
+            pin(dsf[P][v >> 3]);
           }
         }
       }
-      if (i < NDMA && G1) issue_one(t3, hq3, q03, i);
+      if constexpr (G1) {
+        if (i < NDMA) dma_one(d, (POS + 3) % RING, (POS + 2) % RING, (POS + 3) % RING, i);
+      }
     }
+    if constexpr (G1) shift();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-
-  // tiles 0 and 1 now; tile j+3 during step j (tile 2 during the scores of
-  // tile 0). Every step that computes scores issues exactly NDMA DMA
-  // instructions, so "all but the last NDMA" always means "the next tile".
-  if (n > 0) {
-    issue(0);
-    issue(min(1, n - 1));
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
-    // scores of tile 0 (parity 0): a step of parity 1 with only the score group
-    step(P1{}, T_{}, F_{}, F_{}, -1);
-  }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // Causal: every step applies the mask (a branch per tile between masked
+  // and unmasked copies of the step costs more in register shuffling than
+  // the two instructions per score). Without it nothing needs masking: rows
+  // past Sq have lse2 = +inf, so their P and dS are 0.
+  using M_ = std::integral_constant<bool, CAUSAL>;
+  auto full = [&](auto pos_, auto g2) __attribute__((always_inline)) { step(pos_, T_{}, g2, T_{}, M_{}); };
   // step j: tile j+1 has landed for every wavefront (each waits for its own
   // DMA, the barrier for all of them), and every wavefront is done with step j-1
-  auto sync = [&](int j) {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
-  };
+  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
+
   if (n > 0) {
-    sync(0);
-    step(P0{}, T_{}, F_{}, T_{}, 0);
+    // DMA groups of steps -3 and -2 (the transposed tiles of "tile -1" are a
+    // dummy copy of tile 0), then the scores of tile 0 as step -1
+    {
+      const Dma d3 = dma_setup(whq[1], wq0[1], whq[1], wq0[1]);
+#pragma unroll
+      for (int qi = 0; qi < NDMA; ++qi) dma_one(d3, 0, 3, 0, qi);
+      const Dma d2 = dma_setup(whq[2], wq0[2], whq[1], wq0[1]);
+#pragma unroll
+      for (int qi = 0; qi < NDMA; ++qi) dma_one(d2, 1, 0, 1, qi);
+    }
+    sync();
+    step(I3{}, T_{}, F_{}, F_{}, F_{});         // j = -1
+    sync();
+    full(I0{}, F_{});                           // j = 0: no gradients yet
   }
   int j = 1;
-  for (; j + 1 < n; j += 2) {
-    sync(j);
-    step(P1{}, T_{}, T_{}, T_{}, j);
-    sync(j + 1);
-    step(P0{}, T_{}, T_{}, T_{}, j + 1);
+  for (; j + 3 < n; j += 4) {
+    sync();
+    full(I1{}, T_{});
+    sync();
+    full(I2{}, T_{});
+    sync();
+    full(I3{}, T_{});
+    sync();
+    full(I0{}, T_{});
   }
   if (j < n) {
-    sync(j);
-    step(P1{}, T_{}, T_{}, T_{}, j);
-    ++j;
+    sync();
+    full(I1{}, T_{});
   }
-  // gradients of the last tile: a step of parity n with only the gradient group
+  if (j + 1 < n) {
+    sync();
+    full(I2{}, T_{});
+  }
+  if (j + 2 < n) {
+    sync();
+    full(I3{}, T_{});
+  }
+  // gradients of the last tile: a step at position n mod 4 with only the gradient group
   if (n > 0) {
-    if (n & 1)
-      step(P1{}, F_{}, T_{}, F_{}, n);
-    else
-      step(P0{}, F_{}, T_{}, F_{}, n);
+    switch (n & 3) {
+      case 0: step(I0{}, F_{}, T_{}, F_{}, F_{}); break;
+      case 1: step(I1{}, F_{}, T_{}, F_{}, F_{}); break;
+      case 2: step(I2{}, F_{}, T_{}, F_{}, F_{}); break;
+      default: step(I3{}, F_{}, T_{}, F_{}, F_{}); break;
+    }
   }
 
   if (!kvalid) return;
@@ -406,23 +500,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ. Wavefront w owns queries p + 32w .. +31 as MFMA columns: S^T = K Q^T and
-// dP^T = V dO^T (rows = 32 keys) take Q and dO from registers; dQ^T += K^T dS^T
-// (rows = d) takes dS^T from the score accumulators.
+// dQ. Wavefront w owns queries p + 64w .. +63 as two blocks of 32 MFMA
+// columns: S^T = K Q^T and dP^T = V dO^T (rows = 32 keys) take Q and dO from
+// registers, dQ^T += K^T dS^T (rows = d) takes dS^T from the score
+// accumulators; each K, V or K^T fragment read from LDS feeds two MFMAs.
+// Rings as in the dK/dV pass: [K | V] rows of key tile t are loaded in step
+// t-3 and read in step t-1, K^T in step t-2 and read in step t+1.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
-  constexpr int NS = MB * 2;                    // steps: 2 score MFMAs + 1 gradient MFMA each
+  constexpr int NU = DC;                        // units per step: 2 row fragments + 1 K^T fragment each
   constexpr int CPR = D / 8;
   constexpr int TB = BT * D * 2;
   constexpr int INSTR = TB / 4096;
   constexpr int NDMA = 3 * INSTR;               // K, V, K^T
-  constexpr int NKV = 3, NT = 5;
-  constexpr int T_OFF = NKV * 2 * TB;
-  static_assert(NS >= NDMA, "one DMA per step at most");
-  __shared__ __attribute__((aligned(1024))) char smem[T_OFF + NT * TB];
+  constexpr int RING = 4;
+  constexpr int T_OFF = RING * 2 * TB;
+  static_assert(2 * MB == NU, "one K^T fragment per unit");
+  static_assert(NU >= NDMA, "one DMA per unit at most");
+  __shared__ __attribute__((aligned(1024))) char smem[T_OFF + RING * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -437,202 +535,254 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int hq = bh % a.Hq;
   const int b = bh / a.Hq;
   const int hkv = hq / a.g;
-  const int p0 = qb * Q_WG + 32 * wid;
-  const int pos = p0 + l32;
-  const bool valid = pos < a.Sq;
+  const int p0 = qb * Q_WG + 64 * wid;          // first query of the wavefront
   const int wg_last = min(qb * Q_WG + Q_WG, a.Sq) - 1;
   int kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
   if (kend < 0) kend = 0;
   const int n = (kend + BT - 1) / BT;
-  const int mask_from = a.causal ? max(0, min(kend, p0 + off + 1)) : kend;
-  const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
 
   const size_t hrow = (size_t)b * a.Hq + hq;
-  const size_t qrow = hrow * a.Sq + (valid ? pos : 0);
-  bf16x8 qf[DC], df[DC];
+  int pos[2], lim[2];
+  bool valid[2];
+  bf16x8 qf[2][DC], df[2][DC];
+  float l2[2], dl[2];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    if (valid) {
-      qf[dc] = *(const bf16x8*)(a.q + qrow * D + 16 * dc + 8 * hi);
-      df[dc] = *(const bf16x8*)(a.dout + qrow * D + 16 * dc + 8 * hi);
-    } else {
-      qf[dc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      df[dc] = qf[dc];
+  for (int cb = 0; cb < 2; ++cb) {
+    pos[cb] = p0 + 32 * cb + l32;
+    valid[cb] = pos[cb] < a.Sq;
+    lim[cb] = a.causal ? min(kend - 1, pos[cb] + off) : kend - 1;
+    const size_t qrow = hrow * a.Sq + (valid[cb] ? pos[cb] : 0);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      if (valid[cb]) {
+        qf[cb][dc] = *(const bf16x8*)(a.q + qrow * D + 16 * dc + 8 * hi);
+        df[cb][dc] = *(const bf16x8*)(a.dout + qrow * D + 16 * dc + 8 * hi);
+      } else {
+        qf[cb][dc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        df[cb][dc] = qf[cb][dc];
+      }
+    }
+    l2[cb] = __builtin_huge_valf();
+    dl[cb] = 0.f;
+    if (valid[cb]) {
+      const float* blk = a.ld + (hrow * (a.sqp / BT) + pos[cb] / BT) * (2 * BT);
+      l2[cb] = blk[pos[cb] % BT];
+      dl[cb] = blk[BT + pos[cb] % BT];
     }
   }
-  float l2 = __builtin_huge_valf(), dl = 0.f;
-  if (valid) {
-    const float* blk = a.ld + (hrow * (a.sqp / BT) + pos / BT) * (2 * BT);
-    l2 = blk[pos % BT];
-    dl = blk[BT + pos % BT];
-  }
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    qf[dc] = settle(qf[dc]);
-    df[dc] = settle(df[dc]);
+  for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      qf[cb][dc] = settle(qf[cb][dc]);
+      df[cb][dc] = settle(df[cb][dc]);
+    }
+    l2[cb] = settle(l2[cb]);
+    dl[cb] = settle(dl[cb]);
   }
-  l2 = settle(l2);
-  dl = settle(dl);
 
-  const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-  const bf16* vg = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-  const bf16* ktg = a.kt + ((size_t)b * a.Hkv + hkv) * (size_t)D * a.skp;
-  int rrow[INSTR];
-  uint32_t rcol[INSTR], toff[INSTR];
+  const size_t kvh = (size_t)b * a.Hkv + hkv;
+  const bf16* kg = a.k + kvh * (size_t)a.Sk * D;
+  const bf16* vg = a.v + kvh * (size_t)a.Sk * D;
+  const bf16* ktg = a.kt + kvh * (size_t)D * a.skp;
+  uint32_t rb[DC], tb[2];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * (2 * D) + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) tb[kc] = T_OFF + l32 * 64 + (((2 * kc + hi) ^ tr_swizzle(l32)) << 4);
+  uint32_t roff[INSTR], toff[INSTR];
 #pragma unroll
   for (int i = 0; i < INSTR; ++i) {
     const int P = (wid * INSTR + i) * 64 + lane;
-    rrow[i] = P / CPR;
-    rcol[i] = ((P % CPR) ^ chunk_swizzle<D>(rrow[i])) * 16;
+    const int rr = P / CPR;
+    roff[i] = rr * (2 * D) + (((P % CPR) ^ chunk_swizzle<D>(rr)) << 4);
     const int tr = P / 4;
     toff[i] = (uint32_t)(tr * a.skp + ((P & 3) ^ tr_swizzle(tr)) * 8) * 2;
   }
-  // DMA instruction qi (0 .. NDMA-1) of tile t (K rows, V rows, K^T) into the
-  // ring slots of tile ts (ts > t only past the last tile: see the dK/dV pass)
-  auto issue_one = [&](int ts, int t, int qi) {
-    const int key0 = t * BT;
+  struct Dma {
+    u32x4 rk, rv;                               // K / V rows from key03 on (rows past Sk read 0)
+    const bf16* t;                              // K^T columns from key02 on
+  };
+  // key tiles past the last one are clamped to it (reloaded into unread slots)
+  auto dma_setup = [&](int t3, int t2) __attribute__((always_inline)) {
+    Dma d;
+    const int key3 = min(t3, n - 1) * BT;
+    const uint32_t left = (uint32_t)(a.Sk - key3) * (2 * D);
+    d.rk = buffer_rsrc(kg + (size_t)key3 * D, left);
+    d.rv = buffer_rsrc(vg + (size_t)key3 * D, left);
+    d.t = ktg + min(max(t2, 0), n - 1) * BT;
+    return d;
+  };
+  auto dma_one = [&](const Dma& d, int SKV, int SKT, int qi) __attribute__((always_inline)) {
     const int i = qi % INSTR;
-    if (qi < 2 * INSTR) {                       // rows past kend repeat row kend-1 (their P is masked to 0)
-      const bf16* src = (qi < INSTR) ? kg : vg;
-      const uint32_t r = (uint32_t)min(key0 + rrow[i], kend - 1);
-      dma16s(src, r * (2 * D) + rcol[i],
-             (lds_void*)(smem + (ts % NKV) * 2 * TB + (qi / INSTR) * TB + (wid * INSTR + i) * 1024));
-    } else {
-      dma16s(ktg + key0, toff[i], (lds_void*)(smem + T_OFF + (ts % NT) * TB + (wid * INSTR + i) * 1024));
-    }
+    const int part = (wid * INSTR + i) * 1024;
+    if (qi < INSTR)
+      dma16b(d.rk, roff[i], (lds_void*)(smem + SKV * 2 * TB + part));
+    else if (qi < 2 * INSTR)
+      dma16b(d.rv, roff[i], (lds_void*)(smem + SKV * 2 * TB + TB + part));
+    else
+      dma16s(d.t, toff[i], (lds_void*)(smem + T_OFF + SKT * TB + part));
   };
-  auto issue = [&](int t) {
+
+  f32x16 dqt[2][MB];
 #pragma unroll
-    for (int qi = 0; qi < NDMA; ++qi) issue_one(t, t, qi);
-  };
-
-  f32x16 dqt[MB];
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) dqt[mb] = f32x16{};
-  f32x16 s_[2], dp_[2];
-  bf16x8 dsf[2][2];                             // [tile parity][16-key chunk]
+    for (int mb = 0; mb < MB; ++mb) dqt[cb][mb] = f32x16{};
+  // S^T of two tiles in flight; dP^T of one (the elementwise work of tile j
+  // reads it before the dP^T products of tile j+1 start)
+  f32x16 s_[2][2], dp_[2];
+  bf16x8 dsf[2][2][2];                          // [tile parity][column block][16-key chunk]
 
-  // score op k (0 .. 2 DC - 1): S^T (even k) or dP^T (odd k) over d-chunk k / 2
-  auto g1_frag = [&](const char* skv, int k) {
-    return row_frag<D>(skv + (k & 1) * TB, l32, 2 * (k >> 1) + hi);
-  };
-  // gradient op k (0 .. 2 MB - 1): d-block k % MB, 16-key chunk k / MB
-  auto g2_frag = [&](const char* st, int k) {
-    const int d = 32 * (k % MB) + l32;
-    return tr_frag(st, d, 2 * (k / MB) + hi);
-  };
-
-  auto step = [&](auto par, auto g1, auto g2, auto ew, int j) {
-    constexpr int P = decltype(par)::value;
+  // One step j (slot position POS = j mod 4), in two phases:
+  //  1. unit u = 0 .. NU-1: S^T of tile j+1 from K fragment u (2 MFMAs), dQ^T of
+  //     tile j-1 from K^T fragment u (d-block u % MB, 16-key chunk u / MB;
+  //     2 MFMAs), and a share of the elementwise work (dS) of tile j;
+  //  2. unit u: dP^T of tile j+1 from V fragment u (2 MFMAs), and the DMA of
+  //     tiles j+2 / j+3.
+  auto step = [&](auto pos_, auto g1, auto g2, auto ew, int j) __attribute__((always_inline)) {
+    constexpr int POS = decltype(pos_)::value;
+    constexpr int P = POS & 1;
     constexpr bool G1 = decltype(g1)::value;
     constexpr bool G2 = decltype(g2)::value;
     constexpr bool EW = decltype(ew)::value;
-    const char* skv = smem + ((j + 1) % NKV) * 2 * TB;
-    const char* st = smem + T_OFF + ((j + NT - 1) % NT) * TB;
-    const int t3 = j + 3;
-    const int t3c = min(t3, n - 1);
+    constexpr int SKV = (POS + 1) % RING;       // K, V rows of tile j+1
+    constexpr int SKT = (POS + 3) % RING;       // K^T of tile j-1
+    const char* lds = smem;
+    auto kfr = [&](int u) __attribute__((always_inline)) { return *(const bf16x8*)(lds + rb[u] + SKV * 2 * TB); };
+    auto vfr = [&](int u) __attribute__((always_inline)) { return *(const bf16x8*)(lds + rb[u] + SKV * 2 * TB + TB); };
+    auto tfr = [&](int u) __attribute__((always_inline)) {
+      return *(const bf16x8*)(lds + tb[u / MB] + SKT * TB + (u % MB) * 32 * 64);
+    };
+    Dma d;
+    if constexpr (G1) d = dma_setup(j + 3, j + 2);
     const int key0 = j * BT;
-    const bool need_mask = key0 + BT > mask_from;
-    if constexpr (G1) s_[P ^ 1] = dp_[P ^ 1] = f32x16{};
-    bf16x8 f1[3], f2[2];
-    if constexpr (G1) {
-      f1[0] = g1_frag(skv, 0);
-      f1[1] = g1_frag(skv, 1);
-    }
-    if constexpr (G2) f2[0] = g2_frag(st, 0);
-    float dt[8];
+    bf16x8 fk[2], ft[2], fv[2];
+    if constexpr (G1) fk[0] = kfr(0);
+    if constexpr (G2) ft[0] = tfr(0);
+    float dt[2][8];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      // reads for the next step: score ops 2i+2, 2i+3, gradient op i+1
-      if constexpr (G1) {
-        if (2 * i + 2 < 2 * DC) f1[(2 * i + 2) % 3] = g1_frag(skv, 2 * i + 2);
+    for (int u = 0; u < NU; ++u) {
+      if (u + 1 < NU) {
+        if constexpr (G1) fk[(u + 1) & 1] = kfr(u + 1);
+        if constexpr (G2) ft[(u + 1) & 1] = tfr(u + 1);
       }
-      if constexpr (G2) {
-        if (i + 1 < NS) f2[(i + 1) & 1] = g2_frag(st, i + 1);
+      if (u + 1 == NU) {
+        if constexpr (G1) fv[0] = vfr(0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (G1) {
+        s_[P ^ 1][0] = mfma32(fk[u & 1], qf[0][u], u == 0 ? f32x16{} : s_[P ^ 1][0]);
+        s_[P ^ 1][1] = mfma32(fk[u & 1], qf[1][u], u == 0 ? f32x16{} : s_[P ^ 1][1]);
+      }
+      if constexpr (G2) {
+        dqt[0][u % MB] = mfma32(ft[u & 1], dsf[P ^ 1][0][u / MB], dqt[0][u % MB]);
+        dqt[1][u % MB] = mfma32(ft[u & 1], dsf[P ^ 1][1][u / MB], dqt[1][u % MB]);
+      }
+      if constexpr (EW) {
+        // values [v0, v1) of the 32 score registers (16 per column block)
+        const int v0 = (u * 32) / NU;
+        const int v1 = ((u + 1) * 32) / NU;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int k = 2 * i + u;
-        if constexpr (G1) {
-          if (k & 1)
-            dp_[P ^ 1] = mfma32(f1[k % 3], df[k >> 1], dp_[P ^ 1]);
-          else
-            s_[P ^ 1] = mfma32(f1[k % 3], qf[k >> 1], s_[P ^ 1]);
-        }
-        if (u == 0) {
-          if constexpr (G2) dqt[i % MB] = mfma32(f2[i & 1], dsf[P ^ 1][i / MB], dqt[i % MB]);
-        }
-        if (u == 0) {
-          if constexpr (G1) {
-            if (2 * i + 3 < 2 * DC) f1[(2 * i + 3) % 3] = g1_frag(skv, 2 * i + 3);
+        for (int vv = v0; vv < v1; ++vv) {
+          const int cb = vv >> 4;
+          const int v = vv & 15;
+          float p = fast_exp2(__builtin_fmaf(s_[P][cb][v], a.c, -l2[cb]));
+          if constexpr (CAUSAL) {
+            if (key0 + 8 * (v >> 2) + 4 * hi + (v & 3) > lim[cb]) p = 0.f;
+          }
+          dt[cb][v & 7] = p * (dp_[cb][v] - dl[cb]);
+          pin(dt[cb][v & 7]);
+          if ((v & 7) == 7) {
+            dsf[P][cb][v >> 3] = to_bf16x8(dt[cb][0], dt[cb][1], dt[cb][2], dt[cb][3], dt[cb][4], dt[cb][5],
+                                           dt[cb][6], dt[cb][7]);
+            pin(dsf[P][cb][v >> 3]);
           }
         }
       }
-      if constexpr (EW) {
-        const int v0 = (i * 16) / NS;
-        const int v1 = ((i + 1) * 16) / NS;
+    }
+    if constexpr (G1) {
 #pragma unroll
-        for (int v = v0; v < v1; ++v) {
-          float p = fast_exp2(__builtin_fmaf(s_[P][v], a.c, -l2));
-          if (need_mask && key0 + 8 * (v >> 2) + 4 * hi + (v & 3) > lim) p = 0.f;
-          dt[v & 7] = p * (dp_[P][v] - dl);
-          if ((v & 7) == 7)
-            dsf[P][v >> 3] = to_bf16x8(dt[0], dt[1], dt[2], dt[3], dt[4], dt[5], dt[6], dt[7]);
-        }
+      for (int u = 0; u < NU; ++u) {
+        if (u + 1 < NU) fv[(u + 1) & 1] = vfr(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dp_[0] = mfma32(fv[u & 1], df[0][u], u == 0 ? f32x16{} : dp_[0]);
+        dp_[1] = mfma32(fv[u & 1], df[1][u], u == 0 ? f32x16{} : dp_[1]);
+        if (u < NDMA) dma_one(d, (POS + 3) % RING, (POS + 2) % RING, u);
       }
-      if (i < NDMA && G1) issue_one(t3, t3c, i);
     }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // Causal: every step applies the mask. Without it nothing needs masking:
+  // keys past Sk have zero K^T columns, so their dS never reaches dQ.
+  auto full = [&](auto pos_, auto g2, int j) __attribute__((always_inline)) { step(pos_, T_{}, g2, T_{}, j); };
+  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
 
-  // tiles 0 and 1 now; tile j+3 during step j (tile 2 during the scores of
-  // tile 0). Every step that computes scores issues exactly NDMA DMA
-  // instructions, so "all but the last NDMA" always means "the next tile".
   if (n > 0) {
-    issue(0);
-    issue(min(1, n - 1));
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
-    step(P1{}, T_{}, F_{}, F_{}, -1);
-  }
-  auto sync = [&](int j) {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
-  };
-  if (n > 0) {
-    sync(0);
-    step(P0{}, T_{}, F_{}, T_{}, 0);
+    {
+      const Dma d3 = dma_setup(0, 0);           // step -3: rows of tile 0, K^T of "tile -1" (dummy)
+#pragma unroll
+      for (int qi = 0; qi < NDMA; ++qi) dma_one(d3, 0, 3, qi);
+      const Dma d2 = dma_setup(1, 0);           // step -2: rows of tile 1, K^T of tile 0
+#pragma unroll
+      for (int qi = 0; qi < NDMA; ++qi) dma_one(d2, 1, 0, qi);
+    }
+    sync();
+    step(I3{}, T_{}, F_{}, F_{}, -1);
+    sync();
+    full(I0{}, F_{}, 0);
   }
   int j = 1;
-  for (; j + 1 < n; j += 2) {
-    sync(j);
-    step(P1{}, T_{}, T_{}, T_{}, j);
-    sync(j + 1);
-    step(P0{}, T_{}, T_{}, T_{}, j + 1);
+  for (; j + 3 < n; j += 4) {
+    sync();
+    full(I1{}, T_{}, j);
+    sync();
+    full(I2{}, T_{}, j + 1);
+    sync();
+    full(I3{}, T_{}, j + 2);
+    sync();
+    full(I0{}, T_{}, j + 3);
   }
   if (j < n) {
-    sync(j);
-    step(P1{}, T_{}, T_{}, T_{}, j);
+    sync();
+    full(I1{}, T_{}, j);
+  }
+  if (j + 1 < n) {
+    sync();
+    full(I2{}, T_{}, j + 1);
+  }
+  if (j + 2 < n) {
+    sync();
+    full(I3{}, T_{}, j + 2);
   }
   if (n > 0) {
-    if (n & 1)
-      step(P1{}, F_{}, T_{}, F_{}, n);
-    else
-      step(P0{}, F_{}, T_{}, F_{}, n);
+    switch (n & 3) {
+      case 0: step(I0{}, F_{}, T_{}, F_{}, n); break;
+      case 1: step(I1{}, F_{}, T_{}, F_{}, n); break;
+      case 2: step(I2{}, F_{}, T_{}, F_{}, n); break;
+      default: step(I3{}, F_{}, T_{}, F_{}, n); break;
+    }
   }
 
-  if (!valid) return;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int cb = 0; cb < 2; ++cb) {
+    if (!valid[cb]) continue;
+    bf16* dst = a.dq + (hrow * a.Sq + pos[cb]) * D;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 r;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = (bf16)(dqt[mb][4 * i4 + e] * a.scale);
-      *(bf16x4*)(a.dq + qrow * D + 32 * mb + 8 * i4 + 4 * hi) = r;
-    }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (bf16)(dqt[cb][mb][4 * i4 + e] * a.scale);
+        *(bf16x4*)(dst + 32 * mb + 8 * i4 + 4 * hi) = r;
+      }
+  }
 }
 
 struct WsLayout {
@@ -683,14 +833,20 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   }
   if (a.total_kv > 0) {
     timing_begin(s, "bwd_dkdv");
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.total_kv), dim3(256), 0, s, a);
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(a.total_kv), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(a.total_kv), dim3(256), 0, s, a);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
   }
   if (a.total_q > 0) {
     timing_begin(s, "bwd_dq");
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.total_q), dim3(256), 0, s, a);
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(a.total_q), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(a.total_q), dim3(256), 0, s, a);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -699,7 +855,7 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
     snprintf(log, log_n,
              "attn_bwd: bwd_pre<d=%d> grid=%zu; transpose_rows<d=%d> x3 (Q^T, dO^T, K^T); "
              "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles); "
-             "bwd_dq<d=%d> grid=%d (128 rows x 32-key tiles)",
+             "bwd_dq<d=%d> grid=%d (256 rows x 32-key tiles)",
              D, (rows + RPB - 1) / RPB, D, D, a.total_kv, D, a.total_q);
   return hipSuccess;
 }

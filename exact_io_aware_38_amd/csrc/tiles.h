@@ -52,6 +52,29 @@ __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, lds_void
 }
 
 
+// Buffer resource for raw loads with range checking: a lane whose byte
+// offset is >= num_bytes reads zeros. Word 3 selects the 32-bit data format
+// (format 0 would read zeros everywhere); stride 0 gives a raw buffer.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(num_bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane from a buffer (offset voff, range-checked) into LDS at
+// base + 16 * lane.
+__device__ __forceinline__ void dma16b(u32x4 rsrc, uint32_t voff, lds_void* base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Re-define a value that a global load produced before a loop, so the
 // compiler knows no load is pending on it inside the loop (it would otherwise
 // wait on the memory counter there, which also waits for DMA in flight). The
