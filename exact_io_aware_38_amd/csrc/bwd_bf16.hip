@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <type_traits>
+#include <utility>
 
 namespace attn {
 
@@ -59,6 +60,17 @@ __device__ __forceinline__ void pin(bf16x8& x) {
   u32x4 w = __builtin_bit_cast(u32x4, x);
   asm volatile("" : "+v"(w));
   x = __builtin_bit_cast(bf16x8, w);
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order, with I usable as
+// a compile-time constant inside f.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 struct BwdArgs {
@@ -242,6 +254,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int tr = P / 4;
     toff[i] = (uint32_t)(tr * a.sqp + ((P & 3) ^ tr_swizzle(tr)) * 8) * 2;
   }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;           // M0 = lds0 (+ wavefront part) + offset
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + wid * INSTR * 1024);
 
   // Tile sequence: for each query head of the group, the 32-row tiles from
   // the last one down to the first one that sees a key of this workgroup.
@@ -279,41 +293,63 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     ++idx3;
   };
 
-  // DMA instruction qi (0 .. NDMA-1): rows (Q, dO) and lse2/D of the tile at
-  // (hq3, q03) into row slot SQ / lse slot SLD, transposed tiles of the tile
-  // at (hq2, q02) into slot STD.
-  struct Dma {
-    u32x4 rq, rd;                               // Q / dO rows from q03 on (rows past Sq read 0)
-    const bf16* tq;                             // Q^T / dO^T columns from q02 on
-    const bf16* td;
-    const float* l;                             // lse2/D block of q03
+  // Buffer descriptors of the heads the two DMA streams read: rows (Q, dO)
+  // and lse2/D of the tile at the window's last entry (tile j+3), transposed
+  // tiles of the entry before it (tile j+2). Rebuilt only when the head
+  // changes; within a head a tile is a byte offset (rows past Sq are out of
+  // the row buffers' range and read zeros).
+  u32x4 rq, rd, rl, rtq, rtd;
+  int h3 = -1, h2 = -1;
+  auto refresh = [&]() __attribute__((always_inline)) {
+    if (whq[3] != h3) {
+      h3 = whq[3];
+      const size_t h = (size_t)b * a.Hq + h3;
+      rq = buffer_rsrc(a.q + h * a.Sq * D, (uint32_t)a.Sq * (2 * D));
+      rd = buffer_rsrc(a.dout + h * a.Sq * D, (uint32_t)a.Sq * (2 * D));
+      rl = buffer_rsrc(a.ld + h * (a.sqp / BT) * (2 * BT), (uint32_t)a.sqp * 8);
+    }
+    if (whq[2] != h2) {
+      h2 = whq[2];
+      const size_t h = (size_t)b * a.Hq + h2;
+      rtq = buffer_rsrc(a.qt + h * D * a.sqp, (uint32_t)a.sqp * (2 * D));
+      rtd = buffer_rsrc(a.dot + h * D * a.sqp, (uint32_t)a.sqp * (2 * D));
+    }
   };
-  auto dma_setup = [&](int hq3, int q03, int hq2, int q02) __attribute__((always_inline)) {
-    Dma d;
-    const size_t h3 = (size_t)b * a.Hq + hq3;
-    const size_t h2 = (size_t)b * a.Hq + hq2;
-    const uint32_t rows_left = (uint32_t)(a.Sq - q03) * (2 * D);
-    d.rq = buffer_rsrc(a.q + (h3 * a.Sq + q03) * D, rows_left);
-    d.rd = buffer_rsrc(a.dout + (h3 * a.Sq + q03) * D, rows_left);
-    d.tq = a.qt + h2 * D * a.sqp + q02;
-    d.td = a.dot + h2 * D * a.sqp + q02;
-    d.l = a.ld + (h3 * (a.sqp / BT) + q03 / BT) * (2 * BT);
-    return d;
+  // Offsets of one step's DMA: row tiles of tile j+3 (per lane), transposed
+  // tiles of tile j+2 and lse2/D of tile j+3 (scalar).
+  struct DmaOff {
+    uint32_t vr[INSTR];
+    uint32_t st, sl;
   };
-  auto dma_one = [&](const Dma& d, int SQ, int STD, int SLD, int qi) __attribute__((always_inline)) {
-    const int i = qi % INSTR;
-    const int part = (wid * INSTR + i) * 1024;
-    if (qi < INSTR)
-      dma16b(d.rq, roff[i], (lds_void*)(smem + SQ * 2 * TB + part));
-    else if (qi < 2 * INSTR)
-      dma16b(d.rd, roff[i], (lds_void*)(smem + SQ * 2 * TB + TB + part));
-    else if (qi < 3 * INSTR)
-      dma16s(d.tq, toff[i], (lds_void*)(smem + T_OFF + STD * 2 * TB + part));
-    else if (qi < 4 * INSTR)
-      dma16s(d.td, toff[i], (lds_void*)(smem + T_OFF + STD * 2 * TB + TB + part));
+  auto dma_offsets = [&](int q03, int q02) __attribute__((always_inline)) {
+    DmaOff o;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) o.vr[i] = roff[i] + (uint32_t)q03 * (2 * D);
+    o.st = (uint32_t)q02 * 2;
+    o.sl = (uint32_t)(q03 / BT) * (2 * BT * 4);
+    return o;
+  };
+  // DMA instruction QI (0 .. NDMA-1) into row slot SQ, transposed slot STD,
+  // lse slot SLD
+  auto dma_one = [&](auto sq_, auto std_, auto sld_, auto qi_, const DmaOff& o) __attribute__((always_inline)) {
+    constexpr int SQ = decltype(sq_)::value, STD = decltype(std_)::value, SLD = decltype(sld_)::value;
+    constexpr int QI = decltype(qi_)::value;
+    constexpr int i = QI % INSTR;
+    constexpr uint32_t part = i * 1024;
+    if constexpr (QI < INSTR)
+      dma16b_at<SQ * 2 * TB + part>(rq, o.vr[i], 0u, ldsw);
+    else if constexpr (QI < 2 * INSTR)
+      dma16b_at<SQ * 2 * TB + TB + part>(rd, o.vr[i], 0u, ldsw);
+    else if constexpr (QI < 3 * INSTR)
+      dma16b_at<T_OFF + STD * 2 * TB + part>(rtq, toff[i], o.st, ldsw);
+    else if constexpr (QI < 4 * INSTR)
+      dma16b_at<T_OFF + STD * 2 * TB + TB + part>(rtd, toff[i], o.st, ldsw);
     else                                        // every wavefront loads the same 256 bytes
-      dma4s(d.l, lane * 4, (lds_void*)(smem + L_OFF + SLD * LB));
+      dma4b_at<L_OFF + SLD * LB>(rl, (uint32_t)lane * 4, o.sl, lds0);
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C3 = std::integral_constant<int, 3>;
 
   f32x16 dkt[MB], dvt[MB];
 #pragma unroll
@@ -346,8 +382,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int ch = k % (2 * MB);
       return *(const bf16x8*)(lds + tb[k / (2 * MB)] + ST * 2 * TB + (ch < MB ? TB : 0) + (ch % MB) * 32 * 64);
     };
-    Dma d;
-    if constexpr (G1) d = dma_setup(whq[3], wq0[3], whq[2], wq0[2]);
+    DmaOff o;
+    if constexpr (G1) {
+      refresh();
+      o = dma_offsets(wq0[3], wq0[2]);
+    }
     const int q0 = wq0[0];
     f32x4 l2v[4], dlv[4];
     if constexpr (EW) {
@@ -367,9 +406,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       f2[1] = g2_frag(1);
     }
     float pt[8], dt[8];
-#pragma unroll
-    for (int i = 0; i < NOPS; ++i) {
-      if (i + 2 < NOPS) {
+    static_for<NOPS>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 2 < NOPS) {
         if constexpr (G1) f1[(i + 2) % 3] = g1_frag(i + 2);
         if constexpr (G2) f2[(i + 2) % 3] = g2_frag(i + 2);
       }
@@ -390,8 +429,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       }
       if constexpr (EW) {
         // values [v0, v1) of the 16 score registers; the first step only reads lse2 / D
-        const int v0 = i == 0 ? 0 : ((i - 1) * 16) / (NOPS - 1);
-        const int v1 = i == 0 ? 0 : (i * 16) / (NOPS - 1);
+        constexpr int v0 = i == 0 ? 0 : ((i - 1) * 16) / (NOPS - 1);
+        constexpr int v1 = i == 0 ? 0 : (i * 16) / (NOPS - 1);
 #pragma unroll
         for (int v = v0; v < v1; ++v) {
           const float l2 = l2v[v >> 2][v & 3];
@@ -411,10 +450,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           }
         }
       }
-      if constexpr (G1) {
-        if (i < NDMA) dma_one(d, (POS + 3) % RING, (POS + 2) % RING, (POS + 3) % RING, i);
-      }
-    }
+      if constexpr (G1 && i < NDMA)
+        dma_one(std::integral_constant<int, (POS + 3) % RING>{}, std::integral_constant<int, (POS + 2) % RING>{},
+                std::integral_constant<int, (POS + 3) % RING>{}, ic, o);
+    });
     if constexpr (G1) shift();
   };
   using T_ = std::true_type;
@@ -423,12 +462,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // Causal: every step applies the mask (a branch per tile between masked
-  // and unmasked copies of the step costs more in register shuffling than
-  // the two instructions per score). Without it nothing needs masking: rows
-  // past Sq have lse2 = +inf, so their P and dS are 0.
   using M_ = std::integral_constant<bool, CAUSAL>;
-  auto full = [&](auto pos_, auto g2) __attribute__((always_inline)) { step(pos_, T_{}, g2, T_{}, M_{}); };
+  // Causal masking is needed only where some key of the workgroup lies above
+  // some query of the tile. The walk runs down to the diagonal, so with one
+  // query head per KV head these are the last tiles: the first n_um steps run
+  // unmasked, the rest masked (the loops switch at a multiple of 4 so slot
+  // positions stay compile-time). With several query heads per KV head every
+  // step is masked. Without a causal mask nothing needs masking: rows past Sq
+  // have lse2 = +inf, so their P and dS are 0.
+  int n_um = n;
+  if (CAUSAL) {
+    n_um = 0;
+    if (a.g == 1) {
+      // tile qt is unmasked iff its first row sees the workgroup's last key
+      const int x = k0 + KV_WG - 1 - off;
+      const int lowest_unmasked = x <= 0 ? 0 : (x + BT - 1) / BT;
+      n_um = min(n, max(0, n_qt - max(lowest_unmasked, qt_lo)));
+    }
+  }
+  auto full = [&](auto pos_, auto g2, auto mask_) __attribute__((always_inline)) {
+    step(pos_, T_{}, g2, T_{}, mask_);
+  };
   // step j: tile j+1 has landed for every wavefront (each waits for its own
   // DMA, the barrier for all of them), and every wavefront is done with step j-1
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
@@ -437,40 +491,61 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // DMA groups of steps -3 and -2 (the transposed tiles of "tile -1" are a
     // dummy copy of tile 0), then the scores of tile 0 as step -1
     {
-      const Dma d3 = dma_setup(whq[1], wq0[1], whq[1], wq0[1]);
-#pragma unroll
-      for (int qi = 0; qi < NDMA; ++qi) dma_one(d3, 0, 3, 0, qi);
-      const Dma d2 = dma_setup(whq[2], wq0[2], whq[1], wq0[1]);
-#pragma unroll
-      for (int qi = 0; qi < NDMA; ++qi) dma_one(d2, 1, 0, 1, qi);
+      // the window's entries 1 and 2 hold tiles 0 and 1 here; the heads of
+      // tiles 0..2 are loaded into the descriptors by hand
+      const int s3 = whq[3], s2 = whq[2];
+      whq[3] = whq[1];
+      whq[2] = whq[1];
+      refresh();
+      const DmaOff o3 = dma_offsets(wq0[1], wq0[1]);
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C0{}, C3{}, C0{}, qi, o3); });
+      whq[3] = s2;
+      refresh();
+      const DmaOff o2 = dma_offsets(wq0[2], wq0[1]);
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C1{}, C0{}, C1{}, qi, o2); });
+      whq[3] = s3;
+      whq[2] = s2;
     }
     sync();
     step(I3{}, T_{}, F_{}, F_{}, F_{});         // j = -1
     sync();
-    full(I0{}, F_{});                           // j = 0: no gradients yet
+    if (n_um > 0)                               // j = 0: no gradients yet
+      full(I0{}, F_{}, F_{});
+    else
+      full(I0{}, F_{}, M_{});
   }
   int j = 1;
+  for (; j + 3 < n_um; j += 4) {
+    sync();
+    full(I1{}, T_{}, F_{});
+    sync();
+    full(I2{}, T_{}, F_{});
+    sync();
+    full(I3{}, T_{}, F_{});
+    sync();
+    full(I0{}, T_{}, F_{});
+  }
   for (; j + 3 < n; j += 4) {
     sync();
-    full(I1{}, T_{});
+    full(I1{}, T_{}, M_{});
     sync();
-    full(I2{}, T_{});
+    full(I2{}, T_{}, M_{});
     sync();
-    full(I3{}, T_{});
+    full(I3{}, T_{}, M_{});
     sync();
-    full(I0{}, T_{});
+    full(I0{}, T_{}, M_{});
   }
   if (j < n) {
     sync();
-    full(I1{}, T_{});
+    full(I1{}, T_{}, M_{});
   }
   if (j + 1 < n) {
     sync();
-    full(I2{}, T_{});
+    full(I2{}, T_{}, M_{});
   }
   if (j + 2 < n) {
     sync();
-    full(I3{}, T_{});
+    full(I3{}, T_{}, M_{});
   }
   // gradients of the last tile: a step at position n mod 4 with only the gradient group
   if (n > 0) {
@@ -599,30 +674,40 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     const int tr = P / 4;
     toff[i] = (uint32_t)(tr * a.skp + ((P & 3) ^ tr_swizzle(tr)) * 8) * 2;
   }
-  struct Dma {
-    u32x4 rk, rv;                               // K / V rows from key03 on (rows past Sk read 0)
-    const bf16* t;                              // K^T columns from key02 on
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + wid * INSTR * 1024);
+  // K / V rows (rows past Sk are out of range and read zeros) and K^T of the
+  // KV head; a key tile is a byte offset
+  const u32x4 rk = buffer_rsrc(kg, (uint32_t)a.Sk * (2 * D));
+  const u32x4 rv = buffer_rsrc(vg, (uint32_t)a.Sk * (2 * D));
+  const u32x4 rkt = buffer_rsrc(ktg, (uint32_t)a.skp * (2 * D));
+  struct DmaOff {
+    uint32_t vr[INSTR];                         // rows of key tile t3 (per lane)
+    uint32_t st;                                // K^T columns of key tile t2
   };
   // key tiles past the last one are clamped to it (reloaded into unread slots)
-  auto dma_setup = [&](int t3, int t2) __attribute__((always_inline)) {
-    Dma d;
-    const int key3 = min(t3, n - 1) * BT;
-    const uint32_t left = (uint32_t)(a.Sk - key3) * (2 * D);
-    d.rk = buffer_rsrc(kg + (size_t)key3 * D, left);
-    d.rv = buffer_rsrc(vg + (size_t)key3 * D, left);
-    d.t = ktg + min(max(t2, 0), n - 1) * BT;
-    return d;
+  auto dma_offsets = [&](int t3, int t2) __attribute__((always_inline)) {
+    DmaOff o;
+    const uint32_t key3 = (uint32_t)min(t3, n - 1) * BT;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) o.vr[i] = roff[i] + key3 * (2 * D);
+    o.st = (uint32_t)min(max(t2, 0), n - 1) * (BT * 2);
+    return o;
   };
-  auto dma_one = [&](const Dma& d, int SKV, int SKT, int qi) __attribute__((always_inline)) {
-    const int i = qi % INSTR;
-    const int part = (wid * INSTR + i) * 1024;
-    if (qi < INSTR)
-      dma16b(d.rk, roff[i], (lds_void*)(smem + SKV * 2 * TB + part));
-    else if (qi < 2 * INSTR)
-      dma16b(d.rv, roff[i], (lds_void*)(smem + SKV * 2 * TB + TB + part));
+  auto dma_one = [&](auto skv_, auto skt_, auto qi_, const DmaOff& o) __attribute__((always_inline)) {
+    constexpr int SKV = decltype(skv_)::value, SKT = decltype(skt_)::value;
+    constexpr int QI = decltype(qi_)::value;
+    constexpr int i = QI % INSTR;
+    constexpr uint32_t part = i * 1024;
+    if constexpr (QI < INSTR)
+      dma16b_at<SKV * 2 * TB + part>(rk, o.vr[i], 0u, ldsw);
+    else if constexpr (QI < 2 * INSTR)
+      dma16b_at<SKV * 2 * TB + TB + part>(rv, o.vr[i], 0u, ldsw);
     else
-      dma16s(d.t, toff[i], (lds_void*)(smem + T_OFF + SKT * TB + part));
+      dma16b_at<T_OFF + SKT * TB + part>(rkt, toff[i], o.st, ldsw);
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C3 = std::integral_constant<int, 3>;
 
   f32x16 dqt[2][MB];
 #pragma unroll
@@ -640,12 +725,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   //     2 MFMAs), and a share of the elementwise work (dS) of tile j;
   //  2. unit u: dP^T of tile j+1 from V fragment u (2 MFMAs), and the DMA of
   //     tiles j+2 / j+3.
-  auto step = [&](auto pos_, auto g1, auto g2, auto ew, int j) __attribute__((always_inline)) {
+  auto step = [&](auto pos_, auto g1, auto g2, auto ew, auto mask_, int j) __attribute__((always_inline)) {
     constexpr int POS = decltype(pos_)::value;
     constexpr int P = POS & 1;
     constexpr bool G1 = decltype(g1)::value;
     constexpr bool G2 = decltype(g2)::value;
     constexpr bool EW = decltype(ew)::value;
+    constexpr bool MASK = decltype(mask_)::value;
     constexpr int SKV = (POS + 1) % RING;       // K, V rows of tile j+1
     constexpr int SKT = (POS + 3) % RING;       // K^T of tile j-1
     const char* lds = smem;
@@ -654,8 +740,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     auto tfr = [&](int u) __attribute__((always_inline)) {
       return *(const bf16x8*)(lds + tb[u / MB] + SKT * TB + (u % MB) * 32 * 64);
     };
-    Dma d;
-    if constexpr (G1) d = dma_setup(j + 3, j + 2);
+    DmaOff o;
+    if constexpr (G1) o = dma_offsets(j + 3, j + 2);
     const int key0 = j * BT;
     bf16x8 fk[2], ft[2], fv[2];
     if constexpr (G1) fk[0] = kfr(0);
@@ -688,7 +774,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
           const int cb = vv >> 4;
           const int v = vv & 15;
           float p = fast_exp2(__builtin_fmaf(s_[P][cb][v], a.c, -l2[cb]));
-          if constexpr (CAUSAL) {
+          if constexpr (MASK) {
             if (key0 + 8 * (v >> 2) + 4 * hi + (v & 3) > lim[cb]) p = 0.f;
           }
           dt[cb][v & 7] = p * (dp_[cb][v] - dl[cb]);
@@ -702,14 +788,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     if constexpr (G1) {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (u + 1 < NU) fv[(u + 1) & 1] = vfr(u + 1);
+      static_for<NU>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u + 1 < NU) fv[(u + 1) & 1] = vfr(u + 1);
         __builtin_amdgcn_sched_barrier(0);
         dp_[0] = mfma32(fv[u & 1], df[0][u], u == 0 ? f32x16{} : dp_[0]);
         dp_[1] = mfma32(fv[u & 1], df[1][u], u == 0 ? f32x16{} : dp_[1]);
-        if (u < NDMA) dma_one(d, (POS + 3) % RING, (POS + 2) % RING, u);
-      }
+        if constexpr (u < NDMA)
+          dma_one(std::integral_constant<int, (POS + 3) % RING>{}, std::integral_constant<int, (POS + 2) % RING>{},
+                  uc, o);
+      });
     }
   };
   using T_ = std::true_type;
@@ -718,54 +806,76 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // Causal: every step applies the mask. Without it nothing needs masking:
-  // keys past Sk have zero K^T columns, so their dS never reaches dQ.
-  auto full = [&](auto pos_, auto g2, int j) __attribute__((always_inline)) { step(pos_, T_{}, g2, T_{}, j); };
+  // Causal masking is needed only for key tiles that reach past the first
+  // query of the workgroup: the last ones of the walk. The first n_um steps
+  // run unmasked, the rest masked (switching at a multiple of 4). Without a
+  // causal mask nothing needs masking: keys past Sk have zero K^T columns, so
+  // their dS never reaches dQ.
+  using M_ = std::integral_constant<bool, CAUSAL>;
+  int n_um = n;
+  if (CAUSAL) {
+    const int y = qb * Q_WG + off - (BT - 1);   // tile t is unmasked iff t * BT <= y
+    n_um = y < 0 ? 0 : min(n, y / BT + 1);
+  }
+  auto full = [&](auto pos_, auto g2, auto mask_, int j) __attribute__((always_inline)) {
+    step(pos_, T_{}, g2, T_{}, mask_, j);
+  };
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
 
   if (n > 0) {
     {
-      const Dma d3 = dma_setup(0, 0);           // step -3: rows of tile 0, K^T of "tile -1" (dummy)
-#pragma unroll
-      for (int qi = 0; qi < NDMA; ++qi) dma_one(d3, 0, 3, qi);
-      const Dma d2 = dma_setup(1, 0);           // step -2: rows of tile 1, K^T of tile 0
-#pragma unroll
-      for (int qi = 0; qi < NDMA; ++qi) dma_one(d2, 1, 0, qi);
+      const DmaOff o3 = dma_offsets(0, 0);      // step -3: rows of tile 0, K^T of "tile -1" (dummy)
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C0{}, C3{}, qi, o3); });
+      const DmaOff o2 = dma_offsets(1, 0);      // step -2: rows of tile 1, K^T of tile 0
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C1{}, C0{}, qi, o2); });
     }
     sync();
-    step(I3{}, T_{}, F_{}, F_{}, -1);
+    step(I3{}, T_{}, F_{}, F_{}, F_{}, -1);
     sync();
-    full(I0{}, F_{}, 0);
+    if (n_um > 0)
+      full(I0{}, F_{}, F_{}, 0);
+    else
+      full(I0{}, F_{}, M_{}, 0);
   }
   int j = 1;
+  for (; j + 3 < n_um; j += 4) {
+    sync();
+    full(I1{}, T_{}, F_{}, j);
+    sync();
+    full(I2{}, T_{}, F_{}, j + 1);
+    sync();
+    full(I3{}, T_{}, F_{}, j + 2);
+    sync();
+    full(I0{}, T_{}, F_{}, j + 3);
+  }
   for (; j + 3 < n; j += 4) {
     sync();
-    full(I1{}, T_{}, j);
+    full(I1{}, T_{}, M_{}, j);
     sync();
-    full(I2{}, T_{}, j + 1);
+    full(I2{}, T_{}, M_{}, j + 1);
     sync();
-    full(I3{}, T_{}, j + 2);
+    full(I3{}, T_{}, M_{}, j + 2);
     sync();
-    full(I0{}, T_{}, j + 3);
+    full(I0{}, T_{}, M_{}, j + 3);
   }
   if (j < n) {
     sync();
-    full(I1{}, T_{}, j);
+    full(I1{}, T_{}, M_{}, j);
   }
   if (j + 1 < n) {
     sync();
-    full(I2{}, T_{}, j + 1);
+    full(I2{}, T_{}, M_{}, j + 1);
   }
   if (j + 2 < n) {
     sync();
-    full(I3{}, T_{}, j + 2);
+    full(I3{}, T_{}, M_{}, j + 2);
   }
   if (n > 0) {
     switch (n & 3) {
-      case 0: step(I0{}, F_{}, T_{}, F_{}, n); break;
-      case 1: step(I1{}, F_{}, T_{}, F_{}, n); break;
-      case 2: step(I2{}, F_{}, T_{}, F_{}, n); break;
-      default: step(I3{}, F_{}, T_{}, F_{}, n); break;
+      case 0: step(I0{}, F_{}, T_{}, F_{}, F_{}, n); break;
+      case 1: step(I1{}, F_{}, T_{}, F_{}, F_{}, n); break;
+      case 2: step(I2{}, F_{}, T_{}, F_{}, F_{}, n); break;
+      default: step(I3{}, F_{}, T_{}, F_{}, F_{}, n); break;
     }
   }
 

@@ -75,6 +75,25 @@ __device__ __forceinline__ void dma16b(u32x4 rsrc, uint32_t voff, lds_void* base
                : "memory", "m0");
 }
 
+// Same with the LDS byte address given as a wave-uniform base plus a
+// compile-time offset (one scalar add builds M0), and a scalar byte offset
+// soff added to the address (not range-checked: only voff is compared with
+// the buffer size).
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16b_at(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+template <uint32_t OFF>
+__device__ __forceinline__ void dma4b_at(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+
 // Re-define a value that a global load produced before a loop, so the
 // compiler knows no load is pending on it inside the loop (it would otherwise
 // wait on the memory counter there, which also waits for DMA in flight). The
