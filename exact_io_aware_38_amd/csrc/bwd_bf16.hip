@@ -73,6 +73,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Score MFMAs with the accumulator in VGPRs (the elementwise code reads every
+// score; AGPR accumulators would need one v_accvgpr_read per score), issued
+// as inline assembly because the kernels otherwise compile with AGPR
+// accumulators (the gradient accumulators do not fit next to everything else
+// in the 256 VGPRs). The compiler does not track hazards through inline
+// assembly: score_settle() must follow the last MFMA of a chain before any
+// other instruction reads the accumulator (an MFMA result needs up to 19
+// wait states before a non-MFMA read); chained MFMAs with the same
+// accumulator as srcC and vdst issue back to back.
+__device__ __forceinline__ void mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_next(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_settle(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
 struct BwdArgs {
   const bf16* q;
   const bf16* k;
@@ -414,10 +433,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);        // keep the reads two MFMAs ahead of their use
       if constexpr (G1) {
-        if (i & 1)
-          dp_[P ^ 1] = mfma32(f1[i % 3], vf[i >> 1], i < 2 ? f32x16{} : dp_[P ^ 1]);
-        else
-          s_[P ^ 1] = mfma32(f1[i % 3], kf[i >> 1], i < 2 ? f32x16{} : s_[P ^ 1]);
+        if constexpr (i < 2) {
+          if constexpr (i & 1)
+            mfma_first(dp_[P ^ 1], f1[i % 3], vf[i >> 1]);
+          else
+            mfma_first(s_[P ^ 1], f1[i % 3], kf[i >> 1]);
+        } else {
+          if constexpr (i & 1)
+            mfma_next(dp_[P ^ 1], f1[i % 3], vf[i >> 1]);
+          else
+            mfma_next(s_[P ^ 1], f1[i % 3], kf[i >> 1]);
+        }
+        if constexpr (i == NOPS - 1) score_settle(s_[P ^ 1], dp_[P ^ 1]);
       }
       if constexpr (G2) {
         const int ch = i % (2 * MB);
@@ -648,7 +675,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
+    for (int dc = 0; dc < DC; ++dc) {       // only MFMAs read them: keep them in AGPRs
       qf[cb][dc] = settle(qf[cb][dc]);
       df[cb][dc] = settle(df[cb][dc]);
     }
@@ -747,13 +774,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     if constexpr (G1) fk[0] = kfr(0);
     if constexpr (G2) ft[0] = tfr(0);
     float dt[2][8];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (u + 1 < NU) {
+    static_for<NU>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u + 1 < NU) {
         if constexpr (G1) fk[(u + 1) & 1] = kfr(u + 1);
         if constexpr (G2) ft[(u + 1) & 1] = tfr(u + 1);
       }
-      if (u + 1 == NU) {
+      if constexpr (u + 1 == NU) {
         if constexpr (G1) fv[0] = vfr(0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -767,8 +794,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
       if constexpr (EW) {
         // values [v0, v1) of the 32 score registers (16 per column block)
-        const int v0 = (u * 32) / NU;
-        const int v1 = ((u + 1) * 32) / NU;
+        constexpr int v0 = (u * 32) / NU;
+        constexpr int v1 = ((u + 1) * 32) / NU;
 #pragma unroll
         for (int vv = v0; vv < v1; ++vv) {
           const int cb = vv >> 4;
@@ -786,7 +813,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
           }
         }
       }
-    }
+    });
     if constexpr (G1) {
       static_for<NU>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
