@@ -49,8 +49,8 @@ KERNEL_SOURCES = {
 KERNEL_SYMBOLS = {
     "fwd_prefill_bf16": "fwd_prefill_kernel<128>",
     "fwd_split_bf16": "fwd_split_kernel<128>",
-    "bwd_dkdv": "bwd_dkdv_kernel<128>",
-    "bwd_dq": "bwd_dq_kernel<128>",
+    "bwd_dkdv": "bwd_dkdv_kernel<128",
+    "bwd_dq": "bwd_dq_kernel<128",
     "bwd_pre": "bwd_pre_kernel<128>",
     "transpose_rows": "transpose_rows_kernel<128>",
 }
@@ -311,6 +311,28 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch
         print(kern, out["hbm_bytes_per_launch"])
 
 
+def _short_kernel_name(name: str) -> str:
+    # "void attn::(anonymous namespace)::bwd_dq_kernel<128, true>(attn::...)" -> "bwd_dq_kernel<128, true>"
+    name = name.replace("void ", "").replace("attn::(anonymous namespace)::", "")
+    return name.split("(")[0].strip()
+
+
+def summarize_stats(stats_csv: str, title: str, out_md: str, command: str) -> None:
+    """Markdown table of a rocprofv3 --stats kernel_stats.csv, written to out_md."""
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# rocprofv3 kernel statistics: {title}", "",
+             "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,11 +343,15 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5,
                     metavar=("WORKLOAD", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "OUT_MD"))
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, command=args.command)
+        return 0
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats, command=args.command)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
