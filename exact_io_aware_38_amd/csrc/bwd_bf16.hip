@@ -49,30 +49,6 @@ constexpr int BT = 32;        // rows of a pipeline tile (queries for dK/dV, key
 constexpr int KV_WG = 128;    // keys per dK/dV workgroup (4 wavefronts x 32)
 constexpr int Q_WG = 256;     // queries per dQ workgroup (4 wavefronts x 64)
 
-// Pins where values are computed: results that are only consumed in the next
-// pipeline step would otherwise all be computed in one block just before the
-// step boundary (instruction selection places pure arithmetic next to its
-// first chained use), instead of interleaved with the MFMAs they should hide
-// behind. The empty volatile statement forces them to exist at this point.
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float& x, float& y) { asm volatile("" : "+v"(x), "+v"(y)); }
-__device__ __forceinline__ void pin(bf16x8& x) {
-  u32x4 w = __builtin_bit_cast(u32x4, x);
-  asm volatile("" : "+v"(w));
-  x = __builtin_bit_cast(bf16x8, w);
-}
-
-// f(integral_constant<int, I>) for I = 0 .. N-1, in order, with I usable as
-// a compile-time constant inside f.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Score MFMAs with the accumulator in VGPRs (the elementwise code reads every
 // score; AGPR accumulators would need one v_accvgpr_read per score), issued
 // as inline assembly because the kernels otherwise compile with AGPR

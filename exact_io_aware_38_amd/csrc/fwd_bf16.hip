@@ -79,12 +79,15 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int DC = D / 16;
   constexpr int CPR = D / 8;                    // 16-byte chunks per K row
   constexpr int RB = 2 * D;                     // bytes per K row
+  constexpr int NP = 2 * DC;                    // MFMA pairs per step (= 4 * MB for the PV half)
+  constexpr int NDMA = 2 * R::INSTR;            // DMA instructions per wavefront per step
+  static_assert(R::NSTAGE == 4, "the main loop is unrolled by the ring size");
 
   __shared__ __attribute__((aligned(1024))) char smem[R::NSTAGE * R::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool phase_b = wid >= 4;
@@ -107,10 +110,6 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   int kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
   if (kend < 0) kend = 0;
   const int ntiles = (kend + BC - 1) / BC;
-  const int wave_maxpos = min(p0 + 31, a.Sq - 1);
-  int kend_w = a.causal ? min(kend, wave_maxpos + off + 1) : kend;
-  if (p0 >= a.Sq || kend_w < 0) kend_w = 0;
-  const int nt_w = (kend_w + BC - 1) / BC;       // tiles this wavefront computes (a prefix)
   const int mask_from = a.causal ? max(0, min(kend, p0 + off + 1)) : kend;
   const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
 
@@ -124,45 +123,61 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
     // load is pending on them inside the loop, where a wait on the memory
     // counter would also wait for the K/V prefetch in flight.
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      u32x4 t = __builtin_bit_cast(u32x4, qf[dc]);
-      asm volatile("" : "+v"(t));
-      qf[dc] = __builtin_bit_cast(bf16x8, t);
-    }
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
   }
   const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
   const bf16* vtg = a.vt + ((size_t)b * a.Hkv + hkv) * (size_t)D * a.skp;
 
+  // Per-lane LDS read offsets (the ring slot and the constant parts of each
+  // fragment's address are immediate offsets of the reads): K row l32 (+32 for
+  // the second key block) at logical chunk 2 dc + hi; V^T row l32 (+32 mb) at
+  // logical chunk 2 kc + hi.
+  constexpr int KCH = BC / 16;                  // 16-key chunks of a tile
+  uint32_t kb[DC], vb[KCH];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) kb[dc] = l32 * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+#pragma unroll
+  for (int kc = 0; kc < KCH; ++kc) vb[kc] = R::TILE + l32 * (2 * BC) + (((2 * kc + hi) ^ vt_swizzle(l32)) << 4);
+
   // Per-lane DMA geometry: lane i of instruction n writes LDS chunk
   // P = (wid*INSTR + n)*64 + i of a tile, i.e. K row P / CPR, physical chunk
   // P % CPR (V^T row P / 8, physical chunk P % 8), and loads the logical chunk
-  // (physical ^ swizzle(row)) from global memory.
-  int krow[R::INSTR], koff[R::INSTR], voff[R::INSTR];
+  // (physical ^ swizzle(row)); byte offsets relative to the tile's first key.
+  uint32_t koff[R::INSTR], voff[R::INSTR];
 #pragma unroll
   for (int n = 0; n < R::INSTR; ++n) {
     const int P = (wid * R::INSTR + n) * 64 + lane;
-    krow[n] = P / CPR;
-    koff[n] = ((P % CPR) ^ chunk_swizzle<D>(krow[n])) * 8;
+    const int krow = P / CPR;
+    koff[n] = krow * RB + (((P % CPR) ^ chunk_swizzle<D>(krow)) << 4);
     const int vrow = P / 8;
-    voff[n] = vrow * a.skp + ((P % 8) ^ vt_swizzle(vrow)) * 8;
+    voff[n] = (uint32_t)(vrow * a.skp + ((P % 8) ^ vt_swizzle(vrow)) * 8) * 2;
   }
-  // DMA instruction q (0 .. 2*INSTR-1) of tile t: K for even q, V^T for odd q.
-  auto issue_one = [&](int t, int q) {
-    const int key0 = t * BC;
-    char* stage = smem + (t % R::NSTAGE) * R::STAGE;
-    const int n = q >> 1;
-    if ((q & 1) == 0) {
-      // rows past kend repeat row kend-1 (finite data; their probabilities are masked to 0)
-      const bf16* ks = (key0 + BC <= kend) ? kg + (size_t)key0 * D + krow[n] * D + koff[n]
-                                           : kg + (size_t)min(key0 + krow[n], kend - 1) * D + koff[n];
-      dma16(ks, (lds_void*)(stage + (wid * R::INSTR + n) * 1024));
-    } else {
-      dma16(vtg + key0 + voff[n], (lds_void*)(stage + R::TILE + (wid * R::INSTR + n) * 1024));
-    }
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + wid * R::INSTR * 1024);
+  const u32x4 rvt = buffer_rsrc(vtg, (uint32_t)a.skp * (2 * D));
+  // DMA of key tile t (clamped to the last one: past it, the last tile is
+  // reloaded into a slot nobody reads, which keeps the per-step DMA count
+  // uniform). K rows past kend are out of the buffer's range and read zeros;
+  // their scores are masked.
+  struct Dma {
+    u32x4 rk;
+    uint32_t sv;
   };
-  auto issue = [&](int t) {
-#pragma unroll
-    for (int q = 0; q < 2 * R::INSTR; ++q) issue_one(t, q);
+  auto dma_for = [&](int t) __attribute__((always_inline)) {
+    Dma d;
+    const int key0 = min(t, ntiles - 1) * BC;
+    d.rk = buffer_rsrc(kg + (size_t)key0 * D, (uint32_t)(kend - key0) * RB);
+    d.sv = (uint32_t)key0 * 2;
+    return d;
+  };
+  // DMA instruction QI (0 .. NDMA-1) into ring slot SLOT: K for even QI, V^T for odd
+  auto issue_one = [&](auto slot_, auto qi_, const Dma& d) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_)::value;
+    constexpr int QI = decltype(qi_)::value;
+    constexpr int n = QI >> 1;
+    if constexpr ((QI & 1) == 0)
+      dma16b_at<SLOT * R::STAGE + n * 1024>(d.rk, koff[n], 0u, ldsw);
+    else
+      dma16b_at<SLOT * R::STAGE + R::TILE + n * 1024>(rvt, voff[n], d.sv, ldsw);
   };
 
   f32x16 acc[MB];
@@ -172,49 +187,52 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   bf16x8 pf[4];
   f32x16 s[2];
 
-  // One basic block of MFMAs: S(j) = K_j Q^T (16 MFMAs, 2 chains) interleaved
-  // one-for-one with O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs, MB chains); with the
-  // two products alternating, a chain's next MFMA issues at least four MFMAs
-  // after its previous one (a dependent MFMA waits ~150 cycles for its
-  // predecessor). LDS operand fragments are loaded two pairs ahead so that
-  // their latency is covered by the MFMAs in between.
-  auto mma = [&](auto do_s, auto do_pv, int j, int dma_tile) {
-    const char* stK = smem + (j % R::NSTAGE) * R::STAGE;
-    const char* stV = smem + ((j + R::NSTAGE - 1) % R::NSTAGE) * R::STAGE + R::TILE;
-    constexpr int NP = 2 * DC;                 // MFMA pairs (= 4 * MB for the PV half)
-    auto kfrag = [&](int i) {                  // pair i: kb = i & 1, dc = i >> 1
-      const int r = 32 * (i & 1) + l32;
-      return *(const bf16x8*)(stK + r * RB + (((2 * (i >> 1) + hi) ^ chunk_swizzle<D>(r)) << 4));
+  // One basic block of MFMAs (step j, slot position POS = j mod 4): S(j) =
+  // K_j Q^T (16 MFMAs, 2 chains) interleaved one-for-one with O^T +=
+  // V_{j-1}^T P_{j-1}^T (16 MFMAs, MB chains), so a chain's next MFMA issues at
+  // least four MFMAs after its previous one. LDS operand fragments are loaded
+  // two pairs ahead; the DMA of tile j+2 rides in the shadow of the MFMAs.
+  auto mma = [&](auto pos_, auto do_s, auto do_pv, int j) __attribute__((always_inline)) {
+    constexpr int POS = decltype(pos_)::value;
+    constexpr bool DS = decltype(do_s)::value;
+    constexpr bool DP = decltype(do_pv)::value;
+    constexpr int SK = POS;                     // K of tile j
+    constexpr int SV = (POS + 3) % 4;           // V^T of tile j-1
+    constexpr int SD = (POS + 2) % 4;           // DMA target: tile j+2
+    const char* lds = smem;
+    auto kfrag = [&](int i) __attribute__((always_inline)) {   // pair i: key block i & 1, d-chunk i >> 1
+      return *(const bf16x8*)(lds + kb[i >> 1] + SK * R::STAGE + (i & 1) * 32 * RB);
     };
-    auto vfrag = [&](int i) {                  // pair i: mb = i % MB, kc = i / MB
-      const int d = 32 * (i % MB) + l32;
-      return *(const bf16x8*)(stV + d * (2 * BC) + (((2 * (i / MB) + hi) ^ vt_swizzle(d)) << 4));
+    static_assert(NP / MB == KCH, "one key chunk per MB pairs");
+    auto vfrag = [&](int i) __attribute__((always_inline)) {   // pair i: d-block i % MB, key chunk i / MB
+      return *(const bf16x8*)(lds + vb[i / MB] + SV * R::STAGE + (i % MB) * 32 * (2 * BC));
     };
+    Dma d;
+    if constexpr (DS) d = dma_for(j + 2);
     bf16x8 kq[3], vq[3];
-    if constexpr (do_s.value) {
-      s[0] = s[1] = f32x16{};
+    if constexpr (DS) {
       kq[0] = kfrag(0);
       kq[1] = kfrag(1);
     }
-    if constexpr (do_pv.value) {
+    if constexpr (DP) {
       vq[0] = vfrag(0);
       vq[1] = vfrag(1);
     }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      if (i + 2 < NP) {
-        if constexpr (do_s.value) kq[(i + 2) % 3] = kfrag(i + 2);
-        if constexpr (do_pv.value) vq[(i + 2) % 3] = vfrag(i + 2);
+    constexpr int EVERY = NP / NDMA;
+    static_for<NP>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 2 < NP) {
+        if constexpr (DS) kq[(i + 2) % 3] = kfrag(i + 2);
+        if constexpr (DP) vq[(i + 2) % 3] = vfrag(i + 2);
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the reads two pairs ahead of their MFMAs
-      if constexpr (do_s.value) s[i & 1] = mfma32(kq[i % 3], qf[i >> 1], s[i & 1]);
-      if constexpr (do_pv.value) acc[i % MB] = mfma32(vq[i % 3], pf[i / MB], acc[i % MB]);
-      // the prefetch of a later tile rides in the shadow of the MFMAs
-      constexpr int EVERY = NP / (2 * R::INSTR);
-      if (i % EVERY == EVERY - 1 && dma_tile >= 0) issue_one(dma_tile, i / EVERY);
-    }
+      if constexpr (DS) s[i & 1] = mfma32(kq[i % 3], qf[i >> 1], i < 2 ? f32x16{} : s[i & 1]);
+      if constexpr (DP) acc[i % MB] = mfma32(vq[i % 3], pf[i / MB], acc[i % MB]);
+      if constexpr (DS && i % EVERY == EVERY - 1)
+        issue_one(std::integral_constant<int, SD>{}, std::integral_constant<int, i / EVERY>{}, d);
+    });
   };
-  auto softmax = [&](int j) {
+  auto softmax = [&](int j) __attribute__((always_inline)) {
     const int key0 = j * BC;
     float v[32];
 #pragma unroll
@@ -251,32 +269,54 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // step j: tile j has landed for every wavefront (each waits for its own
+  // DMA, the barrier for all of them), and every wavefront is done with step
+  // j-1. Every step that computes scores issues NDMA DMA instructions.
+  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
+  // Wavefronts whose rows see no key of a tile still run it (their scores are
+  // all masked, so P = 0): the step sequence is the same for the whole workgroup.
+  auto full = [&](auto pos_, int j) __attribute__((always_inline)) {
+    sync();
+    if (phase_b) softmax(j - 1);
+    mma(pos_, T_{}, T_{}, j);
+    if (!phase_b) softmax(j);
+  };
 
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
-  for (int j = 0; j <= ntiles; ++j) {
-    // tile j has landed in LDS for every wavefront (each waits for its own DMA,
-    // the barrier for all of them), and every wavefront is done with tile j-2
-    if (j + 1 < ntiles) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * R::INSTR) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    const int dma_tile = (j + 2 < ntiles) ? j + 2 : -1;
-    const bool ds = j < nt_w;                  // scores of tile j
-    const bool dp = j >= 1 && j - 1 < nt_w;    // P V of tile j-1
-    if (phase_b && dp) softmax(j - 1);
-    if (ds && dp) {
-      mma(T_{}, T_{}, j, dma_tile);
-    } else if (ds) {
-      mma(T_{}, F_{}, j, dma_tile);
-    } else if (dp) {
-      mma(F_{}, T_{}, j, dma_tile);
-    } else if (dma_tile >= 0) {
-      issue(dma_tile);
-    }
-    if (!phase_b && ds) softmax(j);
+  if (ntiles > 0) {
+    const Dma d0 = dma_for(0), d1 = dma_for(1);
+    static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { issue_one(I0{}, qi, d0); });
+    static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { issue_one(I1{}, qi, d1); });
+    sync();
+    mma(I0{}, T_{}, F_{}, 0);
+    if (!phase_b) softmax(0);
   }
+  int j = 1;
+  for (; j + 3 < ntiles; j += 4) {
+    full(I1{}, j);
+    full(I2{}, j + 1);
+    full(I3{}, j + 2);
+    full(I0{}, j + 3);
+  }
+  if (j < ntiles) full(I1{}, j);
+  if (j + 1 < ntiles) full(I2{}, j + 1);
+  if (j + 2 < ntiles) full(I3{}, j + 2);
+  if (ntiles > 0) {
+    // P V of the last tile (its V^T sits in slot (ntiles - 1) mod 4); no
+    // barrier is needed since no DMA writes that slot any more
+    if (phase_b) softmax(ntiles - 1);
+    switch (ntiles & 3) {
+      case 0: mma(I0{}, F_{}, T_{}, ntiles); break;
+      case 1: mma(I1{}, F_{}, T_{}, ntiles); break;
+      case 2: mma(I2{}, F_{}, T_{}, ntiles); break;
+      default: mma(I3{}, F_{}, T_{}, ntiles); break;
+    }
+  }
+  // no LDS DMA may still be in flight when the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;

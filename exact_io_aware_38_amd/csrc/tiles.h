@@ -5,6 +5,9 @@
 
 #include "common.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace attn {
 namespace {
 
@@ -92,6 +95,30 @@ __device__ __forceinline__ void dma4b_at(u32x4 rsrc, uint32_t voff, uint32_t sof
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF)
                : "memory", "m0", "scc");
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order, with I usable as
+// a compile-time constant inside f.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Pins where values are computed: results that are only consumed in the next
+// pipeline step would otherwise all be computed in one block just before the
+// step boundary (instruction selection places pure arithmetic next to its
+// first chained use), instead of interleaved with the MFMAs they should hide
+// behind. The empty volatile statement forces them to exist at this point.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x, float& y) { asm volatile("" : "+v"(x), "+v"(y)); }
+__device__ __forceinline__ void pin(bf16x8& x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(w));
+  x = __builtin_bit_cast(bf16x8, w);
 }
 
 // Re-define a value that a global load produced before a loop, so the
