@@ -342,25 +342,24 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
 // MFMA columns pack (query head of the group, query row) pairs, so each K/V
 // byte of the slice is read once for all of them. Writes the slice's
 // normalised partial output and lse; combine_split_kernel merges the slices.
+//
+// The kernel streams K and V from HBM once, so it is sized for occupancy
+// (about eight wavefronts per CU keep enough loads in flight): 32-key tiles,
+// K fragments (the A operand of S^T = K Q^T) loaded straight into registers
+// one tile ahead by range-checked buffer loads, V tiles by LDS DMA into a
+// 2-slot ring (16 KB per wavefront at d = 128) and read transposed for
+// O^T = V^T P^T.
 // ---------------------------------------------------------------------------
 template <int D>
-struct SplitTile {
-  static constexpr int KS = D + 8;       // K row stride in LDS (bf16), 16 B pad
-  static constexpr int VS = D + 16;      // V row stride in LDS (bf16), 32 B pad
-  static constexpr int K_ELEMS = BC * KS;
-  static constexpr int V_ELEMS = BC * VS;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-};
-
-template <int D>
 __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
-  using T = SplitTile<D>;
-  constexpr int CH_ROW = D / 8;
-  constexpr int CH_THR = BC * CH_ROW / 64;
+  constexpr int BK = 32;                        // keys per tile
   constexpr int MB = D / 32;
   constexpr int DC = D / 16;
-
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::BUF];
+  constexpr int RB = 2 * D;                     // bytes per K or V row
+  constexpr int VT = BK * RB;                   // bytes of a V tile
+  constexpr int NV = VT / 1024;                 // DMA instructions per V tile
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  __shared__ __attribute__((aligned(1024))) char smem[2 * VT];
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -379,7 +378,7 @@ __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
   int kend = min(a.Sk, kbeg + a.split_keys);
   if (a.causal) kend = min(kend, a.Sq - 1 + off + 1);
   if (kend < kbeg) kend = kbeg;
-  const int ntiles = (kend - kbeg + BC - 1) / BC;
+  const int ntiles = (kend - kbeg + BK - 1) / BK;
   const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
   const int mask_from = a.causal ? max(kbeg, min(kend, off + 1)) : kend;
 
@@ -389,78 +388,78 @@ __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
   }
-  const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-  const bf16* vg = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
+  const size_t kvh = (size_t)b * a.Hkv + hkv;
+  // whole-head buffers: rows past Sk read zeros (their scores are masked or,
+  // for V, multiplied by P = 0)
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + kvh * (size_t)a.Sk * D), (short)0, a.Sk * RB, 0x00020000);
+  const u32x4 rv = buffer_rsrc(a.v + kvh * (size_t)a.Sk * D, (uint32_t)a.Sk * RB);
+  // K fragment dc of key row l32: byte l32*RB + 16*hi + 32*dc of the tile
+  const uint32_t kl = l32 * RB + 16 * hi;
+  // V DMA: lane of instruction n writes LDS chunk P = 64 n + lane of the tile,
+  // i.e. row P / CPR, physical chunk P % CPR, holding logical chunk
+  // (physical ^ chunk_swizzle(row))
+  uint32_t vo[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const int P = 64 * n + lane;
+    const int r = P / CPR;
+    vo[n] = r * RB + (((P % CPR) ^ chunk_swizzle<D>(r)) << 4);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
-  u32x4 kreg[CH_THR], vreg[CH_THR];
-  auto load_tile = [&](int t) {
-    const int key0 = kbeg + t * BC;
+  auto load_k = [&](int t, bf16x8* kf) __attribute__((always_inline)) {
+    const uint32_t base = kl + (uint32_t)(kbeg + t * BK) * RB;
 #pragma unroll
-    for (int i = 0; i < CH_THR; ++i) {
-      const int c = lane + i * 64;
-      const int row = c / CH_ROW;
-      const int col = c % CH_ROW;
-      const int key = key0 + row;
-      if (key < kend) {
-        kreg[i] = *(const u32x4*)(kg + (size_t)key * D + col * 8);
-        vreg[i] = *(const u32x4*)(vg + (size_t)key * D + col * 8);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int dc = 0; dc < DC; ++dc)
+      kf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, base + 32 * dc, 0, 0));
   };
-  auto store_tile = [&](int buf) {
-    bf16* sk = smem + buf * T::BUF;
-    bf16* sv = sk + T::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < CH_THR; ++i) {
-      const int c = lane + i * 64;
-      const int row = c / CH_ROW;
-      const int col = c % CH_ROW;
-      *(u32x4*)(sk + row * T::KS + col * 8) = kreg[i];
-      *(u32x4*)(sv + row * T::VS + col * 8) = vreg[i];
-    }
+  auto load_v = [&](int t, auto slot_) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_)::value;
+    const uint32_t base = (uint32_t)(kbeg + t * BK) * RB;
+    static_for<NV>([&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      dma16b_at<SLOT * VT + n * 1024>(rv, vo[n] + base, 0u, lds0);
+    });
   };
 
   f32x16 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
   float m2 = kNegInf, lsum = 0.f;
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  bf16x8 kcur[DC], knext[DC];
   const int L = lane & 15;
   const int dhalf = (lane >> 4) & 1;
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int key0 = kbeg + t * BC;
-    const bf16* sk = smem + cur * T::BUF;
-    const bf16* sv = sk + T::K_ELEMS;
-    f32x16 s[2];
-    s[0] = s[1] = f32x16{};
+
+  auto tile = [&](int t, auto slot_) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_)::value;
+    // every load of tile t has arrived (the compiler waits on the memory
+    // counter before the re-definition, which also covers the V DMA issued
+    // with them); then the next tile's loads go out
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma32(*(const bf16x8*)(sk + (32 * kb + l32) * T::KS + 16 * dc + 8 * hi), qf[dc], s[kb]);
-    if (key0 + BC > mask_from) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (key > lim) s[kb][i] = kNegInf;
-        }
+    for (int dc = 0; dc < DC; ++dc) kcur[dc] = settle(knext[dc]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (t + 1 < ntiles) {
+      load_k(t + 1, knext);
+      load_v(t + 1, std::integral_constant<int, SLOT ^ 1>{});
     }
-    float mx = fmaxf(s[0][0], s[1][0]);
+    const int key0 = kbeg + t * BK;
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    for (int dc = 0; dc < DC; ++dc) s = mfma32(kcur[dc], qf[dc], dc == 0 ? f32x16{} : s);
+    if (key0 + BK > mask_from) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        if (key > lim) s[i] = kNegInf;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = max_halves(mx) * a.c;
     const bool grow = mx > m2 + RESCALE_T;
     if (wave_any(grow)) {
@@ -472,30 +471,44 @@ __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
       m2 = mnew;
     }
     const float msub = (m2 == kNegInf) ? 0.f : m2;
-    bf16x8 pf[4];
+    bf16x8 pf[2];
     float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int h = 0; h < 2; ++h) {
+      float p[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(s[kb][8 * h + e], a.c, -msub));
-          ps += p[e];
-        }
-        pf[2 * kb + h] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(s[8 * h + e], a.c, -msub));
+        ps += p[e];
       }
+      pf[h] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    }
     lsum += ps;
+    // O^T += V^T P^T: A operand rows d = 32 mb + l32, reduction slots = the 8
+    // keys of P's register order, read transposed from the row-major V tile
+    const char* sv = smem + SLOT * VT;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16* vp = sv + (16 * kc + 4 * hi + (L >> 2)) * T::VS + 32 * mb + 16 * dhalf + 4 * (L & 3);
-        acc[mb] = mfma32(cat4(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS)), pf[kc], acc[mb]);
+      for (int kc = 0; kc < 2; ++kc) {
+        const int r = 16 * kc + 4 * hi + (L >> 2);
+        const int c = 32 * mb + 16 * dhalf + 4 * (L & 3);
+        const bf16* p0 = (const bf16*)(sv + r * RB + (((c >> 3) ^ chunk_swizzle<D>(r)) << 4) + (c & 7) * 2);
+        const bf16* p1 = (const bf16*)(sv + (r + 8) * RB + (((c >> 3) ^ chunk_swizzle<D>(r + 8)) << 4) + (c & 7) * 2);
+        acc[mb] = mfma32(cat4(lds_read_tr(p0), lds_read_tr(p1)), pf[kc], acc[mb]);
       }
-    if (t + 1 < ntiles) store_tile(cur ^ 1);
+  };
+
+  if (ntiles > 0) {
+    load_k(0, knext);
+    load_v(0, std::integral_constant<int, 0>{});
   }
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    tile(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
 
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
