@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       f2[0] = g2_frag(0);
       f2[1] = g2_frag(1);
     }
-    float pt[8], dt[8];
+    float ex[8], pt[8], dt[8];
     static_for<NOPS>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + 2 < NOPS) {
@@ -431,25 +431,52 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           dkt[ch - MB] = mfma32(f2[i % 3], dsf[P ^ 1][qc], dkt[ch - MB]);
       }
       if constexpr (EW) {
-        // values [v0, v1) of the 16 score registers; the first step only reads lse2 / D
-        constexpr int v0 = i == 0 ? 0 : ((i - 1) * 16) / (NOPS - 1);
-        constexpr int v1 = i == 0 ? 0 : (i * 16) / (NOPS - 1);
+        // The 16 score registers in NG groups, each through three stages in
+        // consecutive MFMA pairs: x = s c - lse2 (pair g + 1), p = 2^x with the
+        // mask (pair g + 2), dS = p (dP - D) (pair g + 3). A pair then carries
+        // the stages of three different groups, whose instructions do not
+        // depend on each other, so in-order issue does not stall on the
+        // latency of a single chain. The stages run in reverse order inside a
+        // pair, so a later group's stage never overwrites a value an earlier
+        // group still has to consume in the same pair.
+        constexpr int NG = NOPS >= 11 ? 8 : 4;
+        constexpr int GS = 16 / NG;
+        if constexpr (i >= 3 && i - 3 < NG) {       // stage 3 of group i - 3
+          constexpr int g = i - 3;
 #pragma unroll
-        for (int v = v0; v < v1; ++v) {
-          const float l2 = l2v[v >> 2][v & 3];
-          const float dl = dlv[v >> 2][v & 3];
-          float p = fast_exp2(__builtin_fmaf(s_[P][v], a.c, -l2));
-          if constexpr (MASK) {
-            if (key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) p = 0.f;
+          for (int e = 0; e < GS; ++e) {
+            const int v = g * GS + e;
+            dt[v & 7] = pt[v & 7] * (dp_[P][v] - dlv[v >> 2][v & 3]);
+            pin(dt[v & 7]);
           }
-          pt[v & 7] = p;
-          dt[v & 7] = p * (dp_[P][v] - dl);
-          pin(pt[v & 7], dt[v & 7]);
-          if ((v & 7) == 7) {
-            pf[P][v >> 3] = to_bf16x8(pt[0], pt[1], pt[2], pt[3], pt[4], pt[5], pt[6], pt[7]);
-            dsf[P][v >> 3] = to_bf16x8(dt[0], dt[1], dt[2], dt[3], dt[4], dt[5], dt[6], dt[7]);
-            pin(pf[P][v >> 3]);
-            pin(dsf[P][v >> 3]);
+          if constexpr ((g * GS + GS) % 8 == 0) {
+            constexpr int h = (g * GS) / 8;
+            pf[P][h] = to_bf16x8(pt[0], pt[1], pt[2], pt[3], pt[4], pt[5], pt[6], pt[7]);
+            dsf[P][h] = to_bf16x8(dt[0], dt[1], dt[2], dt[3], dt[4], dt[5], dt[6], dt[7]);
+            pin(pf[P][h]);
+            pin(dsf[P][h]);
+          }
+        }
+        if constexpr (i >= 2 && i - 2 < NG) {       // stage 2 of group i - 2
+          constexpr int g = i - 2;
+#pragma unroll
+          for (int e = 0; e < GS; ++e) {
+            const int v = g * GS + e;
+            float p = fast_exp2(ex[v & 7]);
+            if constexpr (MASK) {
+              if (key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) p = 0.f;
+            }
+            pt[v & 7] = p;
+            pin(pt[v & 7]);
+          }
+        }
+        if constexpr (i >= 1 && i - 1 < NG) {       // stage 1 of group i - 1
+          constexpr int g = i - 1;
+#pragma unroll
+          for (int e = 0; e < GS; ++e) {
+            const int v = g * GS + e;
+            ex[v & 7] = __builtin_fmaf(s_[P][v], a.c, -l2v[v >> 2][v & 3]);
+            pin(ex[v & 7]);
           }
         }
       }
