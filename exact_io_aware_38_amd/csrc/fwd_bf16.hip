@@ -19,12 +19,11 @@
 //    query row: the row max and sum reduce inside the lane plus one swap between
 //    lane halves, and the probabilities already sit in the B-operand layout of
 //    O^T = V^T P^T;
-//  * V is first transposed once per call into a [d][keys] workspace whose keys
-//    are permuted inside each group of 16 so that one 16-byte LDS read yields
-//    the 8 keys an MFMA lane needs (transposed LDS reads are several times
-//    slower than row reads on this chip);
-//  * K and V^T tiles (64 keys) go HBM -> LDS through the DMA path of
-//    global_load_lds into a 4-stage ring, issued two tiles ahead;
+//  * K and V tiles (64 keys, row-major, 16-byte chunks XOR-swizzled per row)
+//    go HBM -> LDS through the LDS DMA path of buffer loads into a 4-stage
+//    ring, issued two tiles ahead; the V^T operand of O^T = V^T P^T comes
+//    from transposing LDS reads (ds_read_b64_tr_b16) of the row-major V
+//    tile, which the swizzle keeps free of bank conflicts;
 //  * two wavefronts share each SIMD and run the per-tile steps in opposite
 //    orders so that one's softmax (vector ALU) overlaps the other's MFMAs;
 //  * exp2 with log2(e) folded into the score scale: one FMA and one v_exp_f32
@@ -47,13 +46,11 @@ struct FwdArgs {
   const bf16* q;
   const bf16* k;
   const bf16* v;
-  const bf16* vt;    // prefill: transposed V, [B, Hkv, D, skp], keys permuted by vt_perm
   bf16* o;
   float* lse;
   float* part_o;     // split path: [nsplit, B, Hq, Sq, D]
   float* part_lse;   // split path: [nsplit, B, Hq, Sq]
   int B, Hq, Hkv, Sq, Sk, g, causal;
-  int skp;           // Sk rounded up to the key tile
   float c;           // scale * log2(e)
   int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
   int nsplit, split_keys;
@@ -66,8 +63,8 @@ struct FwdArgs {
 // ---------------------------------------------------------------------------
 template <int D>
 struct Ring {
-  static constexpr int TILE = BC * D * 2;       // bytes of one K or V^T tile
-  static constexpr int STAGE = 2 * TILE;        // K then V^T
+  static constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;        // K then V
   static constexpr int NSTAGE = 4;
   static constexpr int INSTR = D / 64;          // DMA instructions per wavefront per tensor per tile
 };
@@ -125,51 +122,61 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
   }
-  const bf16* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-  const bf16* vtg = a.vt + ((size_t)b * a.Hkv + hkv) * (size_t)D * a.skp;
+  const size_t kvh = ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
+  const bf16* kg = a.k + kvh;
+  const bf16* vg = a.v + kvh;
 
   // Per-lane LDS read offsets (the ring slot and the constant parts of each
-  // fragment's address are immediate offsets of the reads): K row l32 (+32 for
-  // the second key block) at logical chunk 2 dc + hi; V^T row l32 (+32 mb) at
-  // logical chunk 2 kc + hi.
-  constexpr int KCH = BC / 16;                  // 16-key chunks of a tile
-  uint32_t kb[DC], vb[KCH];
+  // fragment's address are immediate offsets of the reads). K: row l32 (+32
+  // for the second key block) at logical chunk 2 dc + hi. V: the A operand of
+  // O^T = V^T P^T for d-block mb and 16-key chunk kc is two transposing 4-key
+  // reads at rows 16 kc + 4 hi + (L >> 2) (+8), columns 32 mb + 16 dhalf +
+  // 4 (L & 3); their keys line up with the register order of the P fragments.
+  // The swizzle of those rows does not change with kc (16 kc adds nothing to
+  // the row bits it uses), so kc is an immediate offset too.
+  uint32_t kb[DC], vb[MB][2];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) kb[dc] = l32 * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+  {
+    const int L = lane & 15, dhalf = (lane >> 4) & 1;
 #pragma unroll
-  for (int kc = 0; kc < KCH; ++kc) vb[kc] = R::TILE + l32 * (2 * BC) + (((2 * kc + hi) ^ vt_swizzle(l32)) << 4);
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 4 * hi + (L >> 2) + 8 * h;
+        const int c = 32 * mb + 16 * dhalf + 4 * (L & 3);
+        vb[mb][h] = R::TILE + r * RB + (((c >> 3) ^ chunk_swizzle<D>(r)) << 4) + (c & 7) * 2;
+      }
+  }
 
-  // Per-lane DMA geometry: lane i of instruction n writes LDS chunk
-  // P = (wid*INSTR + n)*64 + i of a tile, i.e. K row P / CPR, physical chunk
-  // P % CPR (V^T row P / 8, physical chunk P % 8), and loads the logical chunk
-  // (physical ^ swizzle(row)); byte offsets relative to the tile's first key.
-  uint32_t koff[R::INSTR], voff[R::INSTR];
+  // Per-lane DMA geometry (the same for K and V tiles): lane i of instruction
+  // n writes LDS chunk P = (wid*INSTR + n)*64 + i of a tile, i.e. row P / CPR,
+  // physical chunk P % CPR, and loads the logical chunk (physical ^
+  // swizzle(row)); byte offsets relative to the tile's first key.
+  uint32_t koff[R::INSTR];
 #pragma unroll
   for (int n = 0; n < R::INSTR; ++n) {
     const int P = (wid * R::INSTR + n) * 64 + lane;
     const int krow = P / CPR;
     koff[n] = krow * RB + (((P % CPR) ^ chunk_swizzle<D>(krow)) << 4);
-    const int vrow = P / 8;
-    voff[n] = (uint32_t)(vrow * a.skp + ((P % 8) ^ vt_swizzle(vrow)) * 8) * 2;
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + wid * R::INSTR * 1024);
-  const u32x4 rvt = buffer_rsrc(vtg, (uint32_t)a.skp * (2 * D));
   // DMA of key tile t (clamped to the last one: past it, the last tile is
   // reloaded into a slot nobody reads, which keeps the per-step DMA count
-  // uniform). K rows past kend are out of the buffer's range and read zeros;
-  // their scores are masked.
+  // uniform). K and V rows past kend are out of the buffers' range and read
+  // zeros: their scores are masked and their P is 0 (and 0 * 0 stays 0).
   struct Dma {
-    u32x4 rk;
-    uint32_t sv;
+    u32x4 rk, rv;
   };
   auto dma_for = [&](int t) __attribute__((always_inline)) {
     Dma d;
     const int key0 = min(t, ntiles - 1) * BC;
-    d.rk = buffer_rsrc(kg + (size_t)key0 * D, (uint32_t)(kend - key0) * RB);
-    d.sv = (uint32_t)key0 * 2;
+    const uint32_t bytes = (uint32_t)(kend - key0) * RB;
+    d.rk = buffer_rsrc(kg + (size_t)key0 * D, bytes);
+    d.rv = buffer_rsrc(vg + (size_t)key0 * D, bytes);
     return d;
   };
-  // DMA instruction QI (0 .. NDMA-1) into ring slot SLOT: K for even QI, V^T for odd
+  // DMA instruction QI (0 .. NDMA-1) into ring slot SLOT: K for even QI, V for odd
   auto issue_one = [&](auto slot_, auto qi_, const Dma& d) __attribute__((always_inline)) {
     constexpr int SLOT = decltype(slot_)::value;
     constexpr int QI = decltype(qi_)::value;
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
     if constexpr ((QI & 1) == 0)
       dma16b_at<SLOT * R::STAGE + n * 1024>(d.rk, koff[n], 0u, ldsw);
     else
-      dma16b_at<SLOT * R::STAGE + R::TILE + n * 1024>(rvt, voff[n], d.sv, ldsw);
+      dma16b_at<SLOT * R::STAGE + R::TILE + n * 1024>(d.rv, koff[n], 0u, ldsw);
   };
 
   f32x16 acc[MB];
@@ -197,15 +204,16 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
     constexpr bool DS = decltype(do_s)::value;
     constexpr bool DP = decltype(do_pv)::value;
     constexpr int SK = POS;                     // K of tile j
-    constexpr int SV = (POS + 3) % 4;           // V^T of tile j-1
+    constexpr int SV = (POS + 3) % 4;           // V of tile j-1
     constexpr int SD = (POS + 2) % 4;           // DMA target: tile j+2
     const char* lds = smem;
     auto kfrag = [&](int i) __attribute__((always_inline)) {   // pair i: key block i & 1, d-chunk i >> 1
       return *(const bf16x8*)(lds + kb[i >> 1] + SK * R::STAGE + (i & 1) * 32 * RB);
     };
-    static_assert(NP / MB == KCH, "one key chunk per MB pairs");
+    static_assert(NP / MB == BC / 16, "one key chunk per MB pairs");
     auto vfrag = [&](int i) __attribute__((always_inline)) {   // pair i: d-block i % MB, key chunk i / MB
-      return *(const bf16x8*)(lds + vb[i / MB] + SV * R::STAGE + (i % MB) * 32 * (2 * BC));
+      const char* p = lds + SV * R::STAGE + (i / MB) * 16 * RB;
+      return cat4(lds_read_tr((const bf16*)(p + vb[i % MB][0])), lds_read_tr((const bf16*)(p + vb[i % MB][1])));
     };
     Dma d;
     if constexpr (DS) d = dma_for(j + 2);
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   if (j + 1 < ntiles) full(I2{}, j + 1);
   if (j + 2 < ntiles) full(I3{}, j + 2);
   if (ntiles > 0) {
-    // P V of the last tile (its V^T sits in slot (ntiles - 1) mod 4); no
+    // P V of the last tile (its V sits in slot (ntiles - 1) mod 4); no
     // barrier is needed since no DMA writes that slot any more
     if (phase_b) softmax(ntiles - 1);
     switch (ntiles & 3) {
@@ -566,19 +574,10 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
 }
 
 template <int D>
-hipError_t launch_prefill_d(const FwdArgs& a, bf16* vt, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  if (a.skp > 0) {
-    timing_begin(s, "transpose_v");
-    hipLaunchKernelGGL((transpose_rows_kernel<D>), dim3(a.skp / BC, a.Hkv, a.B), dim3(256), 0, s, a.v, vt,
-                       a.Hkv, a.Sk, a.skp);
-    e = hipGetLastError();
-    timing_end(s);
-    if (e != hipSuccess) return e;
-  }
+hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
   timing_begin(s, "fwd_prefill_bf16");
   hipLaunchKernelGGL((fwd_prefill_kernel<D>), dim3(a.total_wgs), dim3(512), 0, s, a);
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   timing_end(s);
   return e;
 }
@@ -612,7 +611,6 @@ FwdArgs base_args(const Problem& p, const void* q, const void* k, const void* v,
   a.Sk = p.Sk;
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
-  a.skp = ((p.Sk + BC - 1) / BC) * BC;
   a.c = p.scale * kLog2e;
   return a;
 }
@@ -627,8 +625,7 @@ PrefillPlan plan_prefill(const Problem& p) {
   pl.rows_per_wg = 8 * 32 / pl.hw;
   pl.n_ptiles = (p.Sq + pl.rows_per_wg - 1) / pl.rows_per_wg;
   pl.total_wgs = p.B * p.Hkv * pl.n_hgroups * pl.n_ptiles;
-  const size_t skp = (size_t)((p.Sk + BC - 1) / BC) * BC;
-  pl.ws_bytes = (size_t)p.B * p.Hkv * p.d * skp * 2;
+  pl.ws_bytes = 0;
   return pl;
 }
 
@@ -660,9 +657,9 @@ hipError_t launch_fwd_prefill_bf16(const Problem& p, const PrefillPlan& pl, cons
   a.rows_per_wg = pl.rows_per_wg;
   a.n_ptiles = pl.n_ptiles;
   a.total_wgs = pl.total_wgs;
-  a.vt = (const bf16*)ws;
+  (void)ws;
   if (a.total_wgs == 0) return hipSuccess;
-  return p.d == 64 ? launch_prefill_d<64>(a, (bf16*)ws, s) : launch_prefill_d<128>(a, (bf16*)ws, s);
+  return p.d == 64 ? launch_prefill_d<64>(a, s) : launch_prefill_d<128>(a, s);
 }
 
 hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& sp, const void* q, const void* k,

@@ -28,7 +28,7 @@ struct PrefillPlan {
   int rows_per_wg;  // query positions per workgroup
   int n_ptiles;     // ceil(Sq / rows_per_wg)
   int total_wgs;
-  size_t ws_bytes;  // workspace for the transposed copy of V
+  size_t ws_bytes;  // 0: K and V tiles are read in place
 };
 PrefillPlan plan_prefill(const Problem& p);
 hipError_t launch_fwd_prefill_bf16(const Problem& p, const PrefillPlan& plan, const void* q,

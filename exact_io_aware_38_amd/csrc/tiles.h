@@ -21,9 +21,12 @@ typedef __attribute__((address_space(1))) void glb_void;
 // otherwise make every later LDS read wait for all outstanding DMA (it cannot
 // tell the ring stages apart), which serialises the prefetch; the kernels wait
 // for their DMA explicitly (s_waitcnt vmcnt + s_barrier) before reading a stage.
+// On this chip generation an LDS DMA instruction must not read M0 in the cycle
+// right after a scalar write to it, so every helper puts one s_nop between
+// the two (the compiler's hazard pass does not look inside inline assembly).
 __device__ __forceinline__ void dma16(const void* g, lds_void* base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(m0), "v"(g)
                : "memory", "m0");
@@ -41,14 +44,14 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // offset), which keeps the per-lane address arithmetic to 32 bits.
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, lds_void* base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(uniform_ptr(sbase))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, lds_void* base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(uniform_ptr(sbase))
                : "memory", "m0");
@@ -72,7 +75,7 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t num_byte
 // base + 16 * lane.
 __device__ __forceinline__ void dma16b(u32x4 rsrc, uint32_t voff, lds_void* base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(m0), "v"(voff), "s"(rsrc)
                : "memory", "m0");
@@ -84,14 +87,14 @@ __device__ __forceinline__ void dma16b(u32x4 rsrc, uint32_t voff, lds_void* base
 // the buffer size).
 template <uint32_t OFF>
 __device__ __forceinline__ void dma16b_at(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF)
                : "memory", "m0", "scc");
 }
 template <uint32_t OFF>
 __device__ __forceinline__ void dma4b_at(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dword %1, %2, %3 offen lds"
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF)
                : "memory", "m0", "scc");

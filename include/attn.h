@@ -70,10 +70,10 @@ enum attn_status {
 enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
 
 /* Bytes of device workspace attn_fwd needs for these arguments (0 if none).
- * ATTN_BF16 prefill keeps a transposed copy of V there (B*Hkv*d*Sk' bf16,
- * Sk' = Sk rounded up to 64); the split-key decode path (Hq/Hkv * Sq <= 32,
- * e.g. one query row) keeps per-split partial results there. ATTN_F32 needs
- * none. Returns 0 for invalid arguments too; the call then reports the error. */
+ * Only the ATTN_BF16 split-key decode path (Hq/Hkv * Sq <= 32, e.g. one
+ * query row) needs any: it keeps per-split partial results there. The bf16
+ * prefill and ATTN_F32 read their inputs in place and need none. Returns 0
+ * for invalid arguments too; the call then reports the error. */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                 int causal, int dtype);
 

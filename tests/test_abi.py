@@ -62,7 +62,7 @@ def _bwd(**over):
     ({"Hq": 6, "Hkv": 4}, -3), ({"d": 96}, -4), ({"d": 256}, -4), ({"dtype": 7}, -5),
     ({"causal": 3}, -6), ({"causal": -1}, -6), ({"scale": 0.0}, -9), ({"scale": -1.0}, -9),
     ({"scale": float("nan")}, -9), ({"scale": float("inf")}, -9),
-    # decode shape needs a workspace for the per-split partials, prefill one for V^T
+    # the decode-shaped calls (here Hq/Hkv * Sq <= 32) need a workspace for the per-split partials
     ({"Sq": 1, "Sk": 4096}, -7),
     ({"ws": FAKE, "ws_bytes": 16}, -7),
 ])
@@ -82,9 +82,9 @@ def test_bwd_validation(over, code):
 
 
 def test_workspace_queries():
-    # bf16 prefill keeps a transposed copy of V; decode (4 query rows per KV head) the split partials
-    assert attn.fwd_workspace_bytes(2, 32, 32, 8192, 8192, 128, 1, attn.ATTN_BF16) == 2 * 32 * 128 * 8192 * 2
-    assert attn.fwd_workspace_bytes(1, 4, 2, 100, 70, 64, 0, attn.ATTN_BF16) == 1 * 2 * 64 * 128 * 2
+    # bf16 prefill reads K and V in place; decode (4 query rows per KV head) keeps the split partials
+    assert attn.fwd_workspace_bytes(2, 32, 32, 8192, 8192, 128, 1, attn.ATTN_BF16) == 0
+    assert attn.fwd_workspace_bytes(1, 4, 2, 100, 70, 64, 0, attn.ATTN_BF16) == 0
     n = attn.fwd_workspace_bytes(16, 32, 8, 1, 32768, 128, 0, attn.ATTN_BF16)
     assert n >= 16 * 32 * 129 * 4
     assert attn.fwd_workspace_bytes(1, 1, 1, 1, 100, 64, 0, attn.ATTN_F32) == 0
