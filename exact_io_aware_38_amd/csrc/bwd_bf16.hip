@@ -13,25 +13,25 @@
 //  1. bwd_pre:   D_i = dO_i . O_i and lse2_i = lse_i * log2(e) (+inf for rows
 //                that see no key and for padding rows, which makes every
 //                rebuilt probability 0), packed per 32 rows;
-//  2. transpose_rows (x3): Q^T, dO^T and K^T copies whose sequence index is
-//                permuted inside groups of 16, so that every MFMA operand of
-//                the two main kernels is one 16-byte LDS read;
+//  2. transpose_rows: a K^T copy whose sequence index is permuted inside
+//                groups of 16, so that every MFMA operand of the dQ pass is
+//                one 16-byte LDS read;
 //  3. bwd_dkdv:  one workgroup per (KV head, 128-key tile); loops over the
 //                query heads that share the KV head and over 32-row query
 //                tiles, accumulating dK^T and dV^T in registers (no atomics);
-//  4. bwd_dq:    one workgroup per (query head, 128-row tile); loops over
+//  4. bwd_dq:    one workgroup per (query head, 256-row tile); loops over
 //                32-key tiles, accumulating dQ^T in registers.
 // The dK/dV and dQ passes both rebuild S and dP, which costs two GEMMs more
 // than a single pass with atomic dQ but keeps the result deterministic.
 //
-// Mapping to CDNA4: the accumulators (dK^T and dV^T: 128 registers per lane
-// at d = 128) plus the resident K/V fragments leave room for one wavefront per
-// SIMD only, so the overlap of matrix and vector work comes from inside each
-// wavefront: step j of the main loop interleaves, MFMA by MFMA, the score and
-// dP products of tile j+1, the gradient products of tile j-1 and the
-// elementwise work (P, dS) of tile j. Tiles arrive by LDS DMA three steps
-// ahead of their first use, in rings sized so that no slot is rewritten while
-// any wavefront still reads it.
+// Mapping to CDNA4: in the dK/dV pass the two wavefronts that share a SIMD
+// split each tile's work (scores and elementwise terms on one, the gradient
+// products on the other), so one's vector work runs under the other's MFMAs.
+// The dQ pass keeps one wavefront per SIMD, whose step j interleaves, MFMA by
+// MFMA, the score and dP products of tile j+1, the dQ products of tile j-1
+// and the elementwise work (P, dS) of tile j. Tiles arrive by LDS DMA ahead
+// of their first use, in rings sized so that no slot is rewritten while any
+// wavefront still reads it.
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -79,8 +79,6 @@ struct BwdArgs {
   bf16* dk;
   bf16* dv;
   float* ld;      // [B, Hq, sqp / 32][64]: lse2 of 32 rows, then D of the same rows
-  bf16* qt;       // [B, Hq, D, sqp]
-  bf16* dot;      // [B, Hq, D, sqp]
   bf16* kt;       // [B, Hkv, D, skp]
   int B, Hq, Hkv, Sq, Sk, g, causal;
   int sqp, skp;   // Sq, Sk rounded up to 64
@@ -159,35 +157,49 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV. Wavefront w owns keys k0 + 32w .. +31 as MFMA columns: S = Q K^T and
-// dP = dO V^T (rows = 32 queries) take K and V from registers; dV^T += dO^T P
-// and dK^T += Q^T dS (rows = d) take P and dS straight from the score
-// accumulators, which already have the B-operand layout.
+// dK, dV. A workgroup of 8 wavefronts owns 128 keys as four 32-key blocks;
+// the two wavefronts that share a SIMD (w and w + 4) share block w mod 4,
+// whose keys are their MFMA columns, and split the work of each 32-row query
+// tile between them:
+//  * the score wavefront (w < 4) computes S = Q K^T and dP = dO V^T (rows =
+//    queries) with K and V held in registers, then P = 2^(S c - lse2) and
+//    dS = P (dP - D), and hands the bf16 fragments of P and dS to its partner
+//    through LDS, one lane to the same lane;
+//  * the gradient wavefront (w >= 4) accumulates dV^T += dO^T P and
+//    dK^T += Q^T dS (rows = d) one step later, reading dO^T and Q^T with
+//    transposing LDS reads of the row-major tiles the score wavefront used,
+//    and issues all the tile DMA.
+// The score wavefront raises its issue priority for its MFMAs, so that its
+// partner's gradient MFMAs fill the matrix pipe while it does the vector work.
 //
-// LDS rings (4 slots each, so that a step's slot offsets are compile-time
-// constants once the loop is unrolled by 4): [Q | dO] row tiles of tile t are
-// loaded in step t-3 and read in step t-1, [Q^T | dO^T] in step t-2 and read
-// in step t+1, lse2/D in step t-3 and read in step t.
+// LDS: a 4-slot ring of [Q | dO] row tiles (tile t loaded in step t-2, read
+// in steps t and t+1) with its lse2/D blocks, and a 2-slot exchange buffer of
+// P and dS fragments (written in step t, read in step t+1).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
-  constexpr int NOPS = 2 * DC;                  // MFMAs per product group per step (= 4 * MB)
   constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int TB = BT * D * 2;                // bytes of a 32-row tile, row-major or transposed
-  constexpr int INSTR = TB / 4096;              // DMA instructions per wavefront per tensor
-  constexpr int NDMA = 4 * INSTR + 1;           // ... per step: Q, dO, Q^T, dO^T, lse2/D
+  constexpr int RB = 2 * D;                     // bytes per row
+  constexpr int TB = BT * RB;                   // bytes of a 32-row tile
   constexpr int RING = 4;
-  constexpr int T_OFF = RING * 2 * TB;
-  constexpr int L_OFF = 2 * T_OFF;
-  constexpr int LB = 2 * BT * 4;                // bytes of lse2/D per tile
-  static_assert(NOPS >= NDMA, "one DMA per step at most");
-  __shared__ __attribute__((aligned(1024))) char smem[L_OFF + RING * LB];
+  constexpr int SLOT = 2 * TB;                  // [Q | dO]
+  constexpr int LB = 2 * BT * 4;                // lse2/D of a tile
+  constexpr int L_OFF = RING * SLOT;
+  constexpr int X_OFF = L_OFF + RING * LB;
+  constexpr int XB = 64 * 64;                   // exchange bytes per key block: 64 lanes x (P, dS)
+  constexpr int XSLOT = 4 * XB;
+  constexpr int INSTR = TB / 4096;              // DMA instructions per gradient wavefront per tensor
+  constexpr int NDMA = 2 * INSTR + 1;           // ... per step: Q, dO, lse2/D
+  static_assert(INSTR >= 1, "four wavefronts share each tile's DMA");
+  __shared__ __attribute__((aligned(1024))) char smem[X_OFF + 2 * XSLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wid & 3;                       // key block, shared by the SIMD's two wavefronts
+  const bool grad = wid >= 4;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
@@ -197,74 +209,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int hkv = bh % a.Hkv;
   const int b = bh / a.Hkv;
   const int k0 = kt * KV_WG;
-  const int kw0 = k0 + 32 * wid;
-  const int key = kw0 + l32;
+  const int key = k0 + 32 * kb + l32;
   const bool kvalid = key < a.Sk;
-
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (column = key)
-  bf16x8 kf[DC], vf[DC];
-  {
-    const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.Sk + (kvalid ? key : 0)) * D;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (kvalid) {
-        kf[dc] = *(const bf16x8*)(a.k + kvrow + 16 * dc + 8 * hi);
-        vf[dc] = *(const bf16x8*)(a.v + kvrow + 16 * dc + 8 * hi);
-      } else {
-        kf[dc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        vf[dc] = kf[dc];
-      }
-    }
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      kf[dc] = settle(kf[dc]);
-      vf[dc] = settle(vf[dc]);
-    }
-  }
 
   const int n_qt = (a.Sq + BT - 1) / BT;
   const int qt_lo = a.causal ? min(n_qt, max(0, k0 - off) / BT) : 0;
   const int per_head = n_qt - qt_lo;
   const int n = a.g * per_head;                 // pipeline tiles: (query head, 32-row tile)
 
-  // Per-lane LDS read offsets; ring slots and the constant parts of each
-  // fragment's address become immediate offsets of the reads.
-  uint32_t rb[DC], tb[2];
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * (2 * D) + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
-#pragma unroll
-  for (int qc = 0; qc < 2; ++qc) tb[qc] = T_OFF + l32 * 64 + (((2 * qc + hi) ^ tr_swizzle(l32)) << 4);
-  const uint32_t lb = L_OFF + 16 * hi;
-
-  // Per-lane DMA offsets of instruction i: LDS chunk P = (wid*INSTR + i)*64 +
-  // lane of a tile; row-major tile: row P / CPR, physical chunk P % CPR;
-  // transposed tile: row P / 4, physical chunk P % 4; each lane loads the
-  // logical chunk (physical ^ swizzle(row)).
-  uint32_t roff[INSTR], toff[INSTR];
-#pragma unroll
-  for (int i = 0; i < INSTR; ++i) {
-    const int P = (wid * INSTR + i) * 64 + lane;
-    const int rr = P / CPR;
-    roff[i] = rr * (2 * D) + (((P % CPR) ^ chunk_swizzle<D>(rr)) << 4);
-    const int tr = P / 4;
-    toff[i] = (uint32_t)(tr * a.sqp + ((P & 3) ^ tr_swizzle(tr)) * 8) * 2;
-  }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;           // M0 = lds0 (+ wavefront part) + offset
-  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + wid * INSTR * 1024);
-
   // Tile sequence: for each query head of the group, the 32-row tiles from
   // the last one down to the first one that sees a key of this workgroup.
   // Walking down keeps every workgroup of a head on the same tile at the same
   // time (they all start at the last tile), so each tile is fetched into L2
   // once and then served to all of them.
-  // Window over the sequence (query head hq, first row q0): entry k is tile
-  // j+k at the start of step j. Past the last tile the coordinates stay at the
-  // last one: those DMAs reload it into slots nobody reads, which keeps the
-  // per-step DMA count uniform.
-  int whq[4], wq0[4];
-  int idx3 = 2;
-  whq[1] = hkv * a.g;
-  wq0[1] = (n_qt - 1) * BT;
   auto advance = [&](int& hq, int& q0) __attribute__((always_inline)) {
     q0 -= BT;
     if (q0 < qt_lo * BT) {
@@ -272,219 +229,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       ++hq;
     }
   };
-  whq[2] = whq[1];
-  wq0[2] = wq0[1];
-  if (n > 1) advance(whq[2], wq0[2]);
-  whq[3] = whq[2];
-  wq0[3] = wq0[2];
-  if (n > 2) advance(whq[3], wq0[3]);
-  whq[0] = whq[1];
-  wq0[0] = wq0[1];
-  auto shift = [&]() __attribute__((always_inline)) {
-    whq[0] = whq[1]; wq0[0] = wq0[1];
-    whq[1] = whq[2]; wq0[1] = wq0[2];
-    whq[2] = whq[3]; wq0[2] = wq0[3];
-    if (idx3 < n - 1) advance(whq[3], wq0[3]);
-    ++idx3;
-  };
-
-  // Buffer descriptors of the heads the two DMA streams read: rows (Q, dO)
-  // and lse2/D of the tile at the window's last entry (tile j+3), transposed
-  // tiles of the entry before it (tile j+2). Rebuilt only when the head
-  // changes; within a head a tile is a byte offset (rows past Sq are out of
-  // the row buffers' range and read zeros).
-  u32x4 rq, rd, rl, rtq, rtd;
-  int h3 = -1, h2 = -1;
-  auto refresh = [&]() __attribute__((always_inline)) {
-    if (whq[3] != h3) {
-      h3 = whq[3];
-      const size_t h = (size_t)b * a.Hq + h3;
-      rq = buffer_rsrc(a.q + h * a.Sq * D, (uint32_t)a.Sq * (2 * D));
-      rd = buffer_rsrc(a.dout + h * a.Sq * D, (uint32_t)a.Sq * (2 * D));
-      rl = buffer_rsrc(a.ld + h * (a.sqp / BT) * (2 * BT), (uint32_t)a.sqp * 8);
-    }
-    if (whq[2] != h2) {
-      h2 = whq[2];
-      const size_t h = (size_t)b * a.Hq + h2;
-      rtq = buffer_rsrc(a.qt + h * D * a.sqp, (uint32_t)a.sqp * (2 * D));
-      rtd = buffer_rsrc(a.dot + h * D * a.sqp, (uint32_t)a.sqp * (2 * D));
-    }
-  };
-  // Offsets of one step's DMA: row tiles of tile j+3 (per lane), transposed
-  // tiles of tile j+2 and lse2/D of tile j+3 (scalar).
-  struct DmaOff {
-    uint32_t vr[INSTR];
-    uint32_t st, sl;
-  };
-  auto dma_offsets = [&](int q03, int q02) __attribute__((always_inline)) {
-    DmaOff o;
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) o.vr[i] = roff[i] + (uint32_t)q03 * (2 * D);
-    o.st = (uint32_t)q02 * 2;
-    o.sl = (uint32_t)(q03 / BT) * (2 * BT * 4);
-    return o;
-  };
-  // DMA instruction QI (0 .. NDMA-1) into row slot SQ, transposed slot STD,
-  // lse slot SLD
-  auto dma_one = [&](auto sq_, auto std_, auto sld_, auto qi_, const DmaOff& o) __attribute__((always_inline)) {
-    constexpr int SQ = decltype(sq_)::value, STD = decltype(std_)::value, SLD = decltype(sld_)::value;
-    constexpr int QI = decltype(qi_)::value;
-    constexpr int i = QI % INSTR;
-    constexpr uint32_t part = i * 1024;
-    if constexpr (QI < INSTR)
-      dma16b_at<SQ * 2 * TB + part>(rq, o.vr[i], 0u, ldsw);
-    else if constexpr (QI < 2 * INSTR)
-      dma16b_at<SQ * 2 * TB + TB + part>(rd, o.vr[i], 0u, ldsw);
-    else if constexpr (QI < 3 * INSTR)
-      dma16b_at<T_OFF + STD * 2 * TB + part>(rtq, toff[i], o.st, ldsw);
-    else if constexpr (QI < 4 * INSTR)
-      dma16b_at<T_OFF + STD * 2 * TB + TB + part>(rtd, toff[i], o.st, ldsw);
-    else                                        // every wavefront loads the same 256 bytes
-      dma4b_at<L_OFF + SLD * LB>(rl, (uint32_t)lane * 4, o.sl, lds0);
-  };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C3 = std::integral_constant<int, 3>;
-
-  f32x16 dkt[MB], dvt[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    dkt[mb] = f32x16{};
-    dvt[mb] = f32x16{};
-  }
-  f32x16 s_[2], dp_[2];                         // scores and dP of two tiles in flight
-  bf16x8 pf[2][2], dsf[2][2];                   // [tile parity][16-query chunk]
-
-  // One step j (slot position POS = j mod 4): score group = S, dP of tile j+1
-  // (op k: S for even k, dP for odd, d-chunk k / 2); gradient group = dV^T,
-  // dK^T of tile j-1 (op k: chain k % 2MB, 16-query chunk k / 2MB); elementwise
-  // = P, dS of tile j; and the DMA of tiles j+2 / j+3.
-  auto step = [&](auto pos_, auto g1, auto g2, auto ew, auto mask_) __attribute__((always_inline)) {
-    constexpr int POS = decltype(pos_)::value;
-    constexpr int P = POS & 1;                  // parity of tile j
-    constexpr bool G1 = decltype(g1)::value;
-    constexpr bool G2 = decltype(g2)::value;
-    constexpr bool EW = decltype(ew)::value;
-    constexpr bool MASK = decltype(mask_)::value;
-    constexpr int SQ = (POS + 1) % RING;        // rows of tile j+1
-    constexpr int ST = (POS + 3) % RING;        // transposed tiles of tile j-1
-    constexpr int SL = POS;                     // lse2/D of tile j
-    const char* lds = smem;
-    auto g1_frag = [&](int k) __attribute__((always_inline)) {
-      return *(const bf16x8*)(lds + rb[k >> 1] + SQ * 2 * TB + (k & 1) * TB);
-    };
-    auto g2_frag = [&](int k) __attribute__((always_inline)) {
-      const int ch = k % (2 * MB);
-      return *(const bf16x8*)(lds + tb[k / (2 * MB)] + ST * 2 * TB + (ch < MB ? TB : 0) + (ch % MB) * 32 * 64);
-    };
-    DmaOff o;
-    if constexpr (G1) {
-      refresh();
-      o = dma_offsets(wq0[3], wq0[2]);
-    }
-    const int q0 = wq0[0];
-    f32x4 l2v[4], dlv[4];
-    if constexpr (EW) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        l2v[i4] = *(const f32x4*)(lds + lb + SL * LB + 32 * i4);
-        dlv[i4] = *(const f32x4*)(lds + lb + SL * LB + 4 * BT + 32 * i4);
-      }
-    }
-    bf16x8 f1[3], f2[3];
-    if constexpr (G1) {
-      f1[0] = g1_frag(0);
-      f1[1] = g1_frag(1);
-    }
-    if constexpr (G2) {
-      f2[0] = g2_frag(0);
-      f2[1] = g2_frag(1);
-    }
-    float ex[8], pt[8], dt[8];
-    static_for<NOPS>([&](auto ic) __attribute__((always_inline)) {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (i + 2 < NOPS) {
-        if constexpr (G1) f1[(i + 2) % 3] = g1_frag(i + 2);
-        if constexpr (G2) f2[(i + 2) % 3] = g2_frag(i + 2);
-      }
-      __builtin_amdgcn_sched_barrier(0);        // keep the reads two MFMAs ahead of their use
-      if constexpr (G1) {
-        if constexpr (i < 2) {
-          if constexpr (i & 1)
-            mfma_first(dp_[P ^ 1], f1[i % 3], vf[i >> 1]);
-          else
-            mfma_first(s_[P ^ 1], f1[i % 3], kf[i >> 1]);
-        } else {
-          if constexpr (i & 1)
-            mfma_next(dp_[P ^ 1], f1[i % 3], vf[i >> 1]);
-          else
-            mfma_next(s_[P ^ 1], f1[i % 3], kf[i >> 1]);
-        }
-        if constexpr (i == NOPS - 1) score_settle(s_[P ^ 1], dp_[P ^ 1]);
-      }
-      if constexpr (G2) {
-        const int ch = i % (2 * MB);
-        const int qc = i / (2 * MB);
-        if (ch < MB)
-          dvt[ch] = mfma32(f2[i % 3], pf[P ^ 1][qc], dvt[ch]);
-        else
-          dkt[ch - MB] = mfma32(f2[i % 3], dsf[P ^ 1][qc], dkt[ch - MB]);
-      }
-      if constexpr (EW) {
-        // The 16 score registers in NG groups, each through three stages in
-        // consecutive MFMA pairs: x = s c - lse2 (pair g + 1), p = 2^x with the
-        // mask (pair g + 2), dS = p (dP - D) (pair g + 3). A pair then carries
-        // the stages of three different groups, whose instructions do not
-        // depend on each other, so in-order issue does not stall on the
-        // latency of a single chain. The stages run in reverse order inside a
-        // pair, so a later group's stage never overwrites a value an earlier
-        // group still has to consume in the same pair.
-        constexpr int NG = NOPS >= 11 ? 8 : 4;
-        constexpr int GS = 16 / NG;
-        if constexpr (i >= 3 && i - 3 < NG) {       // stage 3 of group i - 3
-          constexpr int g = i - 3;
-#pragma unroll
-          for (int e = 0; e < GS; ++e) {
-            const int v = g * GS + e;
-            dt[v & 7] = pt[v & 7] * (dp_[P][v] - dlv[v >> 2][v & 3]);
-            pin(dt[v & 7]);
-          }
-          if constexpr ((g * GS + GS) % 8 == 0) {
-            constexpr int h = (g * GS) / 8;
-            pf[P][h] = to_bf16x8(pt[0], pt[1], pt[2], pt[3], pt[4], pt[5], pt[6], pt[7]);
-            dsf[P][h] = to_bf16x8(dt[0], dt[1], dt[2], dt[3], dt[4], dt[5], dt[6], dt[7]);
-            pin(pf[P][h]);
-            pin(dsf[P][h]);
-          }
-        }
-        if constexpr (i >= 2 && i - 2 < NG) {       // stage 2 of group i - 2
-          constexpr int g = i - 2;
-#pragma unroll
-          for (int e = 0; e < GS; ++e) {
-            const int v = g * GS + e;
-            float p = fast_exp2(ex[v & 7]);
-            if constexpr (MASK) {
-              if (key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) p = 0.f;
-            }
-            pt[v & 7] = p;
-            pin(pt[v & 7]);
-          }
-        }
-        if constexpr (i >= 1 && i - 1 < NG) {       // stage 1 of group i - 1
-          constexpr int g = i - 1;
-#pragma unroll
-          for (int e = 0; e < GS; ++e) {
-            const int v = g * GS + e;
-            ex[v & 7] = __builtin_fmaf(s_[P][v], a.c, -l2v[v >> 2][v & 3]);
-            pin(ex[v & 7]);
-          }
-        }
-      }
-      if constexpr (G1 && i < NDMA)
-        dma_one(std::integral_constant<int, (POS + 3) % RING>{}, std::integral_constant<int, (POS + 2) % RING>{},
-                std::integral_constant<int, (POS + 3) % RING>{}, ic, o);
-    });
-    if constexpr (G1) shift();
+  // step j: the tiles j (score wavefronts) and j - 1 (gradient wavefronts)
+  // have landed for every wavefront (the gradient wavefronts wait for their
+  // DMA, the barrier makes it visible to all), the exchange slot of tile j - 1
+  // is complete, and every wavefront is done with step j - 1.
+  auto sync = [&]() __attribute__((always_inline)) {
+    if (grad)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -492,100 +245,300 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  using M_ = std::integral_constant<bool, CAUSAL>;
-  // Causal masking is needed only where some key of the workgroup lies above
-  // some query of the tile. The walk runs down to the diagonal, so with one
-  // query head per KV head these are the last tiles: the first n_um steps run
-  // unmasked, the rest masked (the loops switch at a multiple of 4 so slot
-  // positions stay compile-time). With several query heads per KV head every
-  // step is masked. Without a causal mask nothing needs masking: rows past Sq
-  // have lse2 = +inf, so their P and dS are 0.
-  int n_um = n;
-  if (CAUSAL) {
-    n_um = 0;
-    if (a.g == 1) {
-      // tile qt is unmasked iff its first row sees the workgroup's last key
-      const int x = k0 + KV_WG - 1 - off;
-      const int lowest_unmasked = x <= 0 ? 0 : (x + BT - 1) / BT;
-      n_um = min(n, max(0, n_qt - max(lowest_unmasked, qt_lo)));
-    }
-  }
-  auto full = [&](auto pos_, auto g2, auto mask_) __attribute__((always_inline)) {
-    step(pos_, T_{}, g2, T_{}, mask_);
-  };
-  // step j: tile j+1 has landed for every wavefront (each waits for its own
-  // DMA, the barrier for all of them), and every wavefront is done with step j-1
-  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
+  const char* lds = smem;
 
-  if (n > 0) {
-    // DMA groups of steps -3 and -2 (the transposed tiles of "tile -1" are a
-    // dummy copy of tile 0), then the scores of tile 0 as step -1
+  if (!grad) {
+    // ---------------- score wavefront ----------------
+    // K and V fragments: B operands of S = Q K^T and dP = dO V^T (column = key)
+    bf16x8 kf[DC], vf[DC];
     {
-      // the window's entries 1 and 2 hold tiles 0 and 1 here; the heads of
-      // tiles 0..2 are loaded into the descriptors by hand
-      const int s3 = whq[3], s2 = whq[2];
-      whq[3] = whq[1];
-      whq[2] = whq[1];
-      refresh();
-      const DmaOff o3 = dma_offsets(wq0[1], wq0[1]);
-      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C0{}, C3{}, C0{}, qi, o3); });
-      whq[3] = s2;
-      refresh();
-      const DmaOff o2 = dma_offsets(wq0[2], wq0[1]);
-      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C1{}, C0{}, C1{}, qi, o2); });
-      whq[3] = s3;
-      whq[2] = s2;
+      const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.Sk + (kvalid ? key : 0)) * D;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        if (kvalid) {
+          kf[dc] = *(const bf16x8*)(a.k + kvrow + 16 * dc + 8 * hi);
+          vf[dc] = *(const bf16x8*)(a.v + kvrow + 16 * dc + 8 * hi);
+        } else {
+          kf[dc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+          vf[dc] = kf[dc];
+        }
+      }
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        kf[dc] = settle(kf[dc]);
+        vf[dc] = settle(vf[dc]);
+      }
     }
-    sync();
-    step(I3{}, T_{}, F_{}, F_{}, F_{});         // j = -1
-    sync();
-    if (n_um > 0)                               // j = 0: no gradients yet
-      full(I0{}, F_{}, F_{});
-    else
-      full(I0{}, F_{}, M_{});
+    // A-operand fragments of S and dP: row l32 (query), logical chunk 2 dc + hi
+    uint32_t rb[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+    const uint32_t lb = L_OFF + 16 * hi;
+    const uint32_t xw = X_OFF + kb * XB + lane * 16;
+    int hq = hkv * a.g, q0 = (n_qt - 1) * BT;
+
+    auto step = [&](auto pos_, auto mask_) __attribute__((always_inline)) {
+      constexpr int POS = decltype(pos_)::value;
+      constexpr bool MASK = decltype(mask_)::value;
+      const char* tile = lds + POS * SLOT;
+      auto frag = [&](int k) __attribute__((always_inline)) {   // op k: S (even) / dP (odd), d-chunk k / 2
+        return *(const bf16x8*)(tile + rb[k >> 1] + (k & 1) * TB);
+      };
+      f32x4 l2v[4], dlv[4];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        l2v[i4] = *(const f32x4*)(lds + lb + POS * LB + 32 * i4);
+        dlv[i4] = *(const f32x4*)(lds + lb + POS * LB + 4 * BT + 32 * i4);
+      }
+      f32x16 s, dp;
+      bf16x8 f[3];
+      f[0] = frag(0);
+      f[1] = frag(1);
+      __builtin_amdgcn_s_setprio(2);
+      static_for<2 * DC>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k + 2 < 2 * DC) f[(k + 2) % 3] = frag(k + 2);
+        __builtin_amdgcn_sched_barrier(0);      // keep the reads two MFMAs ahead of their use
+        if constexpr (k < 2) {
+          if constexpr (k & 1)
+            mfma_first(dp, f[k % 3], vf[k >> 1]);
+          else
+            mfma_first(s, f[k % 3], kf[k >> 1]);
+        } else {
+          if constexpr (k & 1)
+            mfma_next(dp, f[k % 3], vf[k >> 1]);
+          else
+            mfma_next(s, f[k % 3], kf[k >> 1]);
+        }
+      });
+      score_settle(s, dp);
+      __builtin_amdgcn_s_setprio(0);
+      // accumulator register v holds query q0 + 8 (v >> 2) + 4 hi + (v & 3)
+      float p[16], ds[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pv = fast_exp2(__builtin_fmaf(s[v], a.c, -l2v[v >> 2][v & 3]));
+        if constexpr (MASK) {
+          if (key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) pv = 0.f;
+        }
+        p[v] = pv;
+        ds[v] = pv * (dp[v] - dlv[v >> 2][v & 3]);
+      }
+      char* xs = smem + xw + (POS & 1) * XSLOT;
+      *(bf16x8*)(xs + 0 * 1024) = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      *(bf16x8*)(xs + 1 * 1024) = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      *(bf16x8*)(xs + 2 * 1024) = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      *(bf16x8*)(xs + 3 * 1024) = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+      advance(hq, q0);
+    };
+    using M_ = std::integral_constant<bool, CAUSAL>;
+    // Causal masking is needed only where some key of the workgroup lies
+    // above some query of the tile. The walk runs down to the diagonal, so
+    // with one query head per KV head these are the last tiles: the first
+    // n_um steps run unmasked, the rest masked (the loops switch at a multiple
+    // of 4 so slot positions stay compile-time). With several query heads per
+    // KV head every step is masked. Without a causal mask nothing needs
+    // masking: rows past Sq have lse2 = +inf, so their P and dS are 0.
+    int n_um = n;
+    if (CAUSAL) {
+      n_um = 0;
+      if (a.g == 1) {
+        // tile qt is unmasked iff its first row sees the workgroup's last key
+        const int x = k0 + KV_WG - 1 - off;
+        const int lowest_unmasked = x <= 0 ? 0 : (x + BT - 1) / BT;
+        n_um = min(n, max(0, n_qt - max(lowest_unmasked, qt_lo)));
+      }
+    }
+    int j = 0;
+    for (; j + 3 < n_um; j += 4) {
+      sync();
+      step(I0{}, F_{});
+      sync();
+      step(I1{}, F_{});
+      sync();
+      step(I2{}, F_{});
+      sync();
+      step(I3{}, F_{});
+    }
+    for (; j + 3 < n; j += 4) {
+      sync();
+      step(I0{}, M_{});
+      sync();
+      step(I1{}, M_{});
+      sync();
+      step(I2{}, M_{});
+      sync();
+      step(I3{}, M_{});
+    }
+    if (j < n) {
+      sync();
+      step(I0{}, M_{});
+    }
+    if (j + 1 < n) {
+      sync();
+      step(I1{}, M_{});
+    }
+    if (j + 2 < n) {
+      sync();
+      step(I2{}, M_{});
+    }
+    if (n > 0) sync();                          // the gradient wavefronts' step n
+    return;
   }
-  int j = 1;
-  for (; j + 3 < n_um; j += 4) {
-    sync();
-    full(I1{}, T_{}, F_{});
-    sync();
-    full(I2{}, T_{}, F_{});
-    sync();
-    full(I3{}, T_{}, F_{});
-    sync();
-    full(I0{}, T_{}, F_{});
+
+  // ---------------- gradient wavefront ----------------
+  // DMA geometry of instruction i: LDS chunk P = (kb*INSTR + i)*64 + lane of a
+  // tile, i.e. row P / CPR, physical chunk P % CPR, loading the logical chunk
+  // (physical ^ swizzle(row)); byte offsets relative to the tile's first row.
+  uint32_t roff[INSTR];
+#pragma unroll
+  for (int i = 0; i < INSTR; ++i) {
+    const int P = (kb * INSTR + i) * 64 + lane;
+    const int rr = P / CPR;
+    roff[i] = rr * RB + (((P % CPR) ^ chunk_swizzle<D>(rr)) << 4);
   }
-  for (; j + 3 < n; j += 4) {
-    sync();
-    full(I1{}, T_{}, M_{});
-    sync();
-    full(I2{}, T_{}, M_{});
-    sync();
-    full(I3{}, T_{}, M_{});
-    sync();
-    full(I0{}, T_{}, M_{});
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + kb * INSTR * 1024);
+  // DMA of the tiles in sequence order; past the last tile it reloads the last
+  // one into a slot nobody reads any more, which keeps the per-step DMA count
+  // uniform. Buffer descriptors are rebuilt only when the head changes; rows
+  // past Sq are out of the row buffers' range and read zeros.
+  int dhq = hkv * a.g, dq0 = (n_qt - 1) * BT, issued = 0, dh = -1;
+  u32x4 rq, rd, rl;
+  struct Dma {
+    uint32_t vr[INSTR];
+    uint32_t sl;
+  };
+  auto next_dma = [&]() __attribute__((always_inline)) {
+    if (dhq != dh) {
+      dh = dhq;
+      const size_t h = (size_t)b * a.Hq + dhq;
+      rq = buffer_rsrc(a.q + h * a.Sq * D, (uint32_t)a.Sq * RB);
+      rd = buffer_rsrc(a.dout + h * a.Sq * D, (uint32_t)a.Sq * RB);
+      rl = buffer_rsrc(a.ld + h * (a.sqp / BT) * (2 * BT), (uint32_t)a.sqp * 8);
+    }
+    Dma o;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) o.vr[i] = roff[i] + (uint32_t)dq0 * RB;
+    o.sl = (uint32_t)(dq0 / BT) * LB;
+    if (++issued < n) advance(dhq, dq0);
+    return o;
+  };
+  // DMA instruction QI (0 .. NDMA-1) of a tile into ring slot S
+  auto dma_one = [&](auto s_, auto qi_, const Dma& o) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_)::value;
+    constexpr int QI = decltype(qi_)::value;
+    constexpr int i = QI % INSTR;
+    if constexpr (QI < INSTR)
+      dma16b_at<S * SLOT + i * 1024>(rq, o.vr[i], 0u, ldsw);
+    else if constexpr (QI < 2 * INSTR)
+      dma16b_at<S * SLOT + TB + i * 1024>(rd, o.vr[i], 0u, ldsw);
+    else                                        // every gradient wavefront loads the same 256 bytes
+      dma4b_at<L_OFF + S * LB>(rl, (uint32_t)lane * 4, o.sl, lds0);
+  };
+  // Transposing reads: the A operand of dV^T += dO^T P for d-block mb and
+  // 16-query chunk qc is two 4-query reads at rows 16 qc + 4 hi + (L >> 2)
+  // (+8) and columns 32 mb + 16 dhalf + 4 (L & 3) of the dO tile (Q tile for
+  // dK^T); their query order is the register order of the P and dS fragments.
+  // The row swizzle does not change with qc, so qc is an immediate offset.
+  uint32_t vb[MB][2];
+  {
+    const int L = lane & 15, dhalf = (lane >> 4) & 1;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 4 * hi + (L >> 2) + 8 * h;
+        const int c = 32 * mb + 16 * dhalf + 4 * (L & 3);
+        vb[mb][h] = r * RB + (((c >> 3) ^ chunk_swizzle<D>(r)) << 4) + (c & 7) * 2;
+      }
   }
-  if (j < n) {
-    sync();
-    full(I1{}, T_{}, M_{});
+  const uint32_t xr = X_OFF + kb * XB + lane * 16;
+
+  f32x16 dkt[MB], dvt[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    dkt[mb] = f32x16{};
+    dvt[mb] = f32x16{};
   }
-  if (j + 1 < n) {
-    sync();
-    full(I2{}, T_{}, M_{});
-  }
-  if (j + 2 < n) {
-    sync();
-    full(I3{}, T_{}, M_{});
-  }
-  // gradients of the last tile: a step at position n mod 4 with only the gradient group
+  // step j at slot position POS = j mod 4: gradients of tile j - 1 (if G),
+  // DMA of tile j + 2
+  auto step = [&](auto pos_, auto g_) __attribute__((always_inline)) {
+    constexpr int POS = decltype(pos_)::value;
+    constexpr bool G = decltype(g_)::value;
+    constexpr int SG = (POS + 3) % RING;        // rows of tile j - 1
+    constexpr int SD = (POS + 2) % RING;        // DMA target: tile j + 2
+    const Dma o = next_dma();
+    if constexpr (!G) {
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(std::integral_constant<int, SD>{}, qi, o); });
+    } else {
+      const char* xs = lds + xr + ((POS + 1) & 1) * XSLOT;
+      bf16x8 pf[2], dsf[2];
+      pf[0] = *(const bf16x8*)(xs + 0 * 1024);
+      pf[1] = *(const bf16x8*)(xs + 1 * 1024);
+      dsf[0] = *(const bf16x8*)(xs + 2 * 1024);
+      dsf[1] = *(const bf16x8*)(xs + 3 * 1024);
+      const char* tile = lds + SG * SLOT;
+      // op k: chain k % 2MB (dV^T for < MB, dK^T above), query chunk k / 2MB
+      auto frag = [&](int k) __attribute__((always_inline)) {
+        const int ch = k % (2 * MB), qc = k / (2 * MB);
+        const char* t = tile + (ch < MB ? TB : 0) + qc * 16 * RB;
+        return cat4(lds_read_tr((const bf16*)(t + vb[ch % MB][0])), lds_read_tr((const bf16*)(t + vb[ch % MB][1])));
+      };
+      constexpr int NOPS = 4 * MB;
+      constexpr int EVERY = NOPS / NDMA;
+      bf16x8 f[3];
+      f[0] = frag(0);
+      f[1] = frag(1);
+      static_for<NOPS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k + 2 < NOPS) f[(k + 2) % 3] = frag(k + 2);
+        __builtin_amdgcn_sched_barrier(0);      // keep the reads two MFMAs ahead of their use
+        constexpr int ch = k % (2 * MB), qc = k / (2 * MB);
+        if constexpr (ch < MB)
+          dvt[ch] = mfma32(f[k % 3], pf[qc], dvt[ch]);
+        else
+          dkt[ch - MB] = mfma32(f[k % 3], dsf[qc], dkt[ch - MB]);
+        if constexpr (k % EVERY == EVERY - 1 && k / EVERY < NDMA)
+          dma_one(std::integral_constant<int, SD>{}, std::integral_constant<int, k / EVERY>{}, o);
+      });
+    }
+  };
   if (n > 0) {
-    switch (n & 3) {
-      case 0: step(I0{}, F_{}, T_{}, F_{}, F_{}); break;
-      case 1: step(I1{}, F_{}, T_{}, F_{}, F_{}); break;
-      case 2: step(I2{}, F_{}, T_{}, F_{}, F_{}); break;
-      default: step(I3{}, F_{}, T_{}, F_{}, F_{}); break;
+    {
+      const Dma o0 = next_dma();
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(I0{}, qi, o0); });
+      const Dma o1 = next_dma();
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(I1{}, qi, o1); });
+    }
+    sync();
+    step(I0{}, F_{});                           // j = 0: DMA only
+    int j = 1;
+    for (; j + 3 <= n; j += 4) {
+      sync();
+      step(I1{}, T_{});
+      sync();
+      step(I2{}, T_{});
+      sync();
+      step(I3{}, T_{});
+      sync();
+      step(I0{}, T_{});
+    }
+    if (j <= n) {
+      sync();
+      step(I1{}, T_{});
+    }
+    if (j + 1 <= n) {
+      sync();
+      step(I2{}, T_{});
+    }
+    if (j + 2 <= n) {
+      sync();
+      step(I3{}, T_{});
     }
   }
+  // no LDS DMA may still be in flight when the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!kvalid) return;
   const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.Sk + key) * D;
@@ -603,7 +556,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       *(bf16x4*)(a.dv + kvrow + 32 * mb + 8 * i4 + 4 * hi) = rv;
     }
 }
-
 // ---------------------------------------------------------------------------
 // dQ. Wavefront w owns queries p + 64w .. +63 as two blocks of 32 MFMA
 // columns: S^T = K Q^T and dP^T = V dO^T (rows = 32 keys) take Q and dO from
@@ -926,7 +878,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 }
 
 struct WsLayout {
-  size_t ld, qt, dot, kt, total;
+  size_t ld, kt, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -936,9 +888,7 @@ WsLayout ws_layout(const Problem& p) {
   const size_t skp = (size_t)((p.Sk + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
   WsLayout w{};
   w.ld = 0;
-  w.qt = align256((size_t)p.B * p.Hq * sqp * 2 * sizeof(float));
-  w.dot = w.qt + align256((size_t)p.B * p.Hq * p.d * sqp * 2);
-  w.kt = w.dot + align256((size_t)p.B * p.Hq * p.d * sqp * 2);
+  w.kt = align256((size_t)p.B * p.Hq * sqp * 2 * sizeof(float));
   w.total = w.kt + align256((size_t)p.B * p.Hkv * p.d * skp * 2);
   return w;
 }
@@ -954,14 +904,6 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
-    timing_begin(s, "bwd_transpose");
-    hipLaunchKernelGGL((transpose_rows_kernel<D>), dim3(a.sqp / TILE_ROWS, a.Hq, a.B), dim3(256), 0, s,
-                       a.q, a.qt, a.Hq, a.Sq, a.sqp);
-    hipLaunchKernelGGL((transpose_rows_kernel<D>), dim3(a.sqp / TILE_ROWS, a.Hq, a.B), dim3(256), 0, s,
-                       a.dout, a.dot, a.Hq, a.Sq, a.sqp);
-    e = hipGetLastError();
-    timing_end(s);
-    if (e != hipSuccess) return e;
   }
   if (a.skp > 0) {
     timing_begin(s, "bwd_transpose");
@@ -974,9 +916,9 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   if (a.total_kv > 0) {
     timing_begin(s, "bwd_dkdv");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(a.total_kv), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(a.total_kv), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(a.total_kv), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(a.total_kv), dim3(512), 0, s, a);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -993,8 +935,8 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   }
   if (log != nullptr && log_n > 0)
     snprintf(log, log_n,
-             "attn_bwd: bwd_pre<d=%d> grid=%zu; transpose_rows<d=%d> x3 (Q^T, dO^T, K^T); "
-             "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles); "
+             "attn_bwd: bwd_pre<d=%d> grid=%zu; transpose_rows<d=%d> (K^T); "
+             "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles, 8 wavefronts); "
              "bwd_dq<d=%d> grid=%d (256 rows x 32-key tiles)",
              D, (rows + RPB - 1) / RPB, D, D, a.total_kv, D, a.total_q);
   return hipSuccess;
@@ -1019,8 +961,6 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   a.dk = (bf16*)dk;
   a.dv = (bf16*)dv;
   a.ld = (float*)((char*)ws + w.ld);
-  a.qt = (bf16*)((char*)ws + w.qt);
-  a.dot = (bf16*)((char*)ws + w.dot);
   a.kt = (bf16*)((char*)ws + w.kt);
   a.B = p.B;
   a.Hq = p.Hq;
