@@ -172,9 +172,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // The score wavefront raises its issue priority for its MFMAs, so that its
 // partner's gradient MFMAs fill the matrix pipe while it does the vector work.
 //
-// LDS: a 4-slot ring of [Q | dO] row tiles (tile t loaded in step t-2, read
-// in steps t and t+1) with its lse2/D blocks, and a 2-slot exchange buffer of
-// P and dS fragments (written in step t, read in step t+1).
+// LDS: a 4-slot ring of [Q | dO] row tiles (tile t loaded at the start of
+// step t-1, read in steps t and t+1) with its lse2/D blocks, and a 2-slot
+// exchange buffer of P and dS fragments (written in step t, read in step t+1).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
@@ -230,12 +230,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   // step j: the tiles j (score wavefronts) and j - 1 (gradient wavefronts)
-  // have landed for every wavefront (the gradient wavefronts wait for their
-  // DMA, the barrier makes it visible to all), the exchange slot of tile j - 1
-  // is complete, and every wavefront is done with step j - 1.
+  // have landed for every wavefront (the gradient wavefronts wait for all
+  // their DMA, the barrier makes it visible to all), the exchange slot of
+  // tile j - 1 is complete, and every wavefront is done with step j - 1.
   auto sync = [&]() __attribute__((always_inline)) {
     if (grad)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
@@ -461,17 +461,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     dkt[mb] = f32x16{};
     dvt[mb] = f32x16{};
   }
-  // step j at slot position POS = j mod 4: gradients of tile j - 1 (if G),
-  // DMA of tile j + 2
+  // step j at slot position POS = j mod 4: DMA of tile j + 1, issued first
+  // so that it has the whole step to land, then the gradients of tile j - 1
+  // (if G)
   auto step = [&](auto pos_, auto g_) __attribute__((always_inline)) {
     constexpr int POS = decltype(pos_)::value;
     constexpr bool G = decltype(g_)::value;
     constexpr int SG = (POS + 3) % RING;        // rows of tile j - 1
-    constexpr int SD = (POS + 2) % RING;        // DMA target: tile j + 2
+    constexpr int SD = (POS + 1) % RING;        // DMA target: tile j + 1
     const Dma o = next_dma();
-    if constexpr (!G) {
-      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(std::integral_constant<int, SD>{}, qi, o); });
-    } else {
+    static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(std::integral_constant<int, SD>{}, qi, o); });
+    if constexpr (G) {
       const char* xs = lds + xr + ((POS + 1) & 1) * XSLOT;
       bf16x8 pf[2], dsf[2];
       pf[0] = *(const bf16x8*)(xs + 0 * 1024);
@@ -486,7 +486,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
         return cat4(lds_read_tr((const bf16*)(t + vb[ch % MB][0])), lds_read_tr((const bf16*)(t + vb[ch % MB][1])));
       };
       constexpr int NOPS = 4 * MB;
-      constexpr int EVERY = NOPS / NDMA;
       bf16x8 f[3];
       f[0] = frag(0);
       f[1] = frag(1);
@@ -499,8 +498,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
           dvt[ch] = mfma32(f[k % 3], pf[qc], dvt[ch]);
         else
           dkt[ch - MB] = mfma32(f[k % 3], dsf[qc], dkt[ch - MB]);
-        if constexpr (k % EVERY == EVERY - 1 && k / EVERY < NDMA)
-          dma_one(std::integral_constant<int, SD>{}, std::integral_constant<int, k / EVERY>{}, o);
       });
     }
   };
@@ -508,8 +505,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     {
       const Dma o0 = next_dma();
       static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(I0{}, qi, o0); });
-      const Dma o1 = next_dma();
-      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(I1{}, qi, o1); });
     }
     sync();
     step(I0{}, F_{});                           // j = 0: DMA only
