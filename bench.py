@@ -43,7 +43,6 @@ KERNEL_SOURCES = {
     "bwd_dkdv": ["bwd_bf16.hip", "common.h", "tiles.h"],
     "bwd_dq": ["bwd_bf16.hip", "common.h", "tiles.h"],
     "bwd_pre": ["bwd_bf16.hip"],
-    "transpose_rows": ["tiles.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {
@@ -52,7 +51,6 @@ KERNEL_SYMBOLS = {
     "bwd_dkdv": "bwd_dkdv_kernel<128",
     "bwd_dq": "bwd_dq_kernel<128",
     "bwd_pre": "bwd_pre_kernel<128>",
-    "transpose_rows": "transpose_rows_kernel<128>",
 }
 
 

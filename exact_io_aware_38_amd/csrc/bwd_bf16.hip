@@ -13,13 +13,10 @@
 //  1. bwd_pre:   D_i = dO_i . O_i and lse2_i = lse_i * log2(e) (+inf for rows
 //                that see no key and for padding rows, which makes every
 //                rebuilt probability 0), packed per 32 rows;
-//  2. transpose_rows: a K^T copy whose sequence index is permuted inside
-//                groups of 16, so that every MFMA operand of the dQ pass is
-//                one 16-byte LDS read;
-//  3. bwd_dkdv:  one workgroup per (KV head, 128-key tile); loops over the
+//  2. bwd_dkdv:  one workgroup per (KV head, 128-key tile); loops over the
 //                query heads that share the KV head and over 32-row query
 //                tiles, accumulating dK^T and dV^T in registers (no atomics);
-//  4. bwd_dq:    one workgroup per (query head, 256-row tile); loops over
+//  3. bwd_dq:    one workgroup per (query head, 256-row tile); loops over
 //                32-key tiles, accumulating dQ^T in registers.
 // The dK/dV and dQ passes both rebuild S and dP, which costs two GEMMs more
 // than a single pass with atomic dQ but keeps the result deterministic.
@@ -79,9 +76,8 @@ struct BwdArgs {
   bf16* dk;
   bf16* dv;
   float* ld;      // [B, Hq, sqp / 32][64]: lse2 of 32 rows, then D of the same rows
-  bf16* kt;       // [B, Hkv, D, skp]
   int B, Hq, Hkv, Sq, Sk, g, causal;
-  int sqp, skp;   // Sq, Sk rounded up to 64
+  int sqp;        // Sq rounded up to 64
   float scale;
   float c;        // scale * log2(e)
   int n_ktiles, total_kv;
@@ -106,21 +102,6 @@ __device__ __forceinline__ void wg_coords(int total, int tiles, int& tile, int& 
   }
   tile = W % tiles;
   head = W / tiles;
-}
-
-// 16-byte MFMA operand fragment of a 32-row LDS tile with D columns (rows of
-// 2D bytes, chunks permuted by chunk_swizzle).
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int chunk) {
-  return *(const bf16x8*)(tile + row * (2 * D) + ((chunk ^ chunk_swizzle<D>(row)) << 4));
-}
-
-// 16-byte fragment of a transposed tile: D rows of 32 sequence positions
-// (64 bytes), chunks permuted by (row >> 2) & 3, which makes 16 consecutive
-// rows at one logical chunk hit 16 distinct bank groups.
-__device__ __forceinline__ int tr_swizzle(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int row, int chunk) {
-  return *(const bf16x8*)(tile + row * 64 + ((chunk ^ tr_swizzle(row)) << 4));
 }
 
 template <int D>
@@ -555,9 +536,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
 // dQ. Wavefront w owns queries p + 64w .. +63 as two blocks of 32 MFMA
 // columns: S^T = K Q^T and dP^T = V dO^T (rows = 32 keys) take Q and dO from
 // registers, dQ^T += K^T dS^T (rows = d) takes dS^T from the score
-// accumulators; each K, V or K^T fragment read from LDS feeds two MFMAs.
-// Rings as in the dK/dV pass: [K | V] rows of key tile t are loaded in step
-// t-3 and read in step t-1, K^T in step t-2 and read in step t+1.
+// accumulators and K^T from transposing LDS reads of the row-major K tile;
+// each K, V or K^T fragment read from LDS feeds two MFMAs. A 4-slot ring of
+// [K | V] row tiles: key tile t is loaded at the start of step t-2 and read in
+// steps t-1 (K, V) and t+1 (K^T).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
@@ -565,14 +547,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int MB = D / 32;
   constexpr int NU = DC;                        // units per step: 2 row fragments + 1 K^T fragment each
   constexpr int CPR = D / 8;
-  constexpr int TB = BT * D * 2;
+  constexpr int RB = 2 * D;                     // bytes per row
+  constexpr int TB = BT * RB;
   constexpr int INSTR = TB / 4096;
-  constexpr int NDMA = 3 * INSTR;               // K, V, K^T
+  constexpr int NDMA = 2 * INSTR;               // K, V
   constexpr int RING = 4;
-  constexpr int T_OFF = RING * 2 * TB;
   static_assert(2 * MB == NU, "one K^T fragment per unit");
-  static_assert(NU >= NDMA, "one DMA per unit at most");
-  __shared__ __attribute__((aligned(1024))) char smem[T_OFF + RING * TB];
+  __shared__ __attribute__((aligned(1024))) char smem[RING * 2 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -636,55 +617,60 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const size_t kvh = (size_t)b * a.Hkv + hkv;
   const bf16* kg = a.k + kvh * (size_t)a.Sk * D;
   const bf16* vg = a.v + kvh * (size_t)a.Sk * D;
-  const bf16* ktg = a.kt + kvh * (size_t)D * a.skp;
-  uint32_t rb[DC], tb[2];
+  uint32_t rb[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * (2 * D) + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+  for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
+  // Transposing reads: the A operand of dQ^T += K^T dS^T for d-block mb and
+  // 16-key chunk kc is two 4-key reads at rows 16 kc + 4 hi + (L >> 2) (+8)
+  // and columns 32 mb + 16 dhalf + 4 (L & 3) of the K tile; their key order is
+  // the register order of the dS^T fragments. The row swizzle does not change
+  // with kc, so kc is an immediate offset.
+  uint32_t vb[MB][2];
+  {
+    const int L = lane & 15, dhalf = (lane >> 4) & 1;
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) tb[kc] = T_OFF + l32 * 64 + (((2 * kc + hi) ^ tr_swizzle(l32)) << 4);
-  uint32_t roff[INSTR], toff[INSTR];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 4 * hi + (L >> 2) + 8 * h;
+        const int c = 32 * mb + 16 * dhalf + 4 * (L & 3);
+        vb[mb][h] = r * RB + (((c >> 3) ^ chunk_swizzle<D>(r)) << 4) + (c & 7) * 2;
+      }
+  }
+  uint32_t roff[INSTR];
 #pragma unroll
   for (int i = 0; i < INSTR; ++i) {
     const int P = (wid * INSTR + i) * 64 + lane;
     const int rr = P / CPR;
-    roff[i] = rr * (2 * D) + (((P % CPR) ^ chunk_swizzle<D>(rr)) << 4);
-    const int tr = P / 4;
-    toff[i] = (uint32_t)(tr * a.skp + ((P & 3) ^ tr_swizzle(tr)) * 8) * 2;
+    roff[i] = rr * RB + (((P % CPR) ^ chunk_swizzle<D>(rr)) << 4);
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + wid * INSTR * 1024);
-  // K / V rows (rows past Sk are out of range and read zeros) and K^T of the
-  // KV head; a key tile is a byte offset
-  const u32x4 rk = buffer_rsrc(kg, (uint32_t)a.Sk * (2 * D));
-  const u32x4 rv = buffer_rsrc(vg, (uint32_t)a.Sk * (2 * D));
-  const u32x4 rkt = buffer_rsrc(ktg, (uint32_t)a.skp * (2 * D));
+  // K / V rows of the KV head (rows past Sk are out of range and read zeros);
+  // a key tile is a byte offset
+  const u32x4 rk = buffer_rsrc(kg, (uint32_t)a.Sk * RB);
+  const u32x4 rv = buffer_rsrc(vg, (uint32_t)a.Sk * RB);
   struct DmaOff {
-    uint32_t vr[INSTR];                         // rows of key tile t3 (per lane)
-    uint32_t st;                                // K^T columns of key tile t2
+    uint32_t vr[INSTR];                         // rows of the key tile (per lane)
   };
   // key tiles past the last one are clamped to it (reloaded into unread slots)
-  auto dma_offsets = [&](int t3, int t2) __attribute__((always_inline)) {
+  auto dma_offsets = [&](int t) __attribute__((always_inline)) {
     DmaOff o;
-    const uint32_t key3 = (uint32_t)min(t3, n - 1) * BT;
+    const uint32_t key = (uint32_t)min(t, n - 1) * BT;
 #pragma unroll
-    for (int i = 0; i < INSTR; ++i) o.vr[i] = roff[i] + key3 * (2 * D);
-    o.st = (uint32_t)min(max(t2, 0), n - 1) * (BT * 2);
+    for (int i = 0; i < INSTR; ++i) o.vr[i] = roff[i] + key * RB;
     return o;
   };
-  auto dma_one = [&](auto skv_, auto skt_, auto qi_, const DmaOff& o) __attribute__((always_inline)) {
-    constexpr int SKV = decltype(skv_)::value, SKT = decltype(skt_)::value;
+  auto dma_one = [&](auto skv_, auto qi_, const DmaOff& o) __attribute__((always_inline)) {
+    constexpr int SKV = decltype(skv_)::value;
     constexpr int QI = decltype(qi_)::value;
     constexpr int i = QI % INSTR;
     constexpr uint32_t part = i * 1024;
     if constexpr (QI < INSTR)
       dma16b_at<SKV * 2 * TB + part>(rk, o.vr[i], 0u, ldsw);
-    else if constexpr (QI < 2 * INSTR)
-      dma16b_at<SKV * 2 * TB + TB + part>(rv, o.vr[i], 0u, ldsw);
     else
-      dma16b_at<T_OFF + SKT * TB + part>(rkt, toff[i], o.st, ldsw);
+      dma16b_at<SKV * 2 * TB + TB + part>(rv, o.vr[i], 0u, ldsw);
   };
   using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C3 = std::integral_constant<int, 3>;
 
   f32x16 dqt[2][MB];
 #pragma unroll
@@ -696,12 +682,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   f32x16 s_[2][2], dp_[2];
   bf16x8 dsf[2][2][2];                          // [tile parity][column block][16-key chunk]
 
-  // One step j (slot position POS = j mod 4), in two phases:
+  // One step j (slot position POS = j mod 4), after the DMA of tile j+2 (issued
+  // first, so that it has the whole step to land), in two phases:
   //  1. unit u = 0 .. NU-1: S^T of tile j+1 from K fragment u (2 MFMAs), dQ^T of
   //     tile j-1 from K^T fragment u (d-block u % MB, 16-key chunk u / MB;
   //     2 MFMAs), and a share of the elementwise work (dS) of tile j;
-  //  2. unit u: dP^T of tile j+1 from V fragment u (2 MFMAs), and the DMA of
-  //     tiles j+2 / j+3.
+  //  2. unit u: dP^T of tile j+1 from V fragment u (2 MFMAs).
   auto step = [&](auto pos_, auto g1, auto g2, auto ew, auto mask_, int j) __attribute__((always_inline)) {
     constexpr int POS = decltype(pos_)::value;
     constexpr int P = POS & 1;
@@ -710,15 +696,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     constexpr bool EW = decltype(ew)::value;
     constexpr bool MASK = decltype(mask_)::value;
     constexpr int SKV = (POS + 1) % RING;       // K, V rows of tile j+1
-    constexpr int SKT = (POS + 3) % RING;       // K^T of tile j-1
+    constexpr int SKT = (POS + 3) % RING;       // K rows of tile j-1, read transposed
+    constexpr int SD = (POS + 2) % RING;        // DMA target: tile j+2
     const char* lds = smem;
     auto kfr = [&](int u) __attribute__((always_inline)) { return *(const bf16x8*)(lds + rb[u] + SKV * 2 * TB); };
     auto vfr = [&](int u) __attribute__((always_inline)) { return *(const bf16x8*)(lds + rb[u] + SKV * 2 * TB + TB); };
     auto tfr = [&](int u) __attribute__((always_inline)) {
-      return *(const bf16x8*)(lds + tb[u / MB] + SKT * TB + (u % MB) * 32 * 64);
+      const char* t = lds + SKT * 2 * TB + (u / MB) * 16 * RB;
+      return cat4(lds_read_tr((const bf16*)(t + vb[u % MB][0])), lds_read_tr((const bf16*)(t + vb[u % MB][1])));
     };
-    DmaOff o;
-    if constexpr (G1) o = dma_offsets(j + 3, j + 2);
+    if constexpr (G1) {
+      const DmaOff o = dma_offsets(j + 2);
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(std::integral_constant<int, SD>{}, qi, o); });
+    }
     const int key0 = j * BT;
     bf16x8 fk[2], ft[2], fv[2];
     if constexpr (G1) fk[0] = kfr(0);
@@ -771,9 +761,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         dp_[0] = mfma32(fv[u & 1], df[0][u], u == 0 ? f32x16{} : dp_[0]);
         dp_[1] = mfma32(fv[u & 1], df[1][u], u == 0 ? f32x16{} : dp_[1]);
-        if constexpr (u < NDMA)
-          dma_one(std::integral_constant<int, (POS + 3) % RING>{}, std::integral_constant<int, (POS + 2) % RING>{},
-                  uc, o);
       });
     }
   };
@@ -786,8 +773,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   // Causal masking is needed only for key tiles that reach past the first
   // query of the workgroup: the last ones of the walk. The first n_um steps
   // run unmasked, the rest masked (switching at a multiple of 4). Without a
-  // causal mask nothing needs masking: keys past Sk have zero K^T columns, so
-  // their dS never reaches dQ.
+  // causal mask nothing needs masking: keys past Sk have zero K rows, so their
+  // dS never reaches dQ.
   using M_ = std::integral_constant<bool, CAUSAL>;
   int n_um = n;
   if (CAUSAL) {
@@ -797,14 +784,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   auto full = [&](auto pos_, auto g2, auto mask_, int j) __attribute__((always_inline)) {
     step(pos_, T_{}, g2, T_{}, mask_, j);
   };
-  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
+  // step j: tile j+1 has landed for every wavefront (each waits for all its
+  // DMA, the barrier for all of them), and every wavefront is done with step
+  // j-1
+  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   if (n > 0) {
     {
-      const DmaOff o3 = dma_offsets(0, 0);      // step -3: rows of tile 0, K^T of "tile -1" (dummy)
-      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C0{}, C3{}, qi, o3); });
-      const DmaOff o2 = dma_offsets(1, 0);      // step -2: rows of tile 1, K^T of tile 0
-      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C1{}, C0{}, qi, o2); });
+      const DmaOff o0 = dma_offsets(0);         // tile 0; step -1 loads tile 1
+      static_for<NDMA>([&](auto qi) __attribute__((always_inline)) { dma_one(C0{}, qi, o0); });
     }
     sync();
     step(I3{}, T_{}, F_{}, F_{}, F_{}, -1);
@@ -855,6 +843,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       default: step(I3{}, F_{}, T_{}, F_{}, F_{}, n); break;
     }
   }
+  // no LDS DMA may still be in flight when the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -873,18 +863,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 }
 
 struct WsLayout {
-  size_t ld, kt, total;
+  size_t ld, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 WsLayout ws_layout(const Problem& p) {
   const size_t sqp = (size_t)((p.Sq + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
-  const size_t skp = (size_t)((p.Sk + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
   WsLayout w{};
   w.ld = 0;
-  w.kt = align256((size_t)p.B * p.Hq * sqp * 2 * sizeof(float));
-  w.total = w.kt + align256((size_t)p.B * p.Hkv * p.d * skp * 2);
+  w.total = align256((size_t)p.B * p.Hq * sqp * 2 * sizeof(float));
   return w;
 }
 
@@ -896,14 +884,6 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   if (rows > 0) {
     timing_begin(s, "bwd_pre");
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
-    e = hipGetLastError();
-    timing_end(s);
-    if (e != hipSuccess) return e;
-  }
-  if (a.skp > 0) {
-    timing_begin(s, "bwd_transpose");
-    hipLaunchKernelGGL((transpose_rows_kernel<D>), dim3(a.skp / TILE_ROWS, a.Hkv, a.B), dim3(256), 0, s,
-                       a.k, a.kt, a.Hkv, a.Sk, a.skp);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -930,10 +910,10 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   }
   if (log != nullptr && log_n > 0)
     snprintf(log, log_n,
-             "attn_bwd: bwd_pre<d=%d> grid=%zu; transpose_rows<d=%d> (K^T); "
+             "attn_bwd: bwd_pre<d=%d> grid=%zu; "
              "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles, 8 wavefronts); "
              "bwd_dq<d=%d> grid=%d (256 rows x 32-key tiles)",
-             D, (rows + RPB - 1) / RPB, D, D, a.total_kv, D, a.total_q);
+             D, (rows + RPB - 1) / RPB, D, a.total_kv, D, a.total_q);
   return hipSuccess;
 }
 
@@ -956,7 +936,6 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   a.dk = (bf16*)dk;
   a.dv = (bf16*)dv;
   a.ld = (float*)((char*)ws + w.ld);
-  a.kt = (bf16*)((char*)ws + w.kt);
   a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
@@ -965,7 +944,6 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
   a.sqp = (p.Sq + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
-  a.skp = (p.Sk + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
   a.n_ktiles = (p.Sk + KV_WG - 1) / KV_WG;

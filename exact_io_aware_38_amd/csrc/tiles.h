@@ -1,6 +1,6 @@
-// Tile helpers shared by the forward and backward kernels: the LDS DMA,
-// the layout of transposed copies (X^T with the sequence index permuted
-// inside groups of 16) and the kernel that writes them.
+// Tile helpers shared by the forward and backward kernels: the LDS DMA
+// (global or buffer loads straight into LDS), compile-time loops and the
+// register pins the pipelined kernels use.
 #pragma once
 
 #include "common.h"
@@ -142,58 +142,6 @@ __device__ __forceinline__ T settle(T x) {
     return __builtin_bit_cast(T, w);
   }
 }
-
-// Swizzle of the 8 16-byte chunks of a 128-byte row of a transposed tile
-// (64 sequence positions): conflict-free 16-byte reads of 16 consecutive rows
-// at one logical chunk.
-__device__ __forceinline__ int vt_swizzle(int row) { return (row >> 1) & 7; }
-
-// Position of sequence index k inside its group of 16 in a transposed row:
-// index 8a + 4h + e is stored at 8h + 4a + e, so that lane half h of an MFMA
-// operand finds its 8 reduction slots (indices 8a + 4h + e, a in {0,1}, e in
-// 0..3; the register order of an accumulator tile) in one 16-byte chunk. The
-// map swaps two bits, so it is its own inverse.
-__device__ __forceinline__ int vt_perm(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
-
-
-// ---------------------------------------------------------------------------
-// X [B, H, S, D] -> X^T [B, H, D, sp] with the sequence index permuted by
-// vt_perm inside each group of 16 and zero padding past S. One workgroup per
-// (64-row tile, head, batch).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void transpose_rows_kernel(const bf16* __restrict__ src_all,
-                                                             bf16* __restrict__ dst_all, int H, int S_len,
-                                                             int sp) {
-  constexpr int S = D + 2;                       // odd word stride: column reads spread over banks
-  __shared__ bf16 tile[TILE_ROWS * S];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * TILE_ROWS;
-  const size_t head = (size_t)blockIdx.z * H + blockIdx.y;
-  const bf16* src = src_all + head * (size_t)S_len * D;
-  for (int c = tid; c < TILE_ROWS * D / 8; c += 256) {
-    const int row = c / (D / 8);
-    const int col = (c % (D / 8)) * 8;
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (t0 + row < S_len) val = *(const u32x4*)(src + (size_t)(t0 + row) * D + col);
-    const bf16x8 e = __builtin_bit_cast(bf16x8, val);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[row * S + col + i] = e[i];
-  }
-  __syncthreads();
-  bf16* dst = dst_all + head * (size_t)D * sp + t0;
-  for (int c = tid; c < D * (TILE_ROWS / 8); c += 256) {
-    const int d = c / (TILE_ROWS / 8);
-    const int ch = c % (TILE_ROWS / 8);
-    bf16x8 e;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = tile[vt_perm(8 * ch + j) * S + d];
-    *(bf16x8*)(dst + (size_t)d * sp + 8 * ch) = e;
-  }
-}
-
 
 }  // namespace
 }  // namespace attn
