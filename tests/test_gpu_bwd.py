@@ -47,6 +47,9 @@ SMALL = [
     (1, 2, 2, 150, 60, 128, 2),     # Sq > Sk bottom-right: fully masked query rows
     (1, 8, 2, 64, 64, 128, 0),      # one tile each way
     (1, 3, 1, 1, 77, 64, 0),        # a single query row
+    (1, 2, 1, 130, 250, 64, 2),     # d = 64, bottom-right, 2 query heads per KV head
+    (1, 8, 2, 520, 520, 128, 1),    # 17 query tiles x 4 query heads per KV head: unrolled loops, head changes
+    (1, 4, 4, 96, 1000, 64, 0),     # Sk >> Sq, no mask: eight 128-key workgroups per head
 ]
 
 
