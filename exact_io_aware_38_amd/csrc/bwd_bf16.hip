@@ -16,7 +16,7 @@
 //  2. bwd_dkdv:  one workgroup per (KV head, 128-key tile); loops over the
 //                query heads that share the KV head and over 32-row query
 //                tiles, accumulating dK^T and dV^T in registers (no atomics);
-//  3. bwd_dq:    one workgroup per (query head, 256-row tile); loops over
+//  3. bwd_dq:    one workgroup per (query head, 128-row tile); loops over
 //                32-key tiles, accumulating dQ^T in registers.
 // The dK/dV and dQ passes both rebuild S and dP, which costs two GEMMs more
 // than a single pass with atomic dQ but keeps the result deterministic.
@@ -24,9 +24,9 @@
 // Mapping to CDNA4: in the dK/dV pass the two wavefronts that share a SIMD
 // split each tile's work (scores and elementwise terms on one, the gradient
 // products on the other), so one's vector work runs under the other's MFMAs.
-// The dQ pass keeps one wavefront per SIMD, whose step j interleaves, MFMA by
-// MFMA, the score and dP products of tile j+1, the dQ products of tile j-1
-// and the elementwise work (P, dS) of tile j. Tiles arrive by LDS DMA ahead
+// In the dQ pass each wavefront's step j interleaves, MFMA by MFMA, the score
+// and dP products of tile j+1, the dQ products of tile j-1 and the
+// elementwise work (P, dS) of tile j; two workgroups share each CU. Tiles arrive by LDS DMA ahead
 // of their first use, in rings sized so that no slot is rewritten while any
 // wavefront still reads it.
 #include "common.h"
@@ -44,7 +44,12 @@ namespace {
 
 constexpr int BT = 32;        // rows of a pipeline tile (queries for dK/dV, keys for dQ)
 constexpr int KV_WG = 128;    // keys per dK/dV workgroup (4 wavefronts x 32)
-constexpr int Q_WG = 256;     // queries per dQ workgroup (4 wavefronts x 64)
+// 32-query column blocks per dQ wavefront. With one, a wavefront needs under
+// 256 registers, so two workgroups share each CU and the two wavefronts on a
+// SIMD fill each other's stalls (measured 4 % faster than two blocks, which
+// let each K, V or K^T fragment feed two MFMAs but held 512 registers).
+constexpr int DQ_NCB = 1;
+constexpr int Q_WG = 4 * 32 * DQ_NCB;         // queries per dQ workgroup (4 wavefronts)
 
 // Score MFMAs with the accumulator in VGPRs (the elementwise code reads every
 // score; AGPR accumulators would need one v_accvgpr_read per score), issued
@@ -533,16 +538,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 // ---------------------------------------------------------------------------
-// dQ. Wavefront w owns queries p + 64w .. +63 as two blocks of 32 MFMA
+// dQ. Wavefront w owns queries p + 32 NCB w .. as NCB blocks of 32 MFMA
 // columns: S^T = K Q^T and dP^T = V dO^T (rows = 32 keys) take Q and dO from
 // registers, dQ^T += K^T dS^T (rows = d) takes dS^T from the score
 // accumulators and K^T from transposing LDS reads of the row-major K tile;
-// each K, V or K^T fragment read from LDS feeds two MFMAs. A 4-slot ring of
+// each K, V or K^T fragment read from LDS feeds NCB MFMAs. A 4-slot ring of
 // [K | V] row tiles: key tile t is loaded at the start of step t-2 and read in
 // steps t-1 (K, V) and t+1 (K^T).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NCB = DQ_NCB;
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
   constexpr int NU = DC;                        // units per step: 2 row fragments + 1 K^T fragment each
@@ -568,19 +574,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int hq = bh % a.Hq;
   const int b = bh / a.Hq;
   const int hkv = hq / a.g;
-  const int p0 = qb * Q_WG + 64 * wid;          // first query of the wavefront
+  const int p0 = qb * Q_WG + 32 * NCB * wid;    // first query of the wavefront
   const int wg_last = min(qb * Q_WG + Q_WG, a.Sq) - 1;
   int kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
   if (kend < 0) kend = 0;
   const int n = (kend + BT - 1) / BT;
 
   const size_t hrow = (size_t)b * a.Hq + hq;
-  int pos[2], lim[2];
-  bool valid[2];
-  bf16x8 qf[2][DC], df[2][DC];
-  float l2[2], dl[2];
+  int pos[NCB], lim[NCB];
+  bool valid[NCB];
+  bf16x8 qf[NCB][DC], df[NCB][DC];
+  float l2[NCB], dl[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     pos[cb] = p0 + 32 * cb + l32;
     valid[cb] = pos[cb] < a.Sq;
     lim[cb] = a.causal ? min(kend - 1, pos[cb] + off) : kend - 1;
@@ -604,7 +610,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {       // only MFMAs read them: keep them in AGPRs
       qf[cb][dc] = settle(qf[cb][dc]);
@@ -672,15 +678,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   };
   using C0 = std::integral_constant<int, 0>;
 
-  f32x16 dqt[2][MB];
+  f32x16 dqt[NCB][MB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) dqt[cb][mb] = f32x16{};
   // S^T of two tiles in flight; dP^T of one (the elementwise work of tile j
   // reads it before the dP^T products of tile j+1 start)
-  f32x16 s_[2][2], dp_[2];
-  bf16x8 dsf[2][2][2];                          // [tile parity][column block][16-key chunk]
+  f32x16 s_[2][NCB], dp_[NCB];
+  bf16x8 dsf[2][NCB][2];                        // [tile parity][column block][16-key chunk]
 
   // One step j (slot position POS = j mod 4), after the DMA of tile j+2 (issued
   // first, so that it has the whole step to land), in two phases:
@@ -713,7 +719,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     bf16x8 fk[2], ft[2], fv[2];
     if constexpr (G1) fk[0] = kfr(0);
     if constexpr (G2) ft[0] = tfr(0);
-    float dt[2][8];
+    float dt[NCB][8];
     static_for<NU>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
       if constexpr (u + 1 < NU) {
@@ -725,17 +731,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (G1) {
-        s_[P ^ 1][0] = mfma32(fk[u & 1], qf[0][u], u == 0 ? f32x16{} : s_[P ^ 1][0]);
-        s_[P ^ 1][1] = mfma32(fk[u & 1], qf[1][u], u == 0 ? f32x16{} : s_[P ^ 1][1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          s_[P ^ 1][cb] = mfma32(fk[u & 1], qf[cb][u], u == 0 ? f32x16{} : s_[P ^ 1][cb]);
       }
       if constexpr (G2) {
-        dqt[0][u % MB] = mfma32(ft[u & 1], dsf[P ^ 1][0][u / MB], dqt[0][u % MB]);
-        dqt[1][u % MB] = mfma32(ft[u & 1], dsf[P ^ 1][1][u / MB], dqt[1][u % MB]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          dqt[cb][u % MB] = mfma32(ft[u & 1], dsf[P ^ 1][cb][u / MB], dqt[cb][u % MB]);
       }
       if constexpr (EW) {
-        // values [v0, v1) of the 32 score registers (16 per column block)
-        constexpr int v0 = (u * 32) / NU;
-        constexpr int v1 = ((u + 1) * 32) / NU;
+        // values [v0, v1) of the 16 NCB score registers (16 per column block)
+        constexpr int v0 = (u * 16 * NCB) / NU;
+        constexpr int v1 = ((u + 1) * 16 * NCB) / NU;
 #pragma unroll
         for (int vv = v0; vv < v1; ++vv) {
           const int cb = vv >> 4;
@@ -759,8 +767,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         constexpr int u = decltype(uc)::value;
         if constexpr (u + 1 < NU) fv[(u + 1) & 1] = vfr(u + 1);
         __builtin_amdgcn_sched_barrier(0);
-        dp_[0] = mfma32(fv[u & 1], df[0][u], u == 0 ? f32x16{} : dp_[0]);
-        dp_[1] = mfma32(fv[u & 1], df[1][u], u == 0 ? f32x16{} : dp_[1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) dp_[cb] = mfma32(fv[u & 1], df[cb][u], u == 0 ? f32x16{} : dp_[cb]);
       });
     }
   };
@@ -847,7 +855,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     if (!valid[cb]) continue;
     bf16* dst = a.dq + (hrow * a.Sq + pos[cb]) * D;
 #pragma unroll
@@ -912,8 +920,8 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
     snprintf(log, log_n,
              "attn_bwd: bwd_pre<d=%d> grid=%zu; "
              "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles, 8 wavefronts); "
-             "bwd_dq<d=%d> grid=%d (256 rows x 32-key tiles)",
-             D, (rows + RPB - 1) / RPB, D, a.total_kv, D, a.total_q);
+             "bwd_dq<d=%d> grid=%d (%d rows x 32-key tiles)",
+             D, (rows + RPB - 1) / RPB, D, a.total_kv, D, a.total_q, Q_WG);
   return hipSuccess;
 }
 
