@@ -97,7 +97,7 @@ __device__ __forceinline__ float tree_sum32(const float* v) {
   return t[0];
 }
 
-// LDS tiles of 64 rows x D bf16 are stored unpadded, with the 16-byte chunks
+// LDS tiles of 32 or 64 rows x D bf16 are stored unpadded, with the 16-byte chunks
 // of each row XOR-permuted by this row function. gfx950 LDS serves 256 bytes
 // per clock over 64 banks: 16-byte row reads (16 consecutive rows, same
 // logical chunk) and transposed 8-byte reads (4 consecutive rows x 4 adjacent

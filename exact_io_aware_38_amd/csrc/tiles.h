@@ -1,6 +1,6 @@
 // Tile helpers shared by the forward and backward kernels: the LDS DMA
-// (global or buffer loads straight into LDS), compile-time loops and the
-// register pins the pipelined kernels use.
+// (buffer loads straight into LDS), compile-time loops and the register pins
+// the pipelined kernels use.
 #pragma once
 
 #include "common.h"
@@ -11,52 +11,7 @@
 namespace attn {
 namespace {
 
-constexpr int TILE_ROWS = 64;        // sequence rows per staged tile
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-// 16 bytes per lane from global memory straight into LDS at base + 16 * lane
-// (base must be wave-uniform). Issued as inline assembly: the compiler would
-// otherwise make every later LDS read wait for all outstanding DMA (it cannot
-// tell the ring stages apart), which serialises the prefetch; the kernels wait
-// for their DMA explicitly (s_waitcnt vmcnt + s_barrier) before reading a stage.
-// On this chip generation an LDS DMA instruction must not read M0 in the cycle
-// right after a scalar write to it, so every helper puts one s_nop between
-// the two (the compiler's hazard pass does not look inside inline assembly).
-__device__ __forceinline__ void dma16(const void* g, lds_void* base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(g)
-               : "memory", "m0");
-}
-
-// Wave-uniform 64-bit pointer held in scalar registers.
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t x = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Scalar-base forms: lane address = sbase + voff (32-bit unsigned byte
-// offset), which keeps the per-lane address arithmetic to 32 bits.
-__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, lds_void* base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(uniform_ptr(sbase))
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, lds_void* base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(uniform_ptr(sbase))
-               : "memory", "m0");
-}
-
+constexpr int TILE_ROWS = 64;        // the backward pads Sq to a multiple of this
 
 // Buffer resource for raw loads with range checking: a lane whose byte
 // offset is >= num_bytes reads zeros. Word 3 selects the 32-bit data format
@@ -71,20 +26,16 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t num_byte
   return r;
 }
 
-// 16 bytes per lane from a buffer (offset voff, range-checked) into LDS at
-// base + 16 * lane.
-__device__ __forceinline__ void dma16b(u32x4 rsrc, uint32_t voff, lds_void* base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-
-// Same with the LDS byte address given as a wave-uniform base plus a
-// compile-time offset (one scalar add builds M0), and a scalar byte offset
-// soff added to the address (not range-checked: only voff is compared with
-// the buffer size).
+// LDS DMA: 16 (or 4) bytes per lane from a buffer (byte offset voff,
+// range-checked, plus a scalar byte offset soff that is not range-checked)
+// straight into LDS at lds_base + OFF + 16 * lane (4 * lane); lds_base must be
+// wave-uniform, OFF is a compile-time offset (one scalar add builds M0).
+// Issued as inline assembly: the compiler would otherwise make every later
+// LDS read wait for all outstanding DMA (it cannot tell the ring slots apart);
+// the kernels wait for their DMA explicitly (s_waitcnt vmcnt + s_barrier)
+// before reading a slot. On this chip generation an LDS DMA instruction must
+// not read M0 in the cycle right after a scalar write to it, hence the s_nop
+// (the compiler's hazard pass does not look inside inline assembly).
 template <uint32_t OFF>
 __device__ __forceinline__ void dma16b_at(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
   asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -117,7 +68,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 // first chained use), instead of interleaved with the MFMAs they should hide
 // behind. The empty volatile statement forces them to exist at this point.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float& x, float& y) { asm volatile("" : "+v"(x), "+v"(y)); }
 __device__ __forceinline__ void pin(bf16x8& x) {
   u32x4 w = __builtin_bit_cast(u32x4, x);
   asm volatile("" : "+v"(w));
