@@ -155,8 +155,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //    dK^T += Q^T dS (rows = d) one step later, reading dO^T and Q^T with
 //    transposing LDS reads of the row-major tiles the score wavefront used,
 //    and issues all the tile DMA.
-// The score wavefront raises its issue priority for its MFMAs, so that its
-// partner's gradient MFMAs fill the matrix pipe while it does the vector work.
+// The partner's gradient MFMAs fill the matrix pipe while the score wavefront
+// does its vector work.
 //
 // LDS: a 4-slot ring of [Q | dO] row tiles (tile t loaded at the start of
 // step t-1, read in steps t and t+1) with its lse2/D blocks, and a 2-slot
@@ -280,7 +280,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 f[3];
       f[0] = frag(0);
       f[1] = frag(1);
-      __builtin_amdgcn_s_setprio(2);
       static_for<2 * DC>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k + 2 < 2 * DC) f[(k + 2) % 3] = frag(k + 2);
@@ -298,7 +297,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
         }
       });
       score_settle(s, dp);
-      __builtin_amdgcn_s_setprio(0);
       // accumulator register v holds query q0 + 8 (v >> 2) + 4 hi + (v & 3)
       float p[16], ds[16];
 #pragma unroll
