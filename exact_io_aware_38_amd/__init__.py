@@ -15,7 +15,8 @@ from typing import Optional, Tuple
 __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "lib", "library_path", "fwd", "bwd",
     "fwd_workspace_bytes", "bwd_workspace_bytes", "strerror", "last_dispatch",
-    "timing_start", "timing_stop",
+    "timing_start", "timing_stop", "fwd_varlen", "bwd_varlen", "fwd_varlen_workspace_bytes",
+    "bwd_varlen_workspace_bytes",
 ]
 
 ATTN_F32 = 0
@@ -29,6 +30,8 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 _Z = ctypes.c_size_t
 _SHAPE = [_I] * 7                      # B, Hq, Hkv, Sq, Sk, d, causal
+_IP = ctypes.POINTER(ctypes.c_int)
+_VSHAPE = [_IP, _IP] + [_I] * 5        # cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal
 
 
 class AttnError(RuntimeError):
@@ -60,6 +63,14 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = _I
         L.attn_bwd.argtypes = [_P] * 9 + _SHAPE + [_F, _I, _P, _Z, _P]
         L.attn_bwd.restype = _I
+        L.attn_fwd_varlen_workspace_bytes.argtypes = _VSHAPE + [_I]
+        L.attn_fwd_varlen_workspace_bytes.restype = _Z
+        L.attn_bwd_varlen_workspace_bytes.argtypes = _VSHAPE + [_I]
+        L.attn_bwd_varlen_workspace_bytes.restype = _Z
+        L.attn_fwd_varlen.argtypes = [_P, _P, _P, _P, _P] + _VSHAPE + [_F, _I, _P, _Z, _P]
+        L.attn_fwd_varlen.restype = _I
+        L.attn_bwd_varlen.argtypes = [_P] * 9 + _VSHAPE + [_F, _I, _P, _Z, _P]
+        L.attn_bwd_varlen.restype = _I
         L.attn_strerror.argtypes = [_I]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_dispatch.argtypes = [ctypes.c_char_p, _Z]
@@ -207,4 +218,100 @@ def bwd(q, k, v, o, lse, dout, *, causal: int = 0, scale: Optional[float] = None
                         _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def _cu_array(cu, name: str):
+    """A host ctypes int array from a sequence or CPU tensor of B+1 offsets."""
+    vals = [int(x) for x in (cu.tolist() if hasattr(cu, "tolist") else cu)]
+    if len(vals) < 2:
+        raise ValueError(f"{name} needs at least 2 entries (B+1 offsets), got {len(vals)}")
+    return (ctypes.c_int * len(vals))(*vals), vals
+
+
+def _varlen_cu(cu_seqlens_q, cu_seqlens_k):
+    cq, vq = _cu_array(cu_seqlens_q, "cu_seqlens_q")
+    ck, vk = _cu_array(cu_seqlens_k, "cu_seqlens_k")
+    if len(vq) != len(vk):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    return cq, ck, len(vq) - 1, vq[-1], vk[-1]
+
+
+def fwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, Hq, Hkv, d, causal, dtype) -> int:
+    cq, ck, B, _, _ = _varlen_cu(cu_seqlens_q, cu_seqlens_k)
+    return int(lib().attn_fwd_varlen_workspace_bytes(cq, ck, B, Hq, Hkv, d, causal, dtype))
+
+
+def bwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, Hq, Hkv, d, causal, dtype) -> int:
+    cq, ck, B, _, _ = _varlen_cu(cu_seqlens_q, cu_seqlens_k)
+    return int(lib().attn_bwd_varlen_workspace_bytes(cq, ck, B, Hq, Hkv, d, causal, dtype))
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: int = 0, scale: Optional[float] = None,
+               out=None, lse=None, need_lse: bool = True, workspace=None, stream=None):
+    """O (and lse) for a packed batch of sequences of different lengths.
+
+    q is [Hq, total_q, d], k and v [Hkv, total_k, d], head-major and packed:
+    sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and rows
+    cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v. The offsets are host
+    data (a list or CPU tensor of B+1 ints). Returns (o [Hq, total_q, d],
+    lse [Hq, total_q]).
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse"), (workspace, "workspace")):
+        _check(t, n)
+    cq, ck, B, tq, tk = _varlen_cu(cu_seqlens_q, cu_seqlens_k)
+    Hq, _, d = q.shape
+    Hkv = k.shape[0]
+    dt = _dtype_code(q)
+    _want(q, (Hq, tq, d), q.dtype, "q")
+    _want(k, (Hkv, tk, d), q.dtype, "k")
+    _want(v, (Hkv, tk, d), q.dtype, "v")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (Hq, tq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and need_lse:
+        lse = torch.empty((Hq, tq), dtype=torch.float32, device=q.device)
+    ws_n = int(lib().attn_fwd_varlen_workspace_bytes(cq, ck, B, Hq, Hkv, d, causal, dt))
+    if workspace is None and ws_n > 0:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), cq, ck, B, Hq, Hkv,
+                               d, causal, sc, dt, _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_varlen")
+    return out, lse
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: int = 0,
+               scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of a packed batch, in the layout of fwd_varlen (bf16 only)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace")):
+        _check(t, n)
+    cq, ck, B, tq, tk = _varlen_cu(cu_seqlens_q, cu_seqlens_k)
+    Hq, _, d = q.shape
+    Hkv = k.shape[0]
+    dt = _dtype_code(q)
+    qs, ks = (Hq, tq, d), (Hkv, tk, d)
+    for t, n, shp in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (o, "o", qs), (dout, "dout", qs),
+                      (dq, "dq", qs), (dk, "dk", ks), (dv, "dv", ks)):
+        _want(t, shp, q.dtype, n)
+    _want(lse, (Hq, tq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_n = int(lib().attn_bwd_varlen_workspace_bytes(cq, ck, B, Hq, Hkv, d, causal, dt))
+    if workspace is None and ws_n > 0:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                               _ptr(dk), _ptr(dv), cq, ck, B, Hq, Hkv, d, causal, sc, dt,
+                               _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_varlen")
     return dq, dk, dv

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -66,7 +67,9 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, floa
   const long long rows_q = (long long)B * Hq * Sq;
   const long long rows_k = (long long)B * Hkv * (long long)Sk;
   if (rows_q > (1LL << 31) - 1 || rows_k > (1LL << 31) - 1) return ATTN_ERR_SHAPE;
-  if (Sq > (1 << 30) || Sk > (1 << 30)) return ATTN_ERR_SHAPE;
+  // the buffer loads take a head's byte range as a 32-bit count (2^24 rows of
+  // 256 bytes at d = 128 would already wrap it)
+  if (Sq >= (1 << 24) || Sk >= (1 << 24)) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
@@ -76,7 +79,71 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, floa
 }
 
 attn::Problem make_problem(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale) {
-  return attn::Problem{B, Hq, Hkv, Sq, Sk, d, causal, scale};
+  return attn::Problem{B, Hq, Hkv, Sq, Sk, d, causal, scale, Sq, Sk};
+}
+
+// Packed variable-length batches: host arrays of B+1 offsets, starting at 0
+// and non-decreasing. Each sequence is then validated as a dense problem of
+// batch 1 (with at least one row, so that the per-sequence checks apply).
+int check_varlen(const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int d, int causal, float scale,
+                 int dtype) {
+  if (cu_q == nullptr || cu_k == nullptr) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1) return ATTN_ERR_SHAPE;
+  if (cu_q[0] != 0 || cu_k[0] != 0) return ATTN_ERR_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return ATTN_ERR_SHAPE;
+  // every packed row index of a head must fit the kernels' 32-bit arithmetic
+  if ((long long)Hq * cu_q[B] > (1LL << 31) - 1 || (long long)Hkv * cu_k[B] > (1LL << 31) - 1)
+    return ATTN_ERR_SHAPE;
+  for (int b = 0; b < B; ++b) {
+    const int st = check_common(1, Hq, Hkv, std::max(1, cu_q[b + 1] - cu_q[b]), cu_k[b + 1] - cu_k[b], d,
+                                causal, scale, dtype);
+    if (st != ATTN_OK) return st;
+  }
+  return ATTN_OK;
+}
+
+// Sequence b of a packed batch as a dense problem of batch 1 whose head
+// strides are the packed totals (the data pointers are advanced to its first
+// row by the caller).
+attn::Problem seq_problem(const int* cu_q, const int* cu_k, int B, int b, int Hq, int Hkv, int d, int causal,
+                          float scale) {
+  attn::Problem p = make_problem(1, Hq, Hkv, cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b], d, causal, scale);
+  p.hsq = cu_q[B];
+  p.hsk = cu_k[B];
+  return p;
+}
+
+size_t fwd_ws(const attn::Problem& p, int dtype) {
+  if (dtype != ATTN_BF16) return 0;
+  const attn::SplitPlan sp = attn::plan_split(p);
+  return sp.use ? sp.ws_bytes : attn::plan_prefill(p).ws_bytes;
+}
+
+// The forward's kernel selection and launch for one validated problem; the
+// workspace must hold fwd_ws(p, dtype) bytes.
+hipError_t fwd_launch(const attn::Problem& p, int dtype, const void* q, const void* k, const void* v, void* o,
+                      float* lse, void* workspace, hipStream_t s, char* text, size_t text_n) {
+  hipError_t e;
+  if (dtype == ATTN_F32) {
+    e = attn::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, s);
+    std::snprintf(text, text_n, "fwd_f32<d=%d> grid=(%d,%d,%d) block=128 (one row per thread, 16-key tiles)",
+                  p.d, (p.Sq + 127) / 128, p.Hq, p.B);
+    return e;
+  }
+  const attn::SplitPlan sp = attn::plan_split(p);
+  if (sp.use) {
+    e = attn::launch_fwd_split_bf16(p, sp, q, k, v, o, lse, workspace, s);
+    std::snprintf(text, text_n,
+                  "fwd_split_bf16<d=%d> grid=%d block=64 nsplit=%d keys/split=%d; combine_split<d=%d> grid=%d",
+                  p.d, sp.nsplit * p.B * p.Hkv, sp.nsplit, sp.split_keys, p.d, p.B * p.Hq * p.Sq);
+    return e;
+  }
+  const attn::PrefillPlan pl = attn::plan_prefill(p);
+  e = attn::launch_fwd_prefill_bf16(p, pl, q, k, v, o, lse, workspace, s);
+  std::snprintf(text, text_n, "fwd_prefill_bf16<d=%d> grid=%d block=512 heads/wg=%d rows/wg=%d key_tile=64 causal=%d",
+                p.d, pl.total_wgs, pl.hw, pl.rows_per_wg, p.causal);
+  return e;
 }
 
 }  // namespace
@@ -180,10 +247,7 @@ int attn_last_dispatch(char* buf, size_t n) {
 
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int dtype) {
   if (check_common(B, Hq, Hkv, Sq, Sk, d, causal, 1.f, dtype) != ATTN_OK) return 0;
-  if (dtype != ATTN_BF16) return 0;
-  const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, 1.f);
-  const attn::SplitPlan sp = attn::plan_split(p);
-  return sp.use ? sp.ws_bytes : attn::plan_prefill(p).ws_bytes;
+  return fwd_ws(make_problem(B, Hq, Hkv, Sq, Sk, d, causal, 1.f), dtype);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -194,33 +258,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
-  hipStream_t s = (hipStream_t)stream;
-  char text[512];
-  hipError_t e;
-  if (dtype == ATTN_F32) {
-    e = attn::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, s);
-    std::snprintf(text, sizeof(text), "attn_fwd: fwd_f32<d=%d> grid=(%d,%d,%d) block=128 (one row per thread, 16-key tiles)",
-                  d, (Sq + 127) / 128, Hq, B);
-  } else {
-    const attn::SplitPlan sp = attn::plan_split(p);
-    if (sp.use) {
-      if (workspace_bytes < sp.ws_bytes || workspace == nullptr) return ATTN_ERR_WORKSPACE;
-      e = attn::launch_fwd_split_bf16(p, sp, q, k, v, o, lse, workspace, s);
-      std::snprintf(text, sizeof(text),
-                    "attn_fwd: fwd_split_bf16<d=%d> grid=%d block=64 nsplit=%d keys/split=%d; combine_split<d=%d> grid=%d",
-                    d, sp.nsplit * B * Hkv, sp.nsplit, sp.split_keys, d, B * Hq * Sq);
-    } else {
-      const attn::PrefillPlan pl = attn::plan_prefill(p);
-      if (pl.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < pl.ws_bytes)) return ATTN_ERR_WORKSPACE;
-      e = attn::launch_fwd_prefill_bf16(p, pl, q, k, v, o, lse, workspace, s);
-      std::snprintf(text, sizeof(text),
-                    "attn_fwd: transpose_v<d=%d> grid=(%d,%d,%d); fwd_prefill_bf16<d=%d> grid=%d block=512 "
-                    "heads/wg=%d rows/wg=%d key_tile=64 causal=%d",
-                    d, (Sk + 63) / 64, Hkv, B, d, pl.total_wgs, pl.hw, pl.rows_per_wg, causal);
-    }
-  }
-  if (e != hipSuccess) return ATTN_ERR_HIP;
-  record(text);
+  if (fwd_ws(p, dtype) > 0 && (workspace == nullptr || workspace_bytes < fwd_ws(p, dtype))) return ATTN_ERR_WORKSPACE;
+  char text[480], line[512];
+  if (fwd_launch(p, dtype, q, k, v, o, lse, workspace, (hipStream_t)stream, text, sizeof(text)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  std::snprintf(line, sizeof(line), "attn_fwd: %s", text);
+  record(line);
   return ATTN_OK;
 }
 
@@ -248,6 +291,98 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
                                              (hipStream_t)stream, text, sizeof(text));
   if (e != hipSuccess) return ATTN_ERR_HIP;
   record(text);
+  return ATTN_OK;
+}
+
+size_t attn_fwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                                       int Hkv, int d, int causal, int dtype) {
+  if (check_varlen(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, 1.f, dtype) != ATTN_OK) return 0;
+  size_t need = 0;
+  for (int b = 0; b < B; ++b) {
+    const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, 1.f);
+    if (p.Sq > 0) need = std::max(need, fwd_ws(p, dtype));
+  }
+  return need;
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int B, int Hq, int Hkv, int d, int causal, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_varlen(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const bool any_q = cu_seqlens_q[B] > 0, any_k = cu_seqlens_k[B] > 0;
+  if ((any_q && (q == nullptr || o == nullptr)) || (any_q && any_k && (k == nullptr || v == nullptr)))
+    return ATTN_ERR_NULL;
+  const size_t need = attn_fwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const size_t es = dtype == ATTN_F32 ? 4 : 2;
+  char text[512] = "";
+  int launched = 0;
+  for (int b = 0; b < B; ++b) {
+    const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, scale);
+    if (p.Sq == 0) continue;
+    const size_t q0 = (size_t)cu_seqlens_q[b], k0 = (size_t)cu_seqlens_k[b];
+    const char* kb = p.Sk > 0 ? (const char*)k + k0 * d * es : nullptr;
+    const char* vb = p.Sk > 0 ? (const char*)v + k0 * d * es : nullptr;
+    if (fwd_launch(p, dtype, (const char*)q + q0 * d * es, kb, vb, (char*)o + q0 * d * es,
+                   lse != nullptr ? lse + q0 : nullptr, workspace, (hipStream_t)stream, text, sizeof(text)) !=
+        hipSuccess)
+      return ATTN_ERR_HIP;
+    ++launched;
+  }
+  char summary[512];
+  std::snprintf(summary, sizeof(summary), "attn_fwd_varlen: %d sequences launched of %d; last: %s", launched, B,
+                text);
+  record(summary);
+  return ATTN_OK;
+}
+
+size_t attn_bwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                                       int Hkv, int d, int causal, int dtype) {
+  if (check_varlen(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, 1.f, dtype) != ATTN_OK) return 0;
+  if (dtype != ATTN_BF16) return 0;
+  size_t need = 0;
+  for (int b = 0; b < B; ++b) {
+    const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, 1.f);
+    if (p.Sq > 0 || p.Sk > 0) need = std::max(need, attn::bwd_workspace_bytes(p));
+  }
+  return need;
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int B, int Hq, int Hkv, int d, int causal, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_varlen(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  const bool any_q = cu_seqlens_q[B] > 0, any_k = cu_seqlens_k[B] > 0;
+  if ((any_q && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr)) ||
+      (any_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
+    return ATTN_ERR_NULL;
+  const size_t need = attn_bwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  char text[512] = "";
+  int launched = 0;
+  for (int b = 0; b < B; ++b) {
+    const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, scale);
+    if (p.Sq == 0 && p.Sk == 0) continue;
+    // a sequence with keys but no query still launches: its dK and dV rows are
+    // written as zeros (no query tile reaches them)
+    const size_t q0 = (size_t)cu_seqlens_q[b] * d * 2, k0 = (size_t)cu_seqlens_k[b] * d * 2;
+    const bool has_k = p.Sk > 0;
+    if (attn::launch_bwd_bf16(p, (const char*)q + q0, has_k ? (const char*)k + k0 : nullptr,
+                              has_k ? (const char*)v + k0 : nullptr, (const char*)o + q0,
+                              lse + cu_seqlens_q[b], (const char*)dout + q0, (char*)dq + q0,
+                              has_k ? (char*)dk + k0 : nullptr, has_k ? (char*)dv + k0 : nullptr, workspace,
+                              (hipStream_t)stream, text, sizeof(text)) != hipSuccess)
+      return ATTN_ERR_HIP;
+    ++launched;
+  }
+  char summary[512];
+  std::snprintf(summary, sizeof(summary), "attn_bwd_varlen: %d sequences launched of %d; last: %s", launched, B,
+                text);
+  record(summary);
   return ATTN_OK;
 }
 

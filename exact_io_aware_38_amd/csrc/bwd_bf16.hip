@@ -82,6 +82,7 @@ struct BwdArgs {
   bf16* dv;
   float* ld;      // [B, Hq, sqp / 32][64]: lse2 of 32 rows, then D of the same rows
   int B, Hq, Hkv, Sq, Sk, g, causal;
+  int hsq, hsk;   // head strides in rows (see Problem)
   int sqp;        // Sq rounded up to 64
   float scale;
   float c;        // scale * log2(e)
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const size_t head = prow / a.sqp;
   const int pos = (int)(prow % a.sqp);
   const bool valid = prow < rows && pos < a.Sq;
-  const size_t row = head * a.Sq + pos;
+  const size_t row = head * a.hsq + pos;
   float acc = 0.f;
   if (valid) {
     const bf16x8 ov = *(const bf16x8*)(a.o + row * D + c * 8);
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     // K and V fragments: B operands of S = Q K^T and dP = dO V^T (column = key)
     bf16x8 kf[DC], vf[DC];
     {
-      const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.Sk + (kvalid ? key : 0)) * D;
+      const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.hsk + (kvalid ? key : 0)) * D;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         if (kvalid) {
@@ -397,8 +398,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
     if (dhq != dh) {
       dh = dhq;
       const size_t h = (size_t)b * a.Hq + dhq;
-      rq = buffer_rsrc(a.q + h * a.Sq * D, (uint32_t)a.Sq * RB);
-      rd = buffer_rsrc(a.dout + h * a.Sq * D, (uint32_t)a.Sq * RB);
+      rq = buffer_rsrc(a.q + h * a.hsq * D, (uint32_t)a.Sq * RB);
+      rd = buffer_rsrc(a.dout + h * a.hsq * D, (uint32_t)a.Sq * RB);
       rl = buffer_rsrc(a.ld + h * (a.sqp / BT) * (2 * BT), (uint32_t)a.sqp * 8);
     }
     Dma o;
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!kvalid) return;
-  const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.Sk + key) * D;
+  const size_t kvrow = (((size_t)b * a.Hkv + hkv) * a.hsk + key) * D;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArg
     pos[cb] = p0 + 32 * cb + l32;
     valid[cb] = pos[cb] < a.Sq;
     lim[cb] = a.causal ? min(kend - 1, pos[cb] + off) : kend - 1;
-    const size_t qrow = hrow * a.Sq + (valid[cb] ? pos[cb] : 0);
+    const size_t qrow = hrow * a.hsq + (valid[cb] ? pos[cb] : 0);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       if (valid[cb]) {
@@ -619,8 +620,8 @@ __global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArg
   }
 
   const size_t kvh = (size_t)b * a.Hkv + hkv;
-  const bf16* kg = a.k + kvh * (size_t)a.Sk * D;
-  const bf16* vg = a.v + kvh * (size_t)a.Sk * D;
+  const bf16* kg = a.k + kvh * (size_t)a.hsk * D;
+  const bf16* vg = a.v + kvh * (size_t)a.hsk * D;
   uint32_t rb[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) rb[dc] = l32 * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
@@ -855,7 +856,7 @@ __global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArg
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     if (!valid[cb]) continue;
-    bf16* dst = a.dq + (hrow * a.Sq + pos[cb]) * D;
+    bf16* dst = a.dq + (hrow * a.hsq + pos[cb]) * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -947,6 +948,8 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   a.Hkv = p.Hkv;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
+  a.hsq = p.hsq;
+  a.hsk = p.hsk;
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
   a.sqp = (p.Sq + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;

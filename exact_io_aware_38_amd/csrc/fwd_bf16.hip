@@ -51,6 +51,7 @@ struct FwdArgs {
   float* part_o;     // split path: [nsplit, B, Hq, Sq, D]
   float* part_lse;   // split path: [nsplit, B, Hq, Sq]
   int B, Hq, Hkv, Sq, Sk, g, causal;
+  int hsq, hsk;      // head strides in rows (see Problem)
   float c;           // scale * log2(e)
   int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
   int nsplit, split_keys;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
 
   bf16x8 qf[DC];
   {
-    const bf16* qp = a.q + (((size_t)b * a.Hq + head) * a.Sq + (colv ? pos : 0)) * D;
+    const bf16* qp = a.q + (((size_t)b * a.Hq + head) * a.hsq + (colv ? pos : 0)) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
   }
-  const size_t kvh = ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
+  const size_t kvh = ((size_t)b * a.Hkv + hkv) * (size_t)a.hsk * D;
   const bf16* kg = a.k + kvh;
   const bf16* vg = a.v + kvh;
 
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse_v = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : kNegInf;
   if (!colv) return;
-  bf16* op = a.o + (((size_t)b * a.Hq + head) * a.Sq + pos) * D;
+  bf16* op = a.o + (((size_t)b * a.Hq + head) * a.hsq + pos) * D;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
       r[3] = (bf16)(acc[mb][4 * q4 + 3] * inv);
       *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi) = r;
     }
-  if (a.lse != nullptr && hi == 0) a.lse[((size_t)b * a.Hq + head) * a.Sq + pos] = lse_v;
+  if (a.lse != nullptr && hi == 0) a.lse[((size_t)b * a.Hq + head) * a.hsq + pos] = lse_v;
 }
 
 // ---------------------------------------------------------------------------
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
 
   bf16x8 qf[DC];
   {
-    const bf16* qp = a.q + (((size_t)b * a.Hq + hq) * a.Sq + pos) * D;
+    const bf16* qp = a.q + (((size_t)b * a.Hq + hq) * a.hsq + pos) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -408,8 +409,8 @@ __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
   // whole-head buffers: rows past Sk read zeros (their scores are masked or,
   // for V, multiplied by P = 0)
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.k + kvh * (size_t)a.Sk * D), (short)0, a.Sk * RB, 0x00020000);
-  const u32x4 rv = buffer_rsrc(a.v + kvh * (size_t)a.Sk * D, (uint32_t)a.Sk * RB);
+      (void*)(a.k + kvh * (size_t)a.hsk * D), (short)0, a.Sk * RB, 0x00020000);
+  const u32x4 rv = buffer_rsrc(a.v + kvh * (size_t)a.hsk * D, (uint32_t)a.Sk * RB);
   // K fragment dc of key row l32: byte l32*RB + 16*hi + 32*dc of the tile
   const uint32_t kl = l32 * RB + 16 * hi;
   // V DMA: lane of instruction n writes LDS chunk P = 64 n + lane of the tile,
@@ -549,9 +550,10 @@ template <int D>
 __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            bf16* __restrict__ o, float* __restrict__ lse,
-                                                           int nsplit, size_t rows) {
+                                                           int nsplit, size_t rows, int Sq, int hsq) {
   const size_t row = blockIdx.x;
   if (row >= rows) return;
+  const size_t orow = (row / Sq) * (size_t)hsq + row % Sq;   // (b, h, i) in the output's layout
   const int lane = threadIdx.x;
   float m = kNegInf;
   for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[(size_t)s * rows + row]);
@@ -574,8 +576,8 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) o[row * D + lane * PER + j] = (bf16)(accv[j] * inv);
-  if (lse != nullptr && lane == 0) lse[row] = tot > 0.f ? m + __logf(tot) : kNegInf;
+  for (int j = 0; j < PER; ++j) o[orow * D + lane * PER + j] = (bf16)(accv[j] * inv);
+  if (lse != nullptr && lane == 0) lse[orow] = tot > 0.f ? m + __logf(tot) : kNegInf;
 }
 
 template <int D>
@@ -596,7 +598,7 @@ hipError_t launch_split_d(const FwdArgs& a, int rows, hipStream_t s) {
   if (e != hipSuccess) return e;
   timing_begin(s, "combine_split");
   hipLaunchKernelGGL((combine_split_kernel<D>), dim3(rows), dim3(64), 0, s, a.part_o, a.part_lse,
-                     a.o, a.lse, a.nsplit, (size_t)rows);
+                     a.o, a.lse, a.nsplit, (size_t)rows, a.Sq, a.hsq);
   e = hipGetLastError();
   timing_end(s);
   return e;
@@ -614,6 +616,8 @@ FwdArgs base_args(const Problem& p, const void* q, const void* k, const void* v,
   a.Hkv = p.Hkv;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
+  a.hsq = p.hsq;
+  a.hsk = p.hsk;
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
   a.c = p.scale * kLog2e;

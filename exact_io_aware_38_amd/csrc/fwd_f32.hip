@@ -22,6 +22,7 @@ struct F32Args {
   float* lse;
   int Hq, Hkv, Sq, Sk, g, causal;
   float scale;
+  int hsq, hsk;      // head strides in rows (see Problem)
 };
 
 template <int D>
@@ -44,15 +45,15 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
   const int lim = a.causal ? min(kend - 1, row + off) : kend - 1;   // last visible key of this row
 
   float q[D], o[D];
-  const float* qp = a.q + (((size_t)b * a.Hq + hq) * a.Sq + (valid ? row : 0)) * D;
+  const float* qp = a.q + (((size_t)b * a.Hq + hq) * a.hsq + (valid ? row : 0)) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     q[c] = valid ? qp[c] : 0.f;
     o[c] = 0.f;
   }
   float m = kNegInf, l = 0.f;
-  const float* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
-  const float* vg = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.Sk * D;
+  const float* kg = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.hsk * D;
+  const float* vg = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.hsk * D;
 
   for (int key0 = 0; key0 < kend; key0 += BC) {
     __syncthreads();
@@ -89,17 +90,17 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
   }
   if (!valid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* op = a.o + (((size_t)b * a.Hq + hq) * a.Sq + row) * D;
+  float* op = a.o + (((size_t)b * a.Hq + hq) * a.hsq + row) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) op[c] = o[c] * inv;
-  if (a.lse != nullptr) a.lse[((size_t)b * a.Hq + hq) * a.Sq + row] = l > 0.f ? m + logf(l) : kNegInf;
+  if (a.lse != nullptr) a.lse[((size_t)b * a.Hq + hq) * a.hsq + row] = l > 0.f ? m + logf(l) : kNegInf;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v, float* o,
                           float* lse, hipStream_t s) {
-  F32Args a{q, k, v, o, lse, p.Hq, p.Hkv, p.Sq, p.Sk, p.Hq / p.Hkv, p.causal, p.scale};
+  F32Args a{q, k, v, o, lse, p.Hq, p.Hkv, p.Sq, p.Sk, p.Hq / p.Hkv, p.causal, p.scale, p.hsq, p.hsk};
   dim3 grid((p.Sq + 127) / 128, p.Hq, p.B);
   timing_begin(s, "fwd_f32");
   if (p.d == 64)

@@ -15,9 +15,15 @@ void timing_begin(hipStream_t s, const char* kernel);
 void timing_end(hipStream_t s);
 
 // Problem description shared by the launchers (already validated).
+// Row (b, h, i) of Q, O, dO, dQ and lse lives at packed row (b Hq + h) hsq + i,
+// row (b, h, j) of K, V, dK, dV at (b Hkv + h) hsk + j: hsq = Sq and hsk = Sk
+// for [B, H, S, d] tensors; a sequence inside head-major packed tensors
+// [H, total, d] (B = 1, data pointers advanced to the sequence's first row)
+// has the packed totals as head strides.
 struct Problem {
   int B, Hq, Hkv, Sq, Sk, d, causal;
   float scale;
+  int hsq, hsk;     // head strides in rows
 };
 
 // ---- forward, bf16 ----------------------------------------------------------

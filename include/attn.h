@@ -32,6 +32,7 @@
  * Restrictions (the kernels are specialised, as that page's limitations
  * section notes for high-performance attention kernels): d in {64, 128};
  * Hq a multiple of Hkv (grouped heads are contiguous); scale finite and > 0;
+ * Sq and Sk below 2^24 per head, B*Hq*Sq and B*Hkv*Sk below 2^31;
  * backward in ATTN_BF16 only; gfx950 only.
  *
  * Ownership and errors. The caller allocates every buffer, including the
@@ -57,7 +58,7 @@ extern "C" {
 enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,       /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = -2,      /* B, Hq, Hkv, Sq < 1, or Sk < 0, or a size overflows */
+  ATTN_ERR_SHAPE = -2,      /* B, Hq, Hkv, Sq < 1, or Sk < 0, or a size past its limit */
   ATTN_ERR_GQA = -3,        /* Hq is not a multiple of Hkv */
   ATTN_ERR_HEADDIM = -4,    /* d not in {64, 128} */
   ATTN_ERR_DTYPE = -5,      /* unknown dtype, or not supported by this entry point */
@@ -101,6 +102,39 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Packed variable-length batches ("ragged layout" of the second page,
+ * section on interface constraints, where a packed row number and a logical
+ * row number are distinct). B sequences of different lengths are stored
+ * head-major and back to back: q, o and dout/dq are [Hq, total_q, d], lse is
+ * [Hq, total_q], k, v and dk/dv are [Hkv, total_k, d], all contiguous, with
+ * total_q = cu_seqlens_q[B] and total_k = cu_seqlens_k[B]. Sequence b holds
+ * the packed query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of every head; cu_seqlens_q and
+ * cu_seqlens_k are HOST arrays of B+1 ints that start at 0 and never
+ * decrease (else ATTN_ERR_SHAPE). Within a sequence the mask uses the logical
+ * positions (query i, key j counted from the sequence's first row), exactly
+ * as attn_fwd/attn_bwd with Sq and Sk set to that sequence's lengths; rows
+ * never attend across sequences. A sequence without queries writes nothing
+ * in the forward and zero dk/dv rows in the backward; one without keys gives
+ * o = 0, lse = -inf, dq = 0. Every other argument means what it means for
+ * attn_fwd/attn_bwd (the per-sequence shape checks apply to each sequence;
+ * Hq * total_q and Hkv * total_k must stay below 2^31). The library launches
+ * the kernels once per non-empty sequence, in order, on the given stream, so
+ * one workspace of the size the query returns serves them all. */
+size_t attn_fwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                                       int Hq, int Hkv, int d, int causal, int dtype);
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int d, int causal, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+size_t attn_bwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                                       int Hq, int Hkv, int d, int causal, int dtype);
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int d, int causal, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* attn_strerror(int status);

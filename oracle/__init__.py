@@ -6,5 +6,5 @@ with the HIP kernels or their host library.
 """
 from .attention import (  # noqa: F401
     visible_mask, attention_forward, attention_backward, online_softmax_forward,
-    merge_states, FullyMaskedRowError,
+    merge_states, FullyMaskedRowError, attention_forward_varlen, attention_backward_varlen,
 )

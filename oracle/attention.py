@@ -37,6 +37,7 @@ import numpy as np
 __all__ = [
     "FullyMaskedRowError", "visible_mask", "attention_forward",
     "attention_backward", "online_softmax_forward", "merge_states",
+    "attention_forward_varlen", "attention_backward_varlen",
 ]
 
 
@@ -267,3 +268,78 @@ def merge_states(o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
     o[live] = (wa[live, None] * o_a[live] + wb[live, None] * o_b[live]) / tot[live, None]
     lse[live] = M[live] + np.log(tot[live])
     return o, lse
+
+
+def _offsets(cu, name: str) -> List[int]:
+    cu = [int(x) for x in cu]
+    if len(cu) < 2 or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError(f"{name} must start at 0 and never decrease, got {cu}")
+    return cu
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: int = 0,
+                             scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over a packed batch of sequences of different lengths.
+
+    q: [Hq, total_q, d]; k, v: [Hkv, total_k, d(v)], sequences back to back:
+    sequence b owns packed query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+    and packed key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
+
+    [P2] "接口与实现约束" asks a ragged layout to keep the logical row number
+    apart from the packed one. Reading taken: every sequence is its own
+    attention problem (no row sees a key of another sequence), and the causal
+    masks compare logical positions, i.e. the packed row minus the sequence's
+    first packed row. Each sequence is cut out and handed to
+    ``attention_forward``. A sequence without keys gets O = 0 and lse = -inf
+    (the defined mode for rows that see nothing). Returns (O [Hq, total_q,
+    dv], lse [Hq, total_q]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = _offsets(cu_seqlens_q, "cu_seqlens_q")
+    cu_k = _offsets(cu_seqlens_k, "cu_seqlens_k")
+    if len(cu_q) != len(cu_k) or cu_q[-1] != q.shape[1] or cu_k[-1] != k.shape[1]:
+        raise ValueError("offsets disagree with the packed tensors")
+    Hq, total_q, _ = q.shape
+    o = np.zeros((Hq, total_q, v.shape[-1]))
+    lse = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        qs = slice(cu_q[b], cu_q[b + 1])
+        ks = slice(cu_k[b], cu_k[b + 1])
+        ob, lb = attention_forward(q[None, :, qs], k[None, :, ks], v[None, :, ks],
+                                   causal=causal, scale=scale)
+        o[:, qs] = ob[0]
+        lse[:, qs] = lb[0]
+    return o, lse
+
+
+def attention_backward_varlen(q, k, v, do, cu_seqlens_q, cu_seqlens_k, *, causal: int = 0,
+                              scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Gradients of ``attention_forward_varlen``, sequence by sequence.
+
+    Same layout and reading as the forward: each sequence's dq, dk, dv come
+    from ``attention_backward`` on that sequence alone, and since no row sees
+    another sequence's keys, nothing crosses sequence boundaries. Key rows of
+    a sequence without queries get zero dk and dv.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cu_q = _offsets(cu_seqlens_q, "cu_seqlens_q")
+    cu_k = _offsets(cu_seqlens_k, "cu_seqlens_k")
+    if len(cu_q) != len(cu_k) or cu_q[-1] != q.shape[1] or cu_k[-1] != k.shape[1]:
+        raise ValueError("offsets disagree with the packed tensors")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(len(cu_q) - 1):
+        qs = slice(cu_q[b], cu_q[b + 1])
+        ks = slice(cu_k[b], cu_k[b + 1])
+        g = attention_backward(q[None, :, qs], k[None, :, ks], v[None, :, ks], do[None, :, qs],
+                               causal=causal, scale=scale)
+        dq[:, qs] = g["dq"][0]
+        dk[:, ks] = g["dk"][0]
+        dv[:, ks] = g["dv"][0]
+    return {"dq": dq, "dk": dk, "dv": dv}

@@ -16,6 +16,11 @@ Recipe (the same for every consumer):
   before the cast to the storage dtype, which pushes scores past ln(FLT_MAX);
 * bf16 storage is round-to-nearest-even of the fp32 draw, kept as raw uint16
   bit patterns. Consumers upcast those exact values.
+
+Packed variable-length batches (``VarlenWorkload``): the sequence lengths are
+drawn first, as integers uniform in [min_len, max_len] (query and key lengths
+equal unless the workload lists them), then q, k, v, dO as above but in the
+packed head-major shapes [H, total, d].
 """
 from __future__ import annotations
 
@@ -26,7 +31,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "bf16_bits_from_f32", "f32_from_bf16_bits",
-    "make_inputs", "to_f64", "get_workload",
+    "make_inputs", "to_f64", "get_workload", "VarlenWorkload", "VARLEN_WORKLOADS",
+    "varlen_lengths", "make_varlen_inputs", "cu_seqlens",
 ]
 
 
@@ -148,4 +154,75 @@ def make_inputs(w: Workload, *, backward: Optional[bool] = None) -> Dict[str, np
     out["q"] = _store(q, w.dtype)
     out["k"] = _store(k, w.dtype)
     out["v"] = _store(v, w.dtype)
+    return out
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of sequences of different lengths.
+
+    Either explicit ``lens_q``/``lens_k`` tuples, or ``B`` lengths drawn
+    uniformly in [min_len, max_len] (the same for queries and keys).
+    Tensors are packed head-major: q/o/dO ``[Hq, total_q, d]``, k/v
+    ``[Hkv, total_k, d]``.
+    """
+    name: str
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str
+    causal: int
+    seed: int
+    B: int = 0
+    min_len: int = 0
+    max_len: int = 0
+    lens_q: Optional[tuple] = None
+    lens_k: Optional[tuple] = None
+    backward: bool = False
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+VARLEN_WORKLOADS: Dict[str, VarlenWorkload] = {w.name: w for w in [
+    VarlenWorkload("varlen_mix_causal_d128", 32, 32, 128, "bf16", 1, seed=7, B=16, min_len=512,
+                   max_len=3584, backward=True,
+                   note="16 causal sequences of 512..3584 tokens (mean 2048) packed back to back"),
+]}
+
+
+def varlen_lengths(w: VarlenWorkload):
+    """(lens_q, lens_k) of a packed workload, as lists of ints."""
+    if w.lens_q is not None:
+        lk = w.lens_q if w.lens_k is None else w.lens_k
+        return list(w.lens_q), list(lk)
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    lens = rng.integers(w.min_len, w.max_len + 1, size=w.B).tolist()
+    return lens, list(lens)
+
+
+def cu_seqlens(lens):
+    """Offsets [0, l0, l0 + l1, ...] of packed sequences."""
+    out = [0]
+    for x in lens:
+        out.append(out[-1] + int(x))
+    return out
+
+
+def make_varlen_inputs(w: VarlenWorkload, *, backward: Optional[bool] = None) -> Dict[str, np.ndarray]:
+    """Packed q, k, v (and dO) plus ``cu_seqlens_q``/``cu_seqlens_k`` for a workload."""
+    want_do = w.backward if backward is None else backward
+    lq, lk = varlen_lengths(w)
+    tq, tk = sum(lq), sum(lk)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 1000003))
+    q = rng.standard_normal((w.Hq, tq, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.Hkv, tk, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.Hkv, tk, w.d), dtype=np.float32)
+    out = {"q": _store(q, w.dtype), "k": _store(k, w.dtype), "v": _store(v, w.dtype),
+           "cu_seqlens_q": np.asarray(cu_seqlens(lq), dtype=np.int64),
+           "cu_seqlens_k": np.asarray(cu_seqlens(lk), dtype=np.int64)}
+    if want_do:
+        out["do"] = _store(rng.standard_normal((w.Hq, tq, w.d), dtype=np.float32), w.dtype)
     return out

@@ -59,6 +59,7 @@ def _bwd(**over):
     ({"q": None}, -1), ({"k": None}, -1), ({"v": None}, -1), ({"o": None}, -1),
     ({"B": 0}, -2), ({"Hq": 0}, -2), ({"Hkv": 0}, -2), ({"Sq": 0}, -2), ({"Sk": -1}, -2),
     ({"B": 1 << 20, "Hq": 1 << 10, "Hkv": 1 << 10}, -2),
+    ({"Hq": 2, "Sk": 1 << 24}, -2), ({"Hq": 2, "Sq": 1 << 24}, -2),   # per-head byte ranges are 32-bit
     ({"Hq": 6, "Hkv": 4}, -3), ({"d": 96}, -4), ({"d": 256}, -4), ({"dtype": 7}, -5),
     ({"causal": 3}, -6), ({"causal": -1}, -6), ({"scale": 0.0}, -9), ({"scale": -1.0}, -9),
     ({"scale": float("nan")}, -9), ({"scale": float("inf")}, -9),
@@ -109,3 +110,81 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(attn, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         attn.lib()
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+def _ints(vals):
+    return None if vals is None else (ctypes.c_int * len(vals))(*vals)
+
+
+def _fwd_varlen(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cq=[0, 5, 12], ck=[0, 7, 7], B=2, Hq=4, Hkv=2,
+             d=64, causal=1, scale=0.125, dtype=attn.ATTN_BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return attn.lib().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], _ints(a["cq"]),
+                                      _ints(a["ck"]), a["B"], a["Hq"], a["Hkv"], a["d"], a["causal"],
+                                      a["scale"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _bwd_varlen(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             cq=[0, 5, 12], ck=[0, 7, 7], B=2, Hq=4, Hkv=2, d=64, causal=1, scale=0.125,
+             dtype=attn.ATTN_BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return attn.lib().attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                      a["dv"], _ints(a["cq"]), _ints(a["ck"]), a["B"], a["Hq"], a["Hkv"],
+                                      a["d"], a["causal"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"cq": None}, -1), ({"ck": None}, -1),
+    ({"q": None}, -1), ({"o": None}, -1), ({"k": None}, -1),
+    ({"B": 0, "cq": [0], "ck": [0]}, -2),
+    ({"cq": [1, 5, 12]}, -2), ({"ck": [0, 7, 3]}, -2),          # must start at 0 and never decrease
+    ({"cq": [0, 1 << 30, (1 << 30) + 2]}, -2),                 # Hq * total_q past 2^31
+    ({"Hq": 2, "ck": [0, 1 << 24, 1 << 24]}, -2),              # one sequence at the per-head limit
+    ({"Hq": 6, "Hkv": 4}, -3), ({"d": 96}, -4), ({"dtype": 3}, -5), ({"causal": 3}, -6),
+    ({"scale": 0.0}, -9),
+    ({"cq": [0, 1, 2], "ck": [0, 4096, 8192]}, -7),            # decode-shaped sequences need a workspace
+])
+def test_fwd_varlen_validation(over, code):
+    assert _fwd_varlen(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"cq": None}, -1), ({"lse": None}, -1), ({"dq": None}, -1), ({"dk": None}, -1),
+    ({"cq": [0, 5, 4]}, -2), ({"Hq": 3, "Hkv": 2}, -3), ({"d": 32}, -4),
+    ({"dtype": attn.ATTN_F32}, -5), ({"causal": -1}, -6), ({"scale": float("nan")}, -9),
+    ({}, -7), ({"ws": FAKE, "ws_bytes": 8}, -7),
+])
+def test_bwd_varlen_validation(over, code):
+    assert _bwd_varlen(**over) == code
+
+
+def test_varlen_with_only_empty_sequences_launches_nothing():
+    # every sequence empty: nothing to read or write, so NULL tensors are fine
+    none = dict(q=None, k=None, v=None, o=None, lse=None, cq=[0, 0, 0], ck=[0, 0, 0])
+    assert _fwd_varlen(**none) == 0
+    assert attn.last_dispatch().startswith("attn_fwd_varlen: 0 sequences launched of 2")
+    assert _bwd_varlen(do=None, dq=None, dk=None, dv=None, **none) == 0
+    assert attn.last_dispatch().startswith("attn_bwd_varlen: 0 sequences launched of 2")
+    # queries without keys still need q and o
+    assert _fwd_varlen(q=None, cq=[0, 3, 3], ck=[0, 0, 0]) == -1
+
+
+def test_varlen_workspace_queries():
+    bf = attn.ATTN_BF16
+    cq, ck = [0, 1, 2, 3], [0, 32768, 40000, 72768]
+    n = attn.fwd_varlen_workspace_bytes(cq, ck, 32, 8, 128, 0, bf)
+    assert n == max(attn.fwd_workspace_bytes(1, 32, 8, 1, s, 128, 0, bf) for s in (32768, 7232, 32768))
+    assert n > 0
+    assert attn.fwd_varlen_workspace_bytes([0, 100, 300], [0, 100, 300], 4, 4, 64, 1, bf) == 0
+    lens = [100, 0, 2000]
+    cu = [0, 100, 100, 2100]
+    nb = attn.bwd_varlen_workspace_bytes(cu, cu, 8, 2, 128, 1, bf)
+    assert nb == max(attn.bwd_workspace_bytes(1, 8, 2, s, s, 128, 1, bf) for s in lens if s)
+    assert attn.bwd_varlen_workspace_bytes(cu, cu, 8, 2, 128, 1, attn.ATTN_F32) == 0
+    assert attn.fwd_varlen_workspace_bytes([0, 5, 3], [0, 5, 6], 1, 1, 64, 0, bf) == 0   # invalid -> 0
+    with pytest.raises(ValueError):
+        attn.fwd_varlen_workspace_bytes([0, 5], [0, 5, 6], 1, 1, 64, 0, bf)

@@ -9,8 +9,9 @@ import pytest
 import torch
 
 import oracle
-from oracle import (FullyMaskedRowError, attention_backward, attention_forward,
-                    merge_states, online_softmax_forward, visible_mask)
+from oracle import (FullyMaskedRowError, attention_backward, attention_backward_varlen,
+                    attention_forward, attention_forward_varlen, merge_states,
+                    online_softmax_forward, visible_mask)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -333,3 +334,142 @@ def test_keys_no_query_sees_get_zero_gradient():
     q, k, v = _rand(rng, 1, 2, 2, 5, 9, 4)          # causal=1: keys 5..8 are never visible
     gr = attention_backward(q, k, v, rng.standard_normal(q.shape), causal=1)
     assert (gr["dk"][:, :, 5:] == 0).all() and (gr["dv"][:, :, 5:] == 0).all()
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+VARLEN_LENS = {   # (query lengths, key lengths) per causal mode; zero-length sequences included
+    0: ((5, 0, 7, 3), (6, 4, 7, 2)),
+    1: ((5, 0, 7, 3), (6, 4, 7, 2)),
+    2: ((5, 0, 7, 3), (3, 4, 9, 2)),      # sequence 0 has query rows that see no key
+}
+
+
+def _cu(lens):
+    return [0] + list(np.cumsum(lens))
+
+
+def _packed(rng, Hq, Hkv, lq, lk, d):
+    tq, tk = sum(lq), sum(lk)
+    return (rng.standard_normal((Hq, tq, d)), rng.standard_normal((Hkv, tk, d)),
+            rng.standard_normal((Hkv, tk, d)))
+
+
+def _block_diagonal_mask(lq, lk, causal):
+    """[total_q, total_k] visibility from packed row numbers: a row sees a key
+    of its own sequence only, and the causal rule compares logical positions
+    (packed number minus the sequence's first packed row)."""
+    cq, ck = _cu(lq), _cu(lk)
+    r = np.arange(cq[-1])
+    c = np.arange(ck[-1])
+    sr = np.searchsorted(cq, r, side="right") - 1        # sequence of each query row
+    sc = np.searchsorted(ck, c, side="right") - 1        # sequence of each key row
+    same = sr[:, None] == sc[None, :]
+    i = (r - np.asarray(cq)[sr])[:, None]
+    j = (c - np.asarray(ck)[sc])[None, :]
+    Sq = np.asarray(lq)[sr][:, None]
+    Sk = np.asarray(lk)[sr][:, None]
+    if causal == 0:
+        rule = np.ones_like(same)
+    elif causal == 1:
+        rule = j <= i
+    else:
+        rule = j <= i + (Sk - Sq)
+    return same & rule
+
+
+@pytest.mark.parametrize("causal", [0, 1, 2])
+def test_varlen_matches_block_diagonal_softmax(causal):
+    # one masked softmax over the whole packed matrix, by torch in fp64
+    rng = np.random.default_rng(22 + causal)
+    lq, lk = VARLEN_LENS[causal]
+    q, k, v = _packed(rng, 4, 2, lq, lk, 6)
+    o, lse = attention_forward_varlen(q, k, v, _cu(lq), _cu(lk), causal=causal, scale=0.4)
+    mask = torch.from_numpy(_block_diagonal_mask(lq, lk, causal))
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    kk, vv = tk.repeat_interleave(2, dim=0), tv.repeat_interleave(2, dim=0)
+    s = (0.4 * tq @ kk.transpose(-1, -2)).masked_fill(~mask, float("-inf"))
+    p = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0)
+    assert np.abs(o - (p @ vv).numpy()).max() < 1e-12
+    ref_lse = torch.logsumexp(s, dim=-1).numpy()
+    assert np.array_equal(np.isinf(lse), np.isinf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    assert np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
+    if causal == 2:
+        assert np.isinf(lse[:, :2]).all() and (o[:, :2] == 0).all()   # 5 queries, 3 keys
+
+
+def test_varlen_equal_lengths_equal_dense_batch():
+    rng = np.random.default_rng(25)
+    B, Hq, Hkv, Sq, Sk, d = 3, 4, 2, 6, 9, 5
+    q, k, v = _rand(rng, B, Hq, Hkv, Sq, Sk, d)
+    do = rng.standard_normal(q.shape)
+    pack = lambda x: x.transpose(1, 0, 2, 3).reshape(x.shape[1], -1, x.shape[3])
+    cq, ck = _cu([Sq] * B), _cu([Sk] * B)
+    for causal in (0, 1, 2):
+        o, lse = attention_forward(q, k, v, causal=causal)
+        ov, lv = attention_forward_varlen(pack(q), pack(k), pack(v), cq, ck, causal=causal)
+        assert np.abs(ov - pack(o)).max() < 1e-14
+        assert np.abs(lv - lse.transpose(1, 0, 2).reshape(Hq, -1)).max() < 1e-14
+        g = attention_backward(q, k, v, do, causal=causal)
+        gv = attention_backward_varlen(pack(q), pack(k), pack(v), pack(do), cq, ck, causal=causal)
+        for n in ("dq", "dk", "dv"):
+            assert np.abs(gv[n] - pack(g[n])).max() < 1e-13, n
+
+
+def test_varlen_empty_sequences():
+    rng = np.random.default_rng(26)
+    lq, lk = (3, 0, 2), (0, 4, 5)
+    q, k, v = _packed(rng, 2, 1, lq, lk, 4)
+    o, lse = attention_forward_varlen(q, k, v, _cu(lq), _cu(lk), causal=1)
+    assert (o[:, :3] == 0).all() and np.isneginf(lse[:, :3]).all()      # no keys
+    g = attention_backward_varlen(q, k, v, rng.standard_normal(q.shape), _cu(lq), _cu(lk), causal=1)
+    assert (g["dq"][:, :3] == 0).all()
+    assert (g["dk"][:, :4] == 0).all() and (g["dv"][:, :4] == 0).all()  # no queries
+    assert np.abs(g["dk"][:, 4:]).max() > 0
+    with pytest.raises(ValueError):
+        attention_forward_varlen(q, k, v, [0, 3, 2, 5], _cu(lk))
+    with pytest.raises(ValueError):
+        attention_forward_varlen(q, k, v, [1, 3, 3, 5], _cu(lk))
+
+
+def _varlen_loss(q, k, v, cq, ck, causal):
+    o, _ = attention_forward_varlen(q, k, v, cq, ck, causal=causal, scale=0.7)
+    return 0.5 * float((o ** 2).sum()), o
+
+
+@pytest.mark.parametrize("causal", [1, 2])
+def test_varlen_central_differences(causal):
+    rng = np.random.default_rng(27 + causal)
+    lq, lk = (2, 0, 3), (3, 2, 1)
+    cq, ck = _cu(lq), _cu(lk)
+    q, k, v = _packed(rng, 2, 1, lq, lk, 2)
+    _, o = _varlen_loss(q, k, v, cq, ck, causal)
+    gr = attention_backward_varlen(q, k, v, o, cq, ck, causal=causal, scale=0.7)
+    h = 1e-6
+    worst = 0.0
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap = {"dq": (xp, k, v), "dk": (q, xp, v), "dv": (q, k, xp)}[name]
+            am = {"dq": (xm, k, v), "dk": (q, xm, v), "dv": (q, k, xm)}[name]
+            num = (_varlen_loss(*ap, cq, ck, causal)[0] - _varlen_loss(*am, cq, ck, causal)[0]) / (2 * h)
+            worst = max(worst, abs(num - gr[name][idx]))
+    assert worst <= 1e-8, worst
+    assert (gr["dk"][:, 3:5] == 0).all()                 # the keys of the sequence without queries
+
+
+def test_varlen_backward_matches_autograd_block_diagonal():
+    rng = np.random.default_rng(30)
+    lq, lk = (4, 6, 1), (5, 6, 3)
+    q, k, v = _packed(rng, 4, 2, lq, lk, 3)
+    do = rng.standard_normal(q.shape)
+    gr = attention_backward_varlen(q, k, v, do, _cu(lq), _cu(lk), causal=1, scale=0.5)
+    mask = torch.from_numpy(_block_diagonal_mask(lq, lk, 1))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    kk, vv = tk.repeat_interleave(2, dim=0), tv.repeat_interleave(2, dim=0)
+    s = (0.5 * tq @ kk.transpose(-1, -2)).masked_fill(~mask, float("-inf"))
+    (torch.softmax(s, dim=-1) @ vv).backward(torch.from_numpy(do))
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert np.abs(gr[name] - t.grad.numpy()).max() < 1e-12, name

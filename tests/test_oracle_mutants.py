@@ -30,6 +30,14 @@ MUTANTS = {
     "backward_dq_missing_scale": ("dq[b, h] = c * (ds @ k[b, hk])", "dq[b, h] = ds @ k[b, hk]"),
     "backward_dk_transposed_operand": ("dk[b, hk] += c * (ds.T @ q[b, h])", "dk[b, hk] += c * (p.T @ q[b, h])"),
     "backward_dv_drops_probabilities": ("dv[b, hk] += p.T @ do[b, h]", "dv[b, hk] += vis.T @ do[b, h]"),
+    "varlen_keys_cut_at_query_offsets": ("        ks = slice(cu_k[b], cu_k[b + 1])\n        ob, lb",
+                                         "        ks = slice(cu_q[b], cu_q[b + 1])\n        ob, lb"),
+    "varlen_mask_on_packed_rows": ("causal=causal, scale=scale)\n        o[:, qs] = ob[0]",
+                                   "causal=causal, scale=scale, rows=list(range(qs.start, qs.stop)),\n"
+                                   "                                   Sq=cu_q[-1])\n        o[:, qs] = ob[0]"),
+    "varlen_backward_dk_overwritten_by_dv": ('        dk[:, ks] = g["dk"][0]', '        dk[:, ks] = g["dv"][0]'),
+    "varlen_backward_keys_cut_at_query_offsets": ("        ks = slice(cu_k[b], cu_k[b + 1])\n        g = attention_backward",
+                                                  "        ks = slice(cu_q[b], cu_q[b + 1])\n        g = attention_backward"),
     "merge_wrong_weight": ("wb[live] = np.exp(lse_b[live] - M[live])", "wb[live] = np.exp(lse_a[live] - M[live])"),
 }
 
@@ -46,10 +54,15 @@ PIN_CALLS = [
     (pins.test_merge_states_equals_single_pass, {}),
     (pins.test_central_differences_masked_2x3x2, {}),
     (pins.test_backward_matches_torch_autograd_fp64, {"causal": 1, "shape": (2, 4, 2, 5, 9, 8)}),
+    (pins.test_varlen_matches_block_diagonal_softmax, {"causal": 1}),
+    (pins.test_varlen_matches_block_diagonal_softmax, {"causal": 2}),
+    (pins.test_varlen_central_differences, {"causal": 2}),
+    (pins.test_varlen_backward_matches_autograd_block_diagonal, {}),
 ]
 
 _NAMES = ["attention_forward", "attention_backward", "online_softmax_forward",
-          "merge_states", "visible_mask", "FullyMaskedRowError"]
+          "merge_states", "visible_mask", "FullyMaskedRowError", "attention_forward_varlen",
+          "attention_backward_varlen"]
 
 
 def _mutant_module(old, new):
