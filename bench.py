@@ -5,8 +5,10 @@ One step is one pass of the whole training path over one batch of synthetic
 input: attn_fwd then attn_bwd on B=1, H=32, S=8192, d=128, causal, bf16 (the
 training workload). The same run also times the long-context causal forward
 (B=2, H=32, S=8192, d=128, 1% of query rows x30) and the grouped-query decode
-(B=16, Hq=32, Hkv=8, one query row against 32768 keys), which report as their
-own sub-objects. Inputs are resident in device memory before timing starts.
+(B=16, Hq=32, Hkv=8, one query row against 32768 keys) and a packed batch of
+16 causal sequences of 512..3584 tokens (forward + backward through the
+variable-length entry points), which report as their own sub-objects. Inputs
+are resident in device memory before timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration          (a plain copy of known size,
@@ -143,7 +145,9 @@ def _fwd_workspace(attn, w):
     return torch.empty(max(1, n), dtype=torch.uint8, device="cuda")
 
 
-def _time(fn, steps: int, warmup: int, attn):
+def _time(fn, steps: int, warmup: int, attn, per_step: bool = False):
+    """Mean ms per step from events around the timed loop, and each kernel's
+    device time: mean per launch, or (per_step) summed over a step."""
     import torch
     for _ in range(warmup):
         fn()
@@ -158,6 +162,8 @@ def _time(fn, steps: int, warmup: int, attn):
     torch.cuda.synchronize()
     kern = attn.timing_stop()
     ms = start.elapsed_time(end) / steps
+    if per_step:
+        return ms, {k: v[1] / steps for k, v in kern.items()}
     return ms, {k: v[1] / v[0] for k, v in kern.items()}
 
 
@@ -221,6 +227,42 @@ def bench_decode(attn, steps, warmup):
             "frac_of_peak": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
             "roofline": roofline("fwd_split_bf16", w, kern["fwd_split_bf16"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
+
+
+def bench_varlen(attn, steps, warmup):
+    """Forward + backward over a packed batch of causal sequences of mixed
+    lengths, credited with the same nominal work as the dense step, summed
+    over the sequences."""
+    import numpy as np
+    import torch
+    import synth
+    w = synth.VARLEN_WORKLOADS["varlen_mix_causal_d128"]
+    x = synth.make_varlen_inputs(w)
+    t = {n: torch.from_numpy(x[n].view(np.int16)).cuda().view(torch.bfloat16) for n in ("q", "k", "v", "do")}
+    cq, ck = x["cu_seqlens_q"].tolist(), x["cu_seqlens_k"].tolist()
+    del x
+    lens = [b - a for a, b in zip(cq, cq[1:])]
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(w.Hq, cq[-1], dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    nb = attn.bwd_varlen_workspace_bytes(cq, ck, w.Hq, w.Hkv, w.d, w.causal, attn.ATTN_BF16)
+    nf = attn.fwd_varlen_workspace_bytes(cq, ck, w.Hq, w.Hkv, w.d, w.causal, attn.ATTN_BF16)
+    ws = torch.empty(max(1, nb, nf), dtype=torch.uint8, device="cuda")
+
+    def step():
+        attn.fwd_varlen(t["q"], t["k"], t["v"], cq, ck, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                        workspace=ws)
+        attn.bwd_varlen(t["q"], t["k"], t["v"], o, lse, t["do"], cq, ck, causal=w.causal, scale=w.scale,
+                        dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms, kern = _time(step, steps, warmup, attn, per_step=True)
+    total = sum(3.5 * nominal_fwd_flops(1, w.Hq, n, n, w.d, w.causal) for n in lens)
+    return {"workload": w.name, "sequences": len(lens), "total_tokens": cq[-1], "min_len": min(lens),
+            "max_len": max(lens), "H": w.Hq, "d": w.d, "causal": w.causal,
+            "step": "attn_fwd_varlen + attn_bwd_varlen", "ms": round(ms, 4),
+            "tokens_per_s": round(cq[-1] / ms * 1e3, 1), "tflops": round(total / ms / 1e9, 2),
+            "frac_of_peak": round(total / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "kernels_ms_per_step": {k: round(v, 4) for k, v in kern.items()}}
 
 
 def cpu_baseline(w, heads: int = 4) -> dict:
@@ -337,7 +379,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "fwd", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen"], default="all")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5,
                     metavar=("WORKLOAD", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -386,6 +428,13 @@ def main() -> int:
         result["decode"] = bench_decode(attn, max(args.steps, 20), args.warmup)
         print(f"# decode: {result['decode']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+    if args.only in ("all", "varlen"):
+        result["varlen"] = bench_varlen(attn, args.steps, args.warmup)
+        print(f"# varlen: {result['varlen']['ms']} ms", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if args.only == "varlen":
+        result.update({"value": result["varlen"]["tflops"], "ms_per_step": result["varlen"]["ms"],
+                       "config": {"workload": result["varlen"]["workload"]}, "roofline": None})
     if args.only == "fwd":
         result.update({"value": result["fwd"]["tflops"], "ms_per_step": result["fwd"]["ms"],
                        "config": {"workload": result["fwd"]["workload"]}, "roofline": result["fwd"]["roofline"]})
