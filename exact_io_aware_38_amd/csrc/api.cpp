@@ -114,6 +114,31 @@ attn::Problem seq_problem(const int* cu_q, const int* cu_k, int B, int b, int Hq
   return p;
 }
 
+// The whole packed batch as the launchers see it: batch 1, the packed totals
+// as head strides (lengths come per sequence).
+attn::Problem packed_problem(const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int d, int causal,
+                             float scale) {
+  attn::Problem p = make_problem(1, Hq, Hkv, 0, 0, d, causal, scale);
+  p.hsq = cu_q[B];
+  p.hsk = cu_k[B];
+  return p;
+}
+
+// The sequences that `keep` selects, most work first, so that each packed
+// launch starts its largest tiles first.
+template <typename Keep>
+std::vector<attn::SeqSpan> packed_order(const int* cu_q, const int* cu_k, int B, Keep keep) {
+  std::vector<attn::SeqSpan> v;
+  for (int b = 0; b < B; ++b) {
+    const attn::SeqSpan sp{cu_q[b], cu_k[b], cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]};
+    if (keep(sp)) v.push_back(sp);
+  }
+  std::stable_sort(v.begin(), v.end(), [](const attn::SeqSpan& a, const attn::SeqSpan& b) {
+    return (long long)(a.sq + 1) * (a.sk + 1) > (long long)(b.sq + 1) * (b.sk + 1);
+  });
+  return v;
+}
+
 size_t fwd_ws(const attn::Problem& p, int dtype) {
   if (dtype != ATTN_BF16) return 0;
   const attn::SplitPlan sp = attn::plan_split(p);
@@ -297,7 +322,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 size_t attn_fwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
                                        int Hkv, int d, int causal, int dtype) {
   if (check_varlen(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, 1.f, dtype) != ATTN_OK) return 0;
-  size_t need = 0;
+  size_t need = 0;       // only the sequences launched one by one on the split path use it
   for (int b = 0; b < B; ++b) {
     const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, 1.f);
     if (p.Sq > 0) need = std::max(need, fwd_ws(p, dtype));
@@ -315,24 +340,45 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
     return ATTN_ERR_NULL;
   const size_t need = attn_fwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
   const size_t es = dtype == ATTN_F32 ? 4 : 2;
   char text[512] = "";
-  int launched = 0;
+  int single = 0, packed = 0, launches = 0;
+  // fp32, and decode-shaped bf16 sequences (split over the keys), one launch each
   for (int b = 0; b < B; ++b) {
     const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, scale);
-    if (p.Sq == 0) continue;
+    if (p.Sq == 0 || (dtype == ATTN_BF16 && !attn::plan_split(p).use)) continue;
     const size_t q0 = (size_t)cu_seqlens_q[b], k0 = (size_t)cu_seqlens_k[b];
     const char* kb = p.Sk > 0 ? (const char*)k + k0 * d * es : nullptr;
     const char* vb = p.Sk > 0 ? (const char*)v + k0 * d * es : nullptr;
     if (fwd_launch(p, dtype, (const char*)q + q0 * d * es, kb, vb, (char*)o + q0 * d * es,
-                   lse != nullptr ? lse + q0 : nullptr, workspace, (hipStream_t)stream, text, sizeof(text)) !=
-        hipSuccess)
+                   lse != nullptr ? lse + q0 : nullptr, workspace, s, text, sizeof(text)) != hipSuccess)
       return ATTN_ERR_HIP;
-    ++launched;
+    ++single;
+  }
+  // every other bf16 sequence: tiled prefill, up to SEQ_MAX sequences per launch
+  if (dtype == ATTN_BF16) {
+    const attn::Problem pp = packed_problem(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, scale);
+    const std::vector<attn::SeqSpan> seqs =
+        packed_order(cu_seqlens_q, cu_seqlens_k, B, [&](const attn::SeqSpan& sp) {
+          attn::Problem p1 = pp;
+          p1.Sq = sp.sq;
+          p1.Sk = sp.sk;
+          return sp.sq > 0 && !attn::plan_split(p1).use;
+        });
+    for (size_t i = 0; i < seqs.size(); i += attn::SEQ_MAX) {
+      const int n = (int)std::min<size_t>(attn::SEQ_MAX, seqs.size() - i);
+      if (attn::launch_fwd_prefill_bf16_packed(pp, seqs.data() + i, n, q, k, v, o, lse, s, text, sizeof(text)) !=
+          hipSuccess)
+        return ATTN_ERR_HIP;
+      packed += n;
+      ++launches;
+    }
   }
   char summary[512];
-  std::snprintf(summary, sizeof(summary), "attn_fwd_varlen: %d sequences launched of %d; last: %s", launched, B,
-                text);
+  std::snprintf(summary, sizeof(summary),
+                "attn_fwd_varlen: %d sequences of %d launched: %d in %d packed launches, %d one by one; last: %s",
+                single + packed, B, packed, launches, single, text);
   record(summary);
   return ATTN_OK;
 }
@@ -341,12 +387,11 @@ size_t attn_bwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_se
                                        int Hkv, int d, int causal, int dtype) {
   if (check_varlen(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, 1.f, dtype) != ATTN_OK) return 0;
   if (dtype != ATTN_BF16) return 0;
-  size_t need = 0;
-  for (int b = 0; b < B; ++b) {
-    const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, 1.f);
-    if (p.Sq > 0 || p.Sk > 0) need = std::max(need, attn::bwd_workspace_bytes(p));
-  }
-  return need;
+  // the lse2/D blocks of every sequence (each packed launch reuses the start of it)
+  const attn::Problem pp = packed_problem(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, 1.f);
+  const std::vector<attn::SeqSpan> seqs =
+      packed_order(cu_seqlens_q, cu_seqlens_k, B, [](const attn::SeqSpan& sp) { return sp.sq > 0; });
+  return attn::bwd_packed_workspace_bytes(pp, seqs.data(), (int)seqs.size());
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -362,28 +407,24 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
     return ATTN_ERR_NULL;
   const size_t need = attn_bwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  // a sequence with keys but no query still takes part: its dK and dV rows
+  // are written as zeros (no query tile reaches them)
+  const attn::Problem pp = packed_problem(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, scale);
+  const std::vector<attn::SeqSpan> seqs = packed_order(
+      cu_seqlens_q, cu_seqlens_k, B, [](const attn::SeqSpan& sp) { return sp.sq > 0 || sp.sk > 0; });
   char text[512] = "";
-  int launched = 0;
-  for (int b = 0; b < B; ++b) {
-    const attn::Problem p = seq_problem(cu_seqlens_q, cu_seqlens_k, B, b, Hq, Hkv, d, causal, scale);
-    if (p.Sq == 0 && p.Sk == 0) continue;
-    // a sequence with keys but no query still launches: its dK and dV rows are
-    // written as zeros (no query tile reaches them)
-    const size_t q0 = (size_t)cu_seqlens_q[b] * d * 2, k0 = (size_t)cu_seqlens_k[b] * d * 2;
-    const bool has_k = p.Sk > 0;
-    if (attn::launch_bwd_bf16(p, (const char*)q + q0, has_k ? (const char*)k + k0 : nullptr,
-                              has_k ? (const char*)v + k0 : nullptr, (const char*)o + q0,
-                              lse + cu_seqlens_q[b], (const char*)dout + q0, (char*)dq + q0,
-                              has_k ? (char*)dk + k0 : nullptr, has_k ? (char*)dv + k0 : nullptr, workspace,
-                              (hipStream_t)stream, text, sizeof(text)) != hipSuccess)
+  int launches = 0;
+  for (size_t i = 0; i < seqs.size(); i += attn::SEQ_MAX) {
+    const int n = (int)std::min<size_t>(attn::SEQ_MAX, seqs.size() - i);
+    if (attn::launch_bwd_bf16_packed(pp, seqs.data() + i, n, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                     (hipStream_t)stream, text, sizeof(text)) != hipSuccess)
       return ATTN_ERR_HIP;
-    ++launched;
+    ++launches;
   }
   char summary[512];
-  std::snprintf(summary, sizeof(summary), "attn_bwd_varlen: %d sequences launched of %d; last: %s", launched, B,
-                text);
+  std::snprintf(summary, sizeof(summary), "attn_bwd_varlen: %d sequences of %d launched in %d packed launches; last: %s",
+                (int)seqs.size(), B, launches, text);
   record(summary);
   return ATTN_OK;
 }
-
 }  // extern "C"

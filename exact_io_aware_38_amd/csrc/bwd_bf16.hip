@@ -110,12 +110,43 @@ __device__ __forceinline__ void wg_coords(int total, int tiles, int& tile, int& 
   head = W / tiles;
 }
 
+// Sequence s of a packed launch as a problem of batch 1: lengths, data
+// pointers and its lse2/D block from the table (the head strides stay the
+// packed totals).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+__device__ __forceinline__ void rebase(BwdArgs& a, const SeqTable& T, int s) {
+  a.Sq = T.sq[s];
+  a.Sk = T.sk[s];
+  a.sqp = (a.Sq + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
+  a.n_ktiles = (a.Sk + KV_WG - 1) / KV_WG;
+  a.n_qtiles = (a.Sq + Q_WG - 1) / Q_WG;
+  const size_t qo = (size_t)T.q0[s] * D, ko = (size_t)T.k0[s] * D;
+  a.q += qo;
+  a.o += qo;
+  a.dout += qo;
+  a.dq += qo;
+  a.lse += T.q0[s];
+  a.k += ko;
+  a.v += ko;
+  a.dk += ko;
+  a.dv += ko;
+  a.ld += (size_t)T.aux[s] * a.Hq * 2;         // aux: padded query rows of the earlier sequences
+}
+
+// Tab (here and in the two gradient kernels): NoTable for one dense problem,
+// SeqTable for a packed launch.
+template <int D, typename Tab>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
   constexpr int LPR = D / 8;       // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;   // rows per block
+  size_t blk = blockIdx.x;
+  if constexpr (std::is_same_v<Tab, SeqTable>) {
+    const SeqCoord sc = seq_coord(T);
+    rebase<D>(a, T, sc.seq);
+    blk = sc.t;
+  }
   const size_t rows = (size_t)a.B * a.Hq * a.sqp;
-  const size_t prow = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;   // padded row
+  const size_t prow = blk * RPB + threadIdx.x / LPR;   // padded row
   const int c = threadIdx.x % LPR;
   const size_t head = prow / a.sqp;
   const int pos = (int)(prow % a.sqp);
@@ -163,8 +194,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // step t-1, read in steps t and t+1) with its lse2/D blocks, and a 2-slot
 // exchange buffer of P and dS fragments (written in step t, read in step t+1).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
+template <int D, bool CAUSAL, typename Tab>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
   constexpr int CPR = D / 8;                    // 16-byte chunks per row
@@ -189,12 +220,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
   const bool grad = wid >= 4;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
 
-  int kt, bh;
-  wg_coords(a.total_kv, a.n_ktiles, kt, bh);
-  const int hkv = bh % a.Hkv;
-  const int b = bh / a.Hkv;
+  int kt, hkv, b;
+  if constexpr (std::is_same_v<Tab, SeqTable>) {
+    const SeqCoord sc = seq_coord(T);
+    rebase<D>(a, T, sc.seq);
+    kt = sc.t;
+    hkv = sc.unit;
+    b = 0;
+  } else {
+    int bh;
+    wg_coords(a.total_kv, a.n_ktiles, kt, bh);
+    hkv = bh % a.Hkv;
+    b = bh / a.Hkv;
+  }
+  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
   const int k0 = kt * KV_WG;
   const int key = k0 + 32 * kb + l32;
   const bool kvalid = key < a.Sk;
@@ -545,8 +585,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a) {
 // [K | V] row tiles: key tile t is loaded at the start of step t-2 and read in
 // steps t-1 (K, V) and t+1 (K^T).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+template <int D, bool CAUSAL, typename Tab>
+__global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a, Tab T) {
   constexpr int NCB = DQ_NCB;
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
@@ -565,13 +605,22 @@ __global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArg
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
 
-  int qtile, bh;
-  wg_coords(a.total_q, a.n_qtiles, qtile, bh);
+  int qtile, hq, b;
+  if constexpr (std::is_same_v<Tab, SeqTable>) {
+    const SeqCoord sc = seq_coord(T);
+    rebase<D>(a, T, sc.seq);
+    qtile = sc.t;
+    hq = sc.unit;
+    b = 0;
+  } else {
+    int bh;
+    wg_coords(a.total_q, a.n_qtiles, qtile, bh);
+    hq = bh % a.Hq;
+    b = bh / a.Hq;
+  }
+  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
   const int qb = a.n_qtiles - 1 - qtile;        // longest causal tiles first
-  const int hq = bh % a.Hq;
-  const int b = bh / a.Hq;
   const int hkv = hq / a.g;
   const int p0 = qb * Q_WG + 32 * NCB * wid;    // first query of the wavefront
   const int wg_last = min(qb * Q_WG + Q_WG, a.Sq) - 1;
@@ -890,7 +939,8 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   hipError_t e = hipSuccess;
   if (rows > 0) {
     timing_begin(s, "bwd_pre");
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, NoTable>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
+                       a, NoTable{});
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -898,9 +948,9 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   if (a.total_kv > 0) {
     timing_begin(s, "bwd_dkdv");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(a.total_kv), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, NoTable>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(a.total_kv), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, NoTable>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -908,9 +958,9 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   if (a.total_q > 0) {
     timing_begin(s, "bwd_dq");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(a.total_q), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, NoTable>), dim3(a.total_q), dim3(256), 0, s, a, NoTable{});
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(a.total_q), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, NoTable>), dim3(a.total_q), dim3(256), 0, s, a, NoTable{});
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -960,6 +1010,97 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   a.n_qtiles = (p.Sq + Q_WG - 1) / Q_WG;
   a.total_q = p.B * p.Hq * a.n_qtiles;
   return p.d == 64 ? launch_bwd_d<64>(a, s, log, log_n) : launch_bwd_d<128>(a, s, log, log_n);
+}
+
+namespace {
+
+template <int D>
+hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tp, int gp, const SeqTable& Tkv, int gkv,
+                               const SeqTable& Tq, int gq, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (gp > 0) {
+    timing_begin(s, "bwd_pre");
+    hipLaunchKernelGGL((bwd_pre_kernel<D, SeqTable>), dim3(gp), dim3(256), 0, s, a, Tp);
+    e = hipGetLastError();
+    timing_end(s);
+    if (e != hipSuccess) return e;
+  }
+  if (gkv > 0) {
+    timing_begin(s, "bwd_dkdv");
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SeqTable>), dim3(gkv), dim3(512), 0, s, a, Tkv);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SeqTable>), dim3(gkv), dim3(512), 0, s, a, Tkv);
+    e = hipGetLastError();
+    timing_end(s);
+    if (e != hipSuccess) return e;
+  }
+  if (gq > 0) {
+    timing_begin(s, "bwd_dq");
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, SeqTable>), dim3(gq), dim3(256), 0, s, a, Tq);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, SeqTable>), dim3(gq), dim3(256), 0, s, a, Tq);
+    e = hipGetLastError();
+    timing_end(s);
+  }
+  return e;
+}
+
+}  // namespace
+
+size_t bwd_packed_workspace_bytes(const Problem& p, const SeqSpan* seqs, int n) {
+  size_t rows = 0;
+  for (int i = 0; i < n; ++i) rows += (size_t)((seqs[i].sq + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
+  return align256(rows * p.Hq * 2 * sizeof(float));
+}
+
+hipError_t launch_bwd_bf16_packed(const Problem& p, const SeqSpan* seqs, int n, const void* q, const void* k,
+                                  const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, void* ws, hipStream_t s, char* log, size_t log_n) {
+  BwdArgs a{};
+  a.q = (const bf16*)q;
+  a.k = (const bf16*)k;
+  a.v = (const bf16*)v;
+  a.o = (const bf16*)o;
+  a.dout = (const bf16*)dout;
+  a.lse = lse;
+  a.dq = (bf16*)dq;
+  a.dk = (bf16*)dk;
+  a.dv = (bf16*)dv;
+  a.ld = (float*)ws;
+  a.B = 1;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.hsq = p.hsq;
+  a.hsk = p.hsk;
+  a.g = p.Hq / p.Hkv;
+  a.causal = p.causal;
+  a.scale = p.scale;
+  a.c = p.scale * kLog2e;
+  const int rpb = 256 / (p.d / 8);              // bwd_pre rows per block
+  int np[SEQ_MAX], nkv[SEQ_MAX], nq[SEQ_MAX], ld0[SEQ_MAX];
+  int rows = 0;
+  for (int i = 0; i < n; ++i) {
+    const int sqp = (seqs[i].sq + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
+    np[i] = p.Hq * (sqp / rpb);
+    nkv[i] = (seqs[i].sk + KV_WG - 1) / KV_WG;
+    nq[i] = (seqs[i].sq + Q_WG - 1) / Q_WG;
+    ld0[i] = rows;
+    rows += sqp;
+  }
+  SeqTable Tp, Tkv, Tq;
+  const int gp = build_seq_table(Tp, seqs, n, 1, np, ld0);
+  const int gkv = build_seq_table(Tkv, seqs, n, p.Hkv, nkv, ld0);
+  const int gq = build_seq_table(Tq, seqs, n, p.Hq, nq, ld0);
+  if (log != nullptr && log_n > 0)
+    snprintf(log, log_n,
+             "bwd_pre<d=%d, packed> grid=%d; bwd_dkdv<d=%d, packed> %d sequences grid=%d%s; "
+             "bwd_dq<d=%d, packed> %d sequences grid=%d%s",
+             p.d, gp, p.d, Tkv.n, gkv, Tkv.split8 ? " (per-XCD head split)" : "", p.d, Tq.n, gq,
+             Tq.split8 ? " (per-XCD head split)" : "");
+  return p.d == 64 ? launch_bwd_packed_d<64>(a, Tp, gp, Tkv, gkv, Tq, gq, s)
+                   : launch_bwd_packed_d<128>(a, Tp, gp, Tkv, gkv, Tq, gq, s);
 }
 
 }  // namespace attn

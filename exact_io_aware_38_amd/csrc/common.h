@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace attn {
 
 typedef __bf16 bf16;
@@ -117,5 +119,30 @@ __device__ __forceinline__ int xcd_logical_id(int linear, int total) {
   if ((total & 7) != 0) return linear;
   return (linear & 7) * (total >> 3) + (linear >> 3);
 }
+
+// Table parameter of a kernel launched on one dense problem.
+struct NoTable {};
+
+// Where this workgroup sits in a packed launch: the sequence, the unit (head
+// or group of heads) and the tile rank inside the unit (0 first). Wave-uniform;
+// a binary search over the table's workgroup offsets.
+struct SeqCoord {
+  int seq, unit, t;
+};
+__host__ __device__ inline SeqCoord seq_coord_of(const SeqTable& T, int id) {
+  int x = 0, r = id, per = T.units;
+  if (T.split8) {
+    x = id & 7;
+    r = id >> 3;
+    per = T.units >> 3;
+  }
+  int s = 0;
+#pragma unroll
+  for (int step = SEQ_MAX / 2; step > 0; step >>= 1)
+    if (s + step < T.n && T.wg0[s + step] <= r) s += step;
+  const int local = r - T.wg0[s];
+  return SeqCoord{s, x * per + local % per, local / per};
+}
+__device__ __forceinline__ SeqCoord seq_coord(const SeqTable& T) { return seq_coord_of(T, blockIdx.x); }
 
 }  // namespace attn

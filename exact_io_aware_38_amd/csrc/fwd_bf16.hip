@@ -33,6 +33,7 @@
 #include "tiles.h"
 
 #include <algorithm>
+#include <cstdio>
 #include <type_traits>
 
 namespace attn {
@@ -70,8 +71,23 @@ struct Ring {
   static constexpr int INSTR = D / 64;          // DMA instructions per wavefront per tensor per tile
 };
 
+// Sequence s of a packed launch as a problem of batch 1: lengths and data
+// pointers from the table (the head strides stay the packed totals).
 template <int D>
-__global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
+__device__ __forceinline__ void rebase(FwdArgs& a, const SeqTable& T, int s) {
+  a.Sq = T.sq[s];
+  a.Sk = T.sk[s];
+  const size_t qo = (size_t)T.q0[s] * D, ko = (size_t)T.k0[s] * D;
+  a.q += qo;
+  a.o += qo;
+  if (a.lse != nullptr) a.lse += T.q0[s];
+  a.k += ko;
+  a.v += ko;
+}
+
+// Tab: NoTable for one dense [B, H, S, d] problem, SeqTable for a packed launch.
+template <int D, typename Tab>
+__global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   using R = Ring<D>;
   constexpr int MB = D / 32;
   constexpr int DC = D / 16;
@@ -89,15 +105,25 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool phase_b = wid >= 4;
-  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
 
-  const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
-  const int ptile = a.n_ptiles - 1 - (W % a.n_ptiles);   // longest causal tiles first
-  int rest = W / a.n_ptiles;
-  const int hgrp = rest % a.n_hgroups;
-  rest /= a.n_hgroups;
-  const int hkv = rest % a.Hkv;
-  const int b = rest / a.Hkv;
+  int ptile, hgrp, hkv, b;                      // longest causal tiles first
+  if constexpr (std::is_same_v<Tab, SeqTable>) {
+    const SeqCoord c = seq_coord(T);
+    rebase<D>(a, T, c.seq);
+    ptile = T.ntile[c.seq] - 1 - c.t;
+    hgrp = c.unit % a.n_hgroups;
+    hkv = c.unit / a.n_hgroups;
+    b = 0;
+  } else {
+    const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
+    ptile = a.n_ptiles - 1 - (W % a.n_ptiles);
+    int rest = W / a.n_ptiles;
+    hgrp = rest % a.n_hgroups;
+    rest /= a.n_hgroups;
+    hkv = rest % a.Hkv;
+    b = rest / a.Hkv;
+  }
+  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
   // the two phases take alternating 32-row blocks, which keeps their causal work equal
   const int slot = (wid & 3) * 2 + (wid >> 2);
   const int head = hkv * a.g + hgrp * a.hw + slot % a.hw;
@@ -583,7 +609,16 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
 template <int D>
 hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
   timing_begin(s, "fwd_prefill_bf16");
-  hipLaunchKernelGGL((fwd_prefill_kernel<D>), dim3(a.total_wgs), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
+  const hipError_t e = hipGetLastError();
+  timing_end(s);
+  return e;
+}
+
+template <int D>
+hipError_t launch_prefill_packed_d(const FwdArgs& a, const SeqTable& T, int grid, hipStream_t s) {
+  timing_begin(s, "fwd_prefill_bf16");
+  hipLaunchKernelGGL((fwd_prefill_kernel<D, SeqTable>), dim3(grid), dim3(512), 0, s, a, T);
   const hipError_t e = hipGetLastError();
   timing_end(s);
   return e;
@@ -669,6 +704,26 @@ hipError_t launch_fwd_prefill_bf16(const Problem& p, const PrefillPlan& pl, cons
   (void)ws;
   if (a.total_wgs == 0) return hipSuccess;
   return p.d == 64 ? launch_prefill_d<64>(a, s) : launch_prefill_d<128>(a, s);
+}
+
+hipError_t launch_fwd_prefill_bf16_packed(const Problem& p, const SeqSpan* seqs, int n, const void* q,
+                                          const void* k, const void* v, void* o, float* lse, hipStream_t s,
+                                          char* log, size_t log_n) {
+  const PrefillPlan pl = plan_prefill(p);       // the head grouping depends only on Hq / Hkv
+  FwdArgs a = base_args(p, q, k, v, o, lse);
+  a.hw = pl.hw;
+  a.n_hgroups = pl.n_hgroups;
+  a.rows_per_wg = pl.rows_per_wg;
+  int ntile[SEQ_MAX];
+  for (int i = 0; i < n; ++i) ntile[i] = (seqs[i].sq + pl.rows_per_wg - 1) / pl.rows_per_wg;
+  SeqTable T;
+  const int grid = build_seq_table(T, seqs, n, p.Hkv * pl.n_hgroups, ntile, nullptr);
+  if (log != nullptr && log_n > 0)
+    snprintf(log, log_n, "fwd_prefill<d=%d, packed> %d sequences grid=%d (%d query rows x %d heads per workgroup%s)",
+             p.d, T.n, grid, pl.rows_per_wg, pl.hw,
+             T.split8 ? ", per-XCD head split" : "");
+  if (grid == 0) return hipSuccess;
+  return p.d == 64 ? launch_prefill_packed_d<64>(a, T, grid, s) : launch_prefill_packed_d<128>(a, T, grid, s);
 }
 
 hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& sp, const void* q, const void* k,

@@ -26,6 +26,64 @@ struct Problem {
   int hsq, hsk;     // head strides in rows
 };
 
+// ---- packed batches in one launch -------------------------------------------
+// A sequence of a head-major packed batch: its first packed query and key row
+// and its lengths.
+struct SeqSpan {
+  int q0, k0, sq, sk;
+};
+
+// Up to SEQ_MAX sequences of a packed batch run as one grid. Workgroups are
+// numbered sequence after sequence; every sequence has `units` independent
+// units (heads or groups of heads) of ntile[i] tiles each. With split8 each
+// of the 8 XCDs (the hardware deals consecutive workgroup ids to them in
+// turn) takes units/8 units of every sequence, so the XCDs get equal work and
+// each unit's K and V stay in one L2; wg0 then counts workgroups per XCD. The
+// table travels in the kernel arguments.
+constexpr int SEQ_MAX = 64;
+struct SeqTable {
+  int n, units, split8;
+  int wg0[SEQ_MAX + 1];      // first workgroup of each sequence
+  int ntile[SEQ_MAX];
+  int q0[SEQ_MAX], k0[SEQ_MAX], sq[SEQ_MAX], sk[SEQ_MAX];
+  int aux[SEQ_MAX];          // per-kernel offset (the backward's lse2/D block, in floats)
+};
+
+// Fills T with the sequences that have at least one tile; returns the grid
+// size.
+inline int build_seq_table(SeqTable& T, const SeqSpan* seqs, int n, int units, const int* ntile,
+                           const int* aux) {
+  T = SeqTable{};
+  T.units = units;
+  T.split8 = (units % 8) == 0;
+  const int per = T.split8 ? units / 8 : units;
+  int w = 0;
+  for (int i = 0; i < n; ++i) {
+    if (ntile[i] == 0) continue;
+    const int j = T.n++;
+    T.wg0[j] = w;
+    T.ntile[j] = ntile[i];
+    T.q0[j] = seqs[i].q0;
+    T.k0[j] = seqs[i].k0;
+    T.sq[j] = seqs[i].sq;
+    T.sk[j] = seqs[i].sk;
+    T.aux[j] = aux != nullptr ? aux[i] : 0;
+    w += per * ntile[i];
+  }
+  T.wg0[T.n] = w;
+  return T.split8 ? 8 * w : w;
+}
+
+// p carries Hq, Hkv, d, causal, scale and the packed totals as head strides
+// (B = 1; Sq and Sk are taken per sequence). n <= SEQ_MAX.
+hipError_t launch_fwd_prefill_bf16_packed(const Problem& p, const SeqSpan* seqs, int n, const void* q,
+                                          const void* k, const void* v, void* o, float* lse, hipStream_t s,
+                                          char* log, size_t log_n);
+size_t bwd_packed_workspace_bytes(const Problem& p, const SeqSpan* seqs, int n);
+hipError_t launch_bwd_bf16_packed(const Problem& p, const SeqSpan* seqs, int n, const void* q, const void* k,
+                                  const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, void* ws, hipStream_t s, char* log, size_t log_n);
+
 // ---- forward, bf16 ----------------------------------------------------------
 // Tiled prefill: one workgroup per (query-row tile, group of query heads).
 struct PrefillPlan {

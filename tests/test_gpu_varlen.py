@@ -49,6 +49,14 @@ FWD_CASES = [
     ("decode_rows", 32, 8, 128, "bf16", 0, (1, 1, 1, 1), (4096, 100, 7000, 1)),
     ("tiny_tail", 2, 2, 128, "bf16", 1, (1, 2, 3, 129, 64), (1, 2, 3, 129, 64)),
     ("f32_causal", 4, 2, 128, "f32", 2, (100, 17), (120, 3)),
+    # eight head units: each XCD takes one head of every sequence
+    ("per_xcd_heads", 8, 8, 128, "bf16", 1, (200, 0, 1, 333, 64), (200, 9, 1, 333, 64)),
+    # decode-shaped sequences (split over the keys) next to packed prefill ones
+    ("decode_and_prefill", 8, 2, 128, "bf16", 0, (1, 300, 2, 77), (500, 300, 1000, 77)),
+    # more sequences than one packed launch takes
+    ("many_sequences", 4, 4, 64, "bf16", 1,
+     tuple(int(x) for x in np.random.default_rng(71).integers(0, 90, 70)),
+     tuple(int(x) for x in np.random.default_rng(71).integers(0, 90, 70))),
 ]
 
 
@@ -108,6 +116,10 @@ BWD_CASES = [
     ("bottom_right", 4, 4, 64, 2, (150, 33, 1), (60, 200, 77)),
     ("no_mask_gqa", 4, 1, 128, 0, (96, 300), (500, 31)),
     ("no_queries_no_keys", 2, 2, 64, 1, (0, 90, 40), (70, 90, 0)),
+    ("per_xcd_heads", 8, 8, 128, 2, (260, 0, 31, 1), (200, 64, 31, 700)),
+    ("many_sequences", 2, 1, 64, 1,
+     tuple(int(x) for x in np.random.default_rng(72).integers(0, 70, 67)),
+     tuple(int(x) for x in np.random.default_rng(73).integers(0, 70, 67))),
 ]
 
 
