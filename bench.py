@@ -40,19 +40,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # kernel name -> source files whose content defines it (for counter staleness)
 KERNEL_SOURCES = {
-    "fwd_prefill_bf16": ["fwd_bf16.hip", "common.h", "tiles.h"],
-    "fwd_split_bf16": ["fwd_bf16.hip", "common.h", "tiles.h"],
-    "bwd_dkdv": ["bwd_bf16.hip", "common.h", "tiles.h"],
-    "bwd_dq": ["bwd_bf16.hip", "common.h", "tiles.h"],
-    "bwd_pre": ["bwd_bf16.hip"],
+    "fwd_prefill_bf16": ["fwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
+    "fwd_split_bf16": ["fwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
+    "bwd_dkdv": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
+    "bwd_dq": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
+    "bwd_pre": ["bwd_bf16.hip", "common.h", "kernels.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
+# (the dense and the packed instantiations both match; a workload uses one)
 KERNEL_SYMBOLS = {
-    "fwd_prefill_bf16": "fwd_prefill_kernel<128>",
+    "fwd_prefill_bf16": "fwd_prefill_kernel<128,",
     "fwd_split_bf16": "fwd_split_kernel<128>",
-    "bwd_dkdv": "bwd_dkdv_kernel<128",
-    "bwd_dq": "bwd_dq_kernel<128",
-    "bwd_pre": "bwd_pre_kernel<128>",
+    "bwd_dkdv": "bwd_dkdv_kernel<128,",
+    "bwd_dq": "bwd_dq_kernel<128,",
+    "bwd_pre": "bwd_pre_kernel<128,",
 }
 
 
@@ -113,8 +114,8 @@ def traffic_for(kernel: str, workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def roofline(kernel: str, w, avg_ms: float) -> dict:
-    work = kernel_work(kernel, w)
+def roofline(kernel: str, w, avg_ms: float, work: dict = None) -> dict:
+    work = kernel_work(kernel, w) if work is None else work
     if work["bound"] == "mfma":
         ach = work["flops"] / (avg_ms * 1e-3) / 1e12
         peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
@@ -257,11 +258,22 @@ def bench_varlen(attn, steps, warmup):
 
     ms, kern = _time(step, steps, warmup, attn, per_step=True)
     total = sum(3.5 * nominal_fwd_flops(1, w.Hq, n, n, w.d, w.causal) for n in lens)
+    # every kernel runs once per step (at most 64 sequences per launch), so its
+    # time per step is its time per launch; the work is summed over sequences
+    assert len(lens) <= 64
+    dom = max(kern, key=kern.get)
+    seq_w = [synth.Workload(w.name, 1, w.Hq, w.Hkv, n, n, w.d, w.dtype, w.causal, seed=0) for n in lens]
+    parts = [kernel_work(dom, sw) for sw in seq_w]
+    key = "flops" if parts[0]["bound"] == "mfma" else "bytes"
+    work = {"bound": parts[0]["bound"], key: sum(p[key] for p in parts)}
+    ws_name = w.name
     return {"workload": w.name, "sequences": len(lens), "total_tokens": cq[-1], "min_len": min(lens),
             "max_len": max(lens), "H": w.Hq, "d": w.d, "causal": w.causal,
             "step": "attn_fwd_varlen + attn_bwd_varlen", "ms": round(ms, 4),
             "tokens_per_s": round(cq[-1] / ms * 1e3, 1), "tflops": round(total / ms / 1e9, 2),
             "frac_of_peak": round(total / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline(dom, synth.Workload(ws_name, 1, w.Hq, w.Hkv, 0, 0, w.d, w.dtype, w.causal, 0),
+                                 kern[dom], work),
             "kernels_ms_per_step": {k: round(v, 4) for k, v in kern.items()}}
 
 
@@ -434,7 +446,8 @@ def main() -> int:
         torch.cuda.empty_cache()
     if args.only == "varlen":
         result.update({"value": result["varlen"]["tflops"], "ms_per_step": result["varlen"]["ms"],
-                       "config": {"workload": result["varlen"]["workload"]}, "roofline": None})
+                       "config": {"workload": result["varlen"]["workload"]},
+                       "roofline": result["varlen"]["roofline"]})
     if args.only == "fwd":
         result.update({"value": result["fwd"]["tflops"], "ms_per_step": result["fwd"]["ms"],
                        "config": {"workload": result["fwd"]["workload"]}, "roofline": result["fwd"]["roofline"]})
