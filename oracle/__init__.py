@@ -7,4 +7,5 @@ with the HIP kernels or their host library.
 from .attention import (  # noqa: F401
     visible_mask, attention_forward, attention_backward, online_softmax_forward,
     merge_states, FullyMaskedRowError, attention_forward_varlen, attention_backward_varlen,
+    philox4x32_10, dropout_threshold, dropout_keep_mask,
 )

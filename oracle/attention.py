@@ -37,7 +37,8 @@ import numpy as np
 __all__ = [
     "FullyMaskedRowError", "visible_mask", "attention_forward",
     "attention_backward", "online_softmax_forward", "merge_states",
-    "attention_forward_varlen", "attention_backward_varlen",
+    "attention_forward_varlen", "attention_backward_varlen", "philox4x32_10",
+    "dropout_threshold", "dropout_keep_mask",
 ]
 
 
@@ -73,9 +74,81 @@ def _group(Hq: int, Hkv: int) -> int:
     return Hq // Hkv
 
 
+_PHILOX_MUL = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_WEYL = (0x9E3779B9, 0xBB67AE85)
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+    numbers: as easy as 1, 2, 3", SC 2011), vectorised over the leading axes.
+
+    counter: integers [..., 4] below 2^32; key: (k0, k1). Each round forms the
+    64-bit products of the first and third counter words with the two round
+    multipliers; the new words are (high of the second product xor word 1 xor
+    k0, low of the second product, high of the first product xor word 3 xor k1,
+    low of the first product). The key advances by the two Weyl constants after
+    every round. Returns uint64 [..., 4] holding 32-bit words.
+    """
+    c = [np.asarray(counter, dtype=np.uint64)[..., w] & _U32 for w in range(4)]
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    for _ in range(10):
+        p0 = c[0] * np.uint64(_PHILOX_MUL[0])          # < 2^64: exact in uint64
+        p1 = c[2] * np.uint64(_PHILOX_MUL[1])
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ np.uint64(k0), p1 & _U32,
+             (p0 >> np.uint64(32)) ^ c[3] ^ np.uint64(k1), p0 & _U32]
+        k0 = (k0 + _PHILOX_WEYL[0]) & 0xFFFFFFFF
+        k1 = (k1 + _PHILOX_WEYL[1]) & 0xFFFFFFFF
+    return np.stack(c, axis=-1)
+
+
+def dropout_threshold(p: float) -> int:
+    """The byte threshold of a dropout probability: round(256 p) with p taken
+    in single precision (the library's argument type), ties to even."""
+    p32 = np.float32(p)
+    if not np.isfinite(p32) or p32 < 0 or p32 >= 1:
+        raise ValueError(f"dropout probability {p} not in [0, 1)")
+    thr = int(np.rint(p32 * np.float32(256.0)))
+    if thr > 255:
+        raise ValueError(f"dropout probability {p} rounds to 256/256")
+    return thr
+
+
+def dropout_keep_mask(B: int, Hq: int, Sq: int, Sk: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Boolean keep mask [B, Hq, Sq, Sk] of the dropout contract.
+
+    [P2] "接口与实现约束" asks that, with dropout on, the mapping to random
+    numbers be part of the contract between the forward and the backward;
+    the pages name no generator. Reading taken: Philox4x32-10 keyed by the
+    64-bit seed (low word first); the 4x4 block of query rows 4a..4a+3 and
+    keys 4c..4c+3 of query head h in batch b takes counter (c, a, b Hq + h,
+    offset); byte t of output word w decides query 4a+w, key 4c+t, which is
+    kept when the byte is at least round(256 p).
+    """
+    thr = dropout_threshold(p)
+    na, nc = (Sq + 3) // 4, (Sk + 3) // 4
+    bh, a, c = np.meshgrid(np.arange(B * Hq), np.arange(na), np.arange(nc), indexing="ij")
+    ctr = np.stack([c, a, bh, np.full_like(c, offset)], axis=-1)
+    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))   # [BH, na, nc, 4]
+    shifts = np.arange(4, dtype=np.uint64) * np.uint64(8)
+    byte = (words[..., :, None] >> shifts) & np.uint64(0xFF)                     # [BH, na, nc, w, t]
+    full = byte.transpose(0, 1, 3, 2, 4).reshape(B * Hq, 4 * na, 4 * nc)         # rows 4a+w, cols 4c+t
+    return (full[:, :Sq, :Sk] >= thr).reshape(B, Hq, Sq, Sk)
+
+
+def _dropout_factor(dropout, B, Hq, Sq, Sk):
+    """Z = keep / (1 - thr/256) as float64 [B, Hq, Sq, Sk], or None."""
+    if dropout is None:
+        return None
+    p, seed, offset = dropout
+    thr = dropout_threshold(p)
+    keep = dropout_keep_mask(B, Hq, Sq, Sk, p, seed, offset)
+    return keep.astype(np.float64) / (1.0 - thr / 256.0)
+
+
 def attention_forward(q, k, v, *, causal: int = 0, scale: Optional[float] = None,
                       strict: bool = False, rows: Optional[Sequence[int]] = None,
-                      Sq: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+                      Sq: Optional[int] = None, dropout=None) -> Tuple[np.ndarray, np.ndarray]:
     """softmax(scale * Q K^T, masked) V by its definition, in float64.
 
     q: [B, Hq, n, d]; k: [B, Hkv, Sk, d]; v: [B, Hkv, Sk, dv]. When ``rows`` is
@@ -87,6 +160,10 @@ def attention_forward(q, k, v, *, causal: int = 0, scale: Optional[float] = None
     applied before the row maximum as [P2] "瓦片状态如何保持精确语义" requires;
     the max is subtracted before exponentiation, which leaves the softmax
     unchanged and keeps exp finite for the large scores of [P2] "工程实操".
+
+    ``dropout=(p, seed, offset)`` multiplies the probabilities by
+    Z = keep / (1 - thr/256) (``dropout_keep_mask``) before V; lse stays the
+    logsumexp of the undropped scores.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -110,6 +187,9 @@ def attention_forward(q, k, v, *, causal: int = 0, scale: Optional[float] = None
     empty = ~vis.any(axis=1)
     if strict and empty.any():
         raise FullyMaskedRowError(f"{int(empty.sum())} query row(s) see no key")
+    if dropout is not None and rows is not None:
+        raise ValueError("dropout applies to whole problems, not row subsets")
+    Z = _dropout_factor(dropout, B, Hq, n, Sk)
     for b in range(B):
         for h in range(Hq):
             hk = h // g
@@ -122,13 +202,15 @@ def attention_forward(q, k, v, *, causal: int = 0, scale: Optional[float] = None
             l = e.sum(axis=1)
             p = np.zeros_like(s)
             p[ok] = e[ok] / l[ok, None]
+            if Z is not None:
+                p = p * Z[b, h]
             o[b, h] = p @ v[b, hk]
             lse[b, h, ok] = m[ok] + np.log(l[ok])
     return o, lse
 
 
 def attention_backward(q, k, v, do, *, causal: int = 0, scale: Optional[float] = None,
-                       return_intermediates: bool = False) -> Dict[str, np.ndarray]:
+                       return_intermediates: bool = False, dropout=None) -> Dict[str, np.ndarray]:
     """Analytic gradients of O = softmax(scale Q K^T, masked) V, in float64.
 
     Follows the chain of [P2] "反向传播为什么可以重算" and "训练与部署":
@@ -140,6 +222,10 @@ def attention_backward(q, k, v, do, *, causal: int = 0, scale: Optional[float] =
     Returns dq [B,Hq,Sq,d], dk [B,Hkv,Sk,d], dv [B,Hkv,Sk,dv]; with
     ``return_intermediates`` also p, ds (per query head, [B,Hq,Sq,Sk]) and
     D (the Jacobian row term sum_k P_ik dP_ik, [B,Hq,Sq]).
+
+    With ``dropout=(p, seed, offset)`` the output is (P o Z) V, so by the chain
+    rule dV = (P o Z)^T dO, the gradient reaching P is Z o (dO V^T), and the
+    softmax Jacobian acts on that (D is then sum_k P_ik Z_ik (dO V^T)_ik).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -153,6 +239,7 @@ def attention_backward(q, k, v, do, *, causal: int = 0, scale: Optional[float] =
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    Z = _dropout_factor(dropout, B, Hq, Sq, Sk)
     extra = {}
     if return_intermediates:
         extra = {"p": np.zeros((B, Hq, Sq, Sk)), "ds": np.zeros((B, Hq, Sq, Sk)),
@@ -167,8 +254,11 @@ def attention_backward(q, k, v, do, *, causal: int = 0, scale: Optional[float] =
             p = np.zeros_like(s)
             p[ok] = np.exp(s[ok] - m[ok, None])
             p[ok] /= p[ok].sum(axis=1, keepdims=True)
-            dv[b, hk] += p.T @ do[b, h]
+            pz = p if Z is None else p * Z[b, h]
+            dv[b, hk] += pz.T @ do[b, h]
             dp = do[b, h] @ v[b, hk].T
+            if Z is not None:
+                dp = dp * Z[b, h]
             D = (p * dp).sum(axis=1)                    # Jacobian row term
             ds = p * (dp - D[:, None])                  # zero wherever p is zero (masked)
             dq[b, h] = c * (ds @ k[b, hk])

@@ -10,8 +10,9 @@ import torch
 
 import oracle
 from oracle import (FullyMaskedRowError, attention_backward, attention_backward_varlen,
-                    attention_forward, attention_forward_varlen, merge_states,
-                    online_softmax_forward, visible_mask)
+                    attention_forward, attention_forward_varlen, dropout_keep_mask,
+                    dropout_threshold, merge_states, online_softmax_forward, philox4x32_10,
+                    visible_mask)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -471,5 +472,97 @@ def test_varlen_backward_matches_autograd_block_diagonal():
     kk, vv = tk.repeat_interleave(2, dim=0), tv.repeat_interleave(2, dim=0)
     s = (0.5 * tq @ kk.transpose(-1, -2)).masked_fill(~mask, float("-inf"))
     (torch.softmax(s, dim=-1) @ vv).backward(torch.from_numpy(do))
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert np.abs(gr[name] - t.grad.numpy()).max() < 1e-12, name
+
+
+# ---------------------------------------------------------------- dropout
+def test_philox_known_answer_vectors():
+    for vec in _load("philox_kat.json")["vectors"]:
+        ctr = [int(x, 16) for x in vec["counter"]]
+        key = [int(x, 16) for x in vec["key"]]
+        out = philox4x32_10(np.array(ctr, dtype=np.uint64), key)
+        assert ["%08x" % int(x) for x in out] == vec["output"]
+
+
+def test_dropout_mask_layout_rate_and_streams():
+    B, Hq, Sq, Sk, seed, off = 2, 3, 10, 13, (7 << 32) | 123, 5
+    m = dropout_keep_mask(B, Hq, Sq, Sk, 0.3, seed, off)
+    thr = dropout_threshold(0.3)
+    assert thr == 77
+    # element by element from single generator calls: counter (j//4, i//4, b*Hq+h, offset),
+    # byte j%4 of word i%4
+    for (b, h, i, j) in np.ndindex(m.shape):
+        w = philox4x32_10(np.array([j // 4, i // 4, b * Hq + h, off], dtype=np.uint64), (123, 7))
+        byte = (int(w[i % 4]) >> (8 * (j % 4))) & 0xFF
+        assert m[b, h, i, j] == (byte >= thr), (b, h, i, j)
+    big = dropout_keep_mask(1, 4, 256, 256, 0.1, 99, 0)
+    keep = 1 - dropout_threshold(0.1) / 256
+    n = big.size
+    assert abs(big.mean() - keep) < 6 * np.sqrt(keep * (1 - keep) / n)
+    assert dropout_keep_mask(1, 1, 8, 8, 0.0, 1, 0).all()
+    assert not np.array_equal(big, dropout_keep_mask(1, 4, 256, 256, 0.1, 99, 1))
+    assert np.array_equal(big, dropout_keep_mask(1, 4, 256, 256, 0.1, 99, 0))
+    for bad in (-0.1, 1.0, 0.999, float("nan")):
+        with pytest.raises(ValueError):
+            dropout_threshold(bad)
+
+
+def test_dropout_zero_probability_is_plain_attention():
+    rng = np.random.default_rng(40)
+    q, k, v = _rand(rng, 1, 4, 2, 9, 11, 4)
+    do = rng.standard_normal(q.shape)
+    o, lse = attention_forward(q, k, v, causal=2)
+    o0, lse0 = attention_forward(q, k, v, causal=2, dropout=(0.0, 5, 0))
+    assert np.array_equal(o, o0) and np.array_equal(lse, lse0)
+    g = attention_backward(q, k, v, do, causal=2)
+    g0 = attention_backward(q, k, v, do, causal=2, dropout=(0.0, 5, 0))
+    for n in ("dq", "dk", "dv"):
+        assert np.array_equal(g[n], g0[n])
+
+
+def _drop_loss(q, k, v, causal, drop):
+    o, _ = attention_forward(q, k, v, causal=causal, scale=0.6, dropout=drop)
+    return 0.5 * float((o ** 2).sum()), o
+
+
+def test_dropout_central_differences():
+    rng = np.random.default_rng(41)
+    q, k, v = _rand(rng, 1, 2, 1, 5, 6, 3)
+    drop = (0.4, 2024, 3)
+    _, o = _drop_loss(q, k, v, 1, drop)
+    gr = attention_backward(q, k, v, o, causal=1, scale=0.6, dropout=drop)
+    h = 1e-6
+    worst = 0.0
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap = {"dq": (xp, k, v), "dk": (q, xp, v), "dv": (q, k, xp)}[name]
+            am = {"dq": (xm, k, v), "dk": (q, xm, v), "dv": (q, k, xm)}[name]
+            num = (_drop_loss(*ap, 1, drop)[0] - _drop_loss(*am, 1, drop)[0]) / (2 * h)
+            worst = max(worst, abs(num - gr[name][idx]))
+    assert worst <= 1e-8, worst
+
+
+@pytest.mark.parametrize("causal", [0, 2])
+def test_dropout_matches_torch_autograd_fp64(causal):
+    rng = np.random.default_rng(42 + causal)
+    B, Hq, Hkv, Sq, Sk, d = 2, 4, 2, 7, 10, 5
+    q, k, v = _rand(rng, B, Hq, Hkv, Sq, Sk, d, outliers=1)
+    do = rng.standard_normal((B, Hq, Sq, d))
+    drop = (0.25, 77, 11)
+    o, lse = attention_forward(q, k, v, causal=causal, scale=0.5, dropout=drop)
+    gr = attention_backward(q, k, v, do, causal=causal, scale=0.5, dropout=drop)
+    z = torch.from_numpy(dropout_keep_mask(B, Hq, Sq, Sk, *drop).astype(np.float64)) / (1 - 64 / 256)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    kk, vv = tk.repeat_interleave(2, dim=1), tv.repeat_interleave(2, dim=1)
+    s = (0.5 * tq @ kk.transpose(-1, -2)).masked_fill(~_torch_mask(Sq, Sk, causal), float("-inf"))
+    p = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0)
+    ref = (p * z) @ vv
+    assert np.abs(o - ref.detach().numpy()).max() < 1e-12
+    assert np.abs(lse - torch.logsumexp(s, dim=-1).detach().numpy()).max() < 1e-12
+    ref.backward(torch.from_numpy(do))
     for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
         assert np.abs(gr[name] - t.grad.numpy()).max() < 1e-12, name

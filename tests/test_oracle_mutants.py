@@ -29,7 +29,11 @@ MUTANTS = {
     "backward_jacobian_sign": ("ds = p * (dp - D[:, None])", "ds = p * (dp + D[:, None])"),
     "backward_dq_missing_scale": ("dq[b, h] = c * (ds @ k[b, hk])", "dq[b, h] = ds @ k[b, hk]"),
     "backward_dk_transposed_operand": ("dk[b, hk] += c * (ds.T @ q[b, h])", "dk[b, hk] += c * (p.T @ q[b, h])"),
-    "backward_dv_drops_probabilities": ("dv[b, hk] += p.T @ do[b, h]", "dv[b, hk] += vis.T @ do[b, h]"),
+    "backward_dv_drops_probabilities": ("dv[b, hk] += pz.T @ do[b, h]", "dv[b, hk] += vis.T @ do[b, h]"),
+    "dropout_dv_without_mask": ("pz = p if Z is None else p * Z[b, h]", "pz = p"),
+    "dropout_dp_without_mask": ("                dp = dp * Z[b, h]", "                dp = dp"),
+    "dropout_rows_and_keys_swapped": ("full = byte.transpose(0, 1, 3, 2, 4)", "full = byte.transpose(0, 1, 2, 3, 4)"),
+    "dropout_kept_values_not_rescaled": ("keep.astype(np.float64) / (1.0 - thr / 256.0)", "keep.astype(np.float64)"),
     "varlen_keys_cut_at_query_offsets": ("        ks = slice(cu_k[b], cu_k[b + 1])\n        ob, lb",
                                          "        ks = slice(cu_q[b], cu_q[b + 1])\n        ob, lb"),
     "varlen_mask_on_packed_rows": ("causal=causal, scale=scale)\n        o[:, qs] = ob[0]",
@@ -58,11 +62,14 @@ PIN_CALLS = [
     (pins.test_varlen_matches_block_diagonal_softmax, {"causal": 2}),
     (pins.test_varlen_central_differences, {"causal": 2}),
     (pins.test_varlen_backward_matches_autograd_block_diagonal, {}),
+    (pins.test_dropout_mask_layout_rate_and_streams, {}),
+    (pins.test_dropout_central_differences, {}),
+    (pins.test_dropout_matches_torch_autograd_fp64, {"causal": 2}),
 ]
 
 _NAMES = ["attention_forward", "attention_backward", "online_softmax_forward",
           "merge_states", "visible_mask", "FullyMaskedRowError", "attention_forward_varlen",
-          "attention_backward_varlen"]
+          "attention_backward_varlen", "philox4x32_10", "dropout_threshold", "dropout_keep_mask"]
 
 
 def _mutant_module(old, new):
