@@ -16,7 +16,7 @@ __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "lib", "library_path", "fwd", "bwd",
     "fwd_workspace_bytes", "bwd_workspace_bytes", "strerror", "last_dispatch",
     "timing_start", "timing_stop", "fwd_varlen", "bwd_varlen", "fwd_varlen_workspace_bytes",
-    "bwd_varlen_workspace_bytes",
+    "bwd_varlen_workspace_bytes", "fwd_dropout", "bwd_dropout", "dropout_mask",
 ]
 
 ATTN_F32 = 0
@@ -71,6 +71,13 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_varlen.restype = _I
         L.attn_bwd_varlen.argtypes = [_P] * 9 + _VSHAPE + [_F, _I, _P, _Z, _P]
         L.attn_bwd_varlen.restype = _I
+        _DROP = [_F, ctypes.c_ulonglong, ctypes.c_uint]     # dropout_p, seed, offset
+        L.attn_fwd_dropout.argtypes = [_P] * 5 + _SHAPE + [_F] + _DROP + [_P]
+        L.attn_fwd_dropout.restype = _I
+        L.attn_bwd_dropout.argtypes = [_P] * 9 + _SHAPE + [_F] + _DROP + [_P, _Z, _P]
+        L.attn_bwd_dropout.restype = _I
+        L.attn_dropout_mask.argtypes = [_P, _I, _I, _I, _I] + _DROP + [_P]
+        L.attn_dropout_mask.restype = _I
         L.attn_strerror.argtypes = [_I]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_dispatch.argtypes = [ctypes.c_char_p, _Z]
@@ -315,3 +322,72 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: int
     if st != 0:
         raise AttnError(st, "attn_bwd_varlen")
     return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, *, dropout_p: float, seed: int, offset: int = 0, causal: int = 0,
+                scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """O and lse with dropout on the probabilities (bf16, [B, H, S, d]).
+
+    The keep mask is a function of (seed, offset, batch, head, query, key)
+    only, so bwd_dropout with the same arguments regenerates it.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse")):
+        _check(t, n)
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    _want(k, (B, Hkv, Sk, d), torch.bfloat16, "k")
+    _want(v, (B, Hkv, Sk, d), torch.bfloat16, "v")
+    _want(q, q.shape, torch.bfloat16, "q")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Sq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, causal,
+                                sc, float(dropout_p), int(seed), int(offset), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_dropout")
+    return out, lse
+
+
+def bwd_dropout(q, k, v, o, lse, dout, *, dropout_p: float, seed: int, offset: int = 0, causal: int = 0,
+                scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of the forward that fwd_dropout computed with the same
+    dropout_p, seed and offset."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace")):
+        _check(t, n)
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    for t, n, shp in ((q, "q", q.shape), (k, "k", k.shape), (v, "v", k.shape), (o, "o", q.shape),
+                      (dout, "dout", q.shape), (dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        _want(t, shp, torch.bfloat16, n)
+    _want(lse, (B, Hq, Sq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_n = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, ATTN_BF16)
+    if workspace is None and ws_n > 0:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, Hq, Hkv, Sq, Sk, d, causal, sc, float(dropout_p), int(seed),
+                                int(offset), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dropout")
+    return dq, dk, dv
+
+
+def dropout_mask(B: int, Hq: int, Sq: int, Sk: int, *, dropout_p: float, seed: int, offset: int = 0,
+                 device="cuda", stream=None):
+    """The keep mask [B, Hq, Sq, Sk] (uint8, 1 = kept) the kernels regenerate."""
+    import torch
+    keep = torch.empty((B, Hq, Sq, Sk), dtype=torch.uint8, device=device)
+    st = lib().attn_dropout_mask(_ptr(keep), B, Hq, Sq, Sk, float(dropout_p), int(seed), int(offset),
+                                 _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_dropout_mask")
+    return keep

@@ -78,6 +78,19 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, floa
   return ATTN_OK;
 }
 
+// Dropout parameters of the generator's contract (include/attn.h).
+int make_drop(float p, unsigned long long seed, unsigned int offset, attn::DropParams& dp) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return ATTN_ERR_DROPOUT;
+  const long thr = std::lrint(p * 256.f);
+  if (thr > 255) return ATTN_ERR_DROPOUT;
+  dp.seed_lo = (uint32_t)seed;
+  dp.seed_hi = (uint32_t)(seed >> 32);
+  dp.offset = offset;
+  dp.thr = (uint32_t)thr;
+  dp.scale = 256.f / (float)(256 - thr);
+  return ATTN_OK;
+}
+
 attn::Problem make_problem(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale) {
   return attn::Problem{B, Hq, Hkv, Sq, Sk, d, causal, scale, Sq, Sk};
 }
@@ -258,6 +271,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than the query returns";
     case ATTN_ERR_HIP: return "HIP runtime error while launching";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_DROPOUT: return "dropout probability must lie in [0, 1) and round below 256/256";
     default: return "unknown status";
   }
 }
@@ -427,4 +441,65 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   record(summary);
   return ATTN_OK;
 }
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int d, int causal, float scale, float dropout_p, unsigned long long seed,
+                     unsigned int offset, void* stream) {
+  if (q == nullptr || o == nullptr || (Sk != 0 && (k == nullptr || v == nullptr))) return ATTN_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, ATTN_BF16);
+  if (st != ATTN_OK) return st;
+  attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
+  st = make_drop(dropout_p, seed, offset, p.drop);
+  if (st != ATTN_OK) return st;
+  // the tiled prefill for every shape (the split-key decode has no dropout)
+  const attn::PrefillPlan pl = attn::plan_prefill(p);
+  if (attn::launch_fwd_prefill_bf16(p, pl, q, k, v, o, lse, nullptr, (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  char line[512];
+  std::snprintf(line, sizeof(line),
+                "attn_fwd_dropout: fwd_prefill<d=%d>%s grid=%d (%d query rows x %d heads per workgroup); "
+                "keep when byte >= %u of 256",
+                d, p.drop.thr ? " with dropout" : "", pl.total_wgs, pl.rows_per_wg, pl.hw, p.drop.thr);
+  record(line);
+  return ATTN_OK;
+}
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                     int d, int causal, float scale, float dropout_p, unsigned long long seed, unsigned int offset,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr ||
+      (Sk != 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
+    return ATTN_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, ATTN_BF16);
+  if (st != ATTN_OK) return st;
+  attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
+  st = make_drop(dropout_p, seed, offset, p.drop);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn::bwd_workspace_bytes(p);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  char text[448], line[512];
+  if (attn::launch_bwd_bf16(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, (hipStream_t)stream, text,
+                            sizeof(text)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  std::snprintf(line, sizeof(line), "attn_bwd_dropout (keep when byte >= %u of 256): %s", p.drop.thr, text);
+  record(line);
+  return ATTN_OK;
+}
+
+int attn_dropout_mask(unsigned char* keep, int B, int Hq, int Sq, int Sk, float dropout_p,
+                      unsigned long long seed, unsigned int offset, void* stream) {
+  if (B < 1 || Hq < 1 || Sq < 1 || Sk < 0) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq > (1LL << 31) - 1 || Sq >= (1 << 24) || Sk >= (1 << 24)) return ATTN_ERR_SHAPE;
+  if (keep == nullptr && Sk > 0) return ATTN_ERR_NULL;
+  attn::Problem p = make_problem(B, Hq, Hq, Sq, Sk, 64, 0, 1.f);
+  const int st = make_drop(dropout_p, seed, offset, p.drop);
+  if (st != ATTN_OK) return st;
+  if (attn::launch_dropout_mask(p, keep, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+  char line[160];
+  std::snprintf(line, sizeof(line), "attn_dropout_mask: B=%d Hq=%d Sq=%d Sk=%d, keep when byte >= %u of 256", B, Hq,
+                Sq, Sk, p.drop.thr);
+  record(line);
+  return ATTN_OK;
+}
+
 }  // extern "C"

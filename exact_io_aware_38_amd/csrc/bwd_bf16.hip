@@ -88,6 +88,7 @@ struct BwdArgs {
   float c;        // scale * log2(e)
   int n_ktiles, total_kv;
   int n_qtiles, total_q;
+  DropParams drop;
 };
 
 // Workgroup order: the 8 XCDs each receive a contiguous range of logical ids
@@ -194,7 +195,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
 // step t-1, read in steps t and t+1) with its lse2/D blocks, and a 2-slot
 // exchange buffer of P and dS fragments (written in step t, read in step t+1).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, typename Tab>
+// DROP (here and in the dQ kernel): dropout with the forward's mask, so that
+// dV takes P Z and dS = P (Z dP - D), Z = keep / (1 - p).
+template <int D, bool CAUSAL, typename Tab, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
@@ -340,14 +343,25 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
       score_settle(s, dp);
       // accumulator register v holds query q0 + 8 (v >> 2) + 4 hi + (v & 3)
       float p[16], ds[16];
+      u32x4 dx;                                 // dropout: block of query rows q0 + 8g + 4hi .. +3
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float pv = fast_exp2(__builtin_fmaf(s[v], a.c, -l2v[v >> 2][v & 3]));
         if constexpr (MASK) {
           if (key > q0 + 8 * (v >> 2) + 4 * hi + (v & 3) + off) pv = 0.f;
         }
-        p[v] = pv;
-        ds[v] = pv * (dp[v] - dlv[v >> 2][v & 3]);
+        if constexpr (DROP) {
+          // this lane's key is byte (key & 3) of word (v & 3) of the block
+          if ((v & 3) == 0)
+            dx = dropout_block(a.drop, (uint32_t)(q0 + 8 * (v >> 2) + 4 * hi) >> 2, (uint32_t)key >> 2,
+                               (uint32_t)(b * a.Hq + hq));
+          const float z = ((dx[v & 3] >> (8 * (key & 3))) & 0xffu) >= a.drop.thr ? a.drop.scale : 0.f;
+          p[v] = pv * z;
+          ds[v] = pv * (z * dp[v] - dlv[v >> 2][v & 3]);
+        } else {
+          p[v] = pv;
+          ds[v] = pv * (dp[v] - dlv[v >> 2][v & 3]);
+        }
       }
       char* xs = smem + xw + (POS & 1) * XSLOT;
       *(bf16x8*)(xs + 0 * 1024) = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -585,8 +599,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
 // [K | V] row tiles: key tile t is loaded at the start of step t-2 and read in
 // steps t-1 (K, V) and t+1 (K^T).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, typename Tab>
-__global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a, Tab T) {
+template <int D, bool CAUSAL, typename Tab, bool DROP>
+__global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_kernel(BwdArgs a, Tab T) {
   constexpr int NCB = DQ_NCB;
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
@@ -768,6 +782,7 @@ __global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArg
     if constexpr (G1) fk[0] = kfr(0);
     if constexpr (G2) ft[0] = tfr(0);
     float dt[NCB][8];
+    uint32_t dword[NCB];                        // dropout: this row's 4 bytes of the current key quad
     static_for<NU>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
       if constexpr (u + 1 < NU) {
@@ -800,7 +815,18 @@ __global__ __launch_bounds__(256, DQ_NCB == 1 ? 2 : 1) void bwd_dq_kernel(BwdArg
           if constexpr (MASK) {
             if (key0 + 8 * (v >> 2) + 4 * hi + (v & 3) > lim[cb]) p = 0.f;
           }
-          dt[cb][v & 7] = p * (dp_[cb][v] - dl[cb]);
+          if constexpr (DROP) {
+            if ((v & 3) == 0) {
+              const u32x4 x = dropout_block(a.drop, (uint32_t)pos[cb] >> 2,
+                                            (uint32_t)(key0 + 8 * (v >> 2) + 4 * hi) >> 2, (uint32_t)hrow);
+              const int w = pos[cb] & 3;
+              dword[cb] = w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3];
+            }
+            const float z = ((dword[cb] >> (8 * (v & 3))) & 0xffu) >= a.drop.thr ? a.drop.scale : 0.f;
+            dt[cb][v & 7] = p * (z * dp_[cb][v] - dl[cb]);
+          } else {
+            dt[cb][v & 7] = p * (dp_[cb][v] - dl[cb]);
+          }
           pin(dt[cb][v & 7]);
           if ((v & 7) == 7) {
             dsf[P][cb][v >> 3] = to_bf16x8(dt[cb][0], dt[cb][1], dt[cb][2], dt[cb][3], dt[cb][4], dt[cb][5],
@@ -932,6 +958,22 @@ WsLayout ws_layout(const Problem& p) {
   return w;
 }
 
+template <int D, bool CAUSAL>
+void launch_dkdv(const BwdArgs& a, hipStream_t s) {
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NoTable, true>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NoTable, false>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
+}
+
+template <int D, bool CAUSAL>
+void launch_dq(const BwdArgs& a, hipStream_t s) {
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NoTable, true>), dim3(a.total_q), dim3(256), 0, s, a, NoTable{});
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NoTable, false>), dim3(a.total_q), dim3(256), 0, s, a, NoTable{});
+}
+
 template <int D>
 hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   const size_t rows = (size_t)a.B * a.Hq * a.sqp;
@@ -948,9 +990,9 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   if (a.total_kv > 0) {
     timing_begin(s, "bwd_dkdv");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, NoTable>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
+      launch_dkdv<D, true>(a, s);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, NoTable>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
+      launch_dkdv<D, false>(a, s);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -958,9 +1000,9 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   if (a.total_q > 0) {
     timing_begin(s, "bwd_dq");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true, NoTable>), dim3(a.total_q), dim3(256), 0, s, a, NoTable{});
+      launch_dq<D, true>(a, s);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false, NoTable>), dim3(a.total_q), dim3(256), 0, s, a, NoTable{});
+      launch_dq<D, false>(a, s);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -1009,6 +1051,7 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   a.total_kv = p.B * p.Hkv * a.n_ktiles;
   a.n_qtiles = (p.Sq + Q_WG - 1) / Q_WG;
   a.total_q = p.B * p.Hq * a.n_qtiles;
+  a.drop = p.drop;
   return p.d == 64 ? launch_bwd_d<64>(a, s, log, log_n) : launch_bwd_d<128>(a, s, log, log_n);
 }
 
@@ -1028,9 +1071,9 @@ hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tp, int gp, con
   if (gkv > 0) {
     timing_begin(s, "bwd_dkdv");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SeqTable>), dim3(gkv), dim3(512), 0, s, a, Tkv);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SeqTable, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SeqTable>), dim3(gkv), dim3(512), 0, s, a, Tkv);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SeqTable, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -1038,9 +1081,9 @@ hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tp, int gp, con
   if (gq > 0) {
     timing_begin(s, "bwd_dq");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true, SeqTable>), dim3(gq), dim3(256), 0, s, a, Tq);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, SeqTable, false>), dim3(gq), dim3(256), 0, s, a, Tq);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false, SeqTable>), dim3(gq), dim3(256), 0, s, a, Tq);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, SeqTable, false>), dim3(gq), dim3(256), 0, s, a, Tq);
     e = hipGetLastError();
     timing_end(s);
   }

@@ -120,6 +120,41 @@ __device__ __forceinline__ int xcd_logical_id(int linear, int total) {
   return (linear & 7) * (total >> 3) + (linear >> 3);
 }
 
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw
+// ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds of two
+// 32x32->64-bit products whose halves are mixed with the other two counter
+// words and the key; the key advances by the two Weyl constants between
+// rounds. Returns the four output words.
+__host__ __device__ inline u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    u32x4 n;
+    n[0] = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    n[1] = (uint32_t)p1;
+    n[2] = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    n[3] = (uint32_t)p0;
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The dropout bytes of one 4x4 block of the score matrix of query head bh
+// (= b * Hq + h): query rows 4 i4 .. 4 i4 + 3, keys 4 j4 .. 4 j4 + 3 (positions
+// within the sequence). Word w holds query row 4 i4 + w; byte t of it key
+// 4 j4 + t. Counter (j4, i4, bh, offset), key the 64-bit seed.
+__host__ __device__ inline u32x4 dropout_block(const DropParams& dp, uint32_t i4, uint32_t j4, uint32_t bh) {
+  u32x4 c;
+  c[0] = j4;
+  c[1] = i4;
+  c[2] = bh;
+  c[3] = dp.offset;
+  return philox4x32_10(c, dp.seed_lo, dp.seed_hi);
+}
+
 // Table parameter of a kernel launched on one dense problem.
 struct NoTable {};
 

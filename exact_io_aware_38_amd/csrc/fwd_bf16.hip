@@ -56,6 +56,7 @@ struct FwdArgs {
   float c;           // scale * log2(e)
   int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
   int nsplit, split_keys;
+  DropParams drop;
 };
 
 // ---------------------------------------------------------------------------
@@ -86,7 +87,9 @@ __device__ __forceinline__ void rebase(FwdArgs& a, const SeqTable& T, int s) {
 }
 
 // Tab: NoTable for one dense [B, H, S, d] problem, SeqTable for a packed launch.
-template <int D, typename Tab>
+// DROP: dropout on the probabilities that multiply V (the denominator counts
+// every visible key, as without dropout).
+template <int D, typename Tab, bool DROP>
 __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   using R = Ring<D>;
   constexpr int MB = D / 32;
@@ -301,11 +304,27 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
     const float msub = (m2 == kNegInf) ? 0.f : m2;
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = fast_exp2(__builtin_fmaf(v[i], a.c, -msub));
+    if constexpr (DROP) {
+      lsum += tree_sum32(v);
+      // values 4g .. 4g+3 are keys 4 j4 .. 4 j4 + 3 of this lane's query row:
+      // word (pos & 3) of block (pos / 4, j4)
+      const uint32_t bh = (uint32_t)(b * a.Hq + head);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const uint32_t j4 = (uint32_t)(key0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * hi) >> 2;
+        const u32x4 x = dropout_block(a.drop, (uint32_t)pos >> 2, j4, bh);
+        const int w = pos & 3;
+        const uint32_t word = w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (((word >> (8 * t)) & 0xffu) < a.drop.thr) v[4 * g + t] = 0.f;
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       pf[q] = to_bf16x8(v[8 * q + 0], v[8 * q + 1], v[8 * q + 2], v[8 * q + 3], v[8 * q + 4], v[8 * q + 5],
                         v[8 * q + 6], v[8 * q + 7]);
-    lsum += tree_sum32(v);
+    if constexpr (!DROP) lsum += tree_sum32(v);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -359,7 +378,8 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = sum_halves(lsum);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if constexpr (DROP) inv *= a.drop.scale;
   const float lse_v = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : kNegInf;
   if (!colv) return;
   bf16* op = a.o + (((size_t)b * a.Hq + head) * a.hsq + pos) * D;
@@ -606,10 +626,33 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
   if (lse != nullptr && lane == 0) lse[orow] = tot > 0.f ? m + __logf(tot) : kNegInf;
 }
 
+// The dropout mask as keep bytes [B, Hq, Sq, Sk]: one thread per 4x4 block.
+__global__ __launch_bounds__(256) void dropout_mask_kernel(DropParams dp, unsigned char* __restrict__ keep,
+                                                           long long blocks, int iq, int jq, int Sq, int Sk) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= blocks) return;
+  const int j4 = (int)(t % jq);
+  const int i4 = (int)((t / jq) % iq);
+  const long long bh = t / ((long long)jq * iq);
+  const u32x4 x = dropout_block(dp, (uint32_t)i4, (uint32_t)j4, (uint32_t)bh);
+  for (int w = 0; w < 4; ++w) {
+    const int i = 4 * i4 + w;
+    if (i >= Sq) break;
+    unsigned char* row = keep + ((size_t)bh * Sq + i) * Sk;
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * j4 + u;
+      if (j < Sk) row[j] = ((x[w] >> (8 * u)) & 0xffu) >= dp.thr ? 1 : 0;
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
   timing_begin(s, "fwd_prefill_bf16");
-  hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable, true>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
+  else
+    hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable, false>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
   const hipError_t e = hipGetLastError();
   timing_end(s);
   return e;
@@ -618,7 +661,7 @@ hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_prefill_packed_d(const FwdArgs& a, const SeqTable& T, int grid, hipStream_t s) {
   timing_begin(s, "fwd_prefill_bf16");
-  hipLaunchKernelGGL((fwd_prefill_kernel<D, SeqTable>), dim3(grid), dim3(512), 0, s, a, T);
+  hipLaunchKernelGGL((fwd_prefill_kernel<D, SeqTable, false>), dim3(grid), dim3(512), 0, s, a, T);
   const hipError_t e = hipGetLastError();
   timing_end(s);
   return e;
@@ -656,6 +699,7 @@ FwdArgs base_args(const Problem& p, const void* q, const void* k, const void* v,
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
   a.c = p.scale * kLog2e;
+  a.drop = p.drop;
   return a;
 }
 
@@ -724,6 +768,15 @@ hipError_t launch_fwd_prefill_bf16_packed(const Problem& p, const SeqSpan* seqs,
              T.split8 ? ", per-XCD head split" : "");
   if (grid == 0) return hipSuccess;
   return p.d == 64 ? launch_prefill_packed_d<64>(a, T, grid, s) : launch_prefill_packed_d<128>(a, T, grid, s);
+}
+
+hipError_t launch_dropout_mask(const Problem& p, unsigned char* keep, hipStream_t s) {
+  const int iq = (p.Sq + 3) / 4, jq = (p.Sk + 3) / 4;
+  const long long blocks = (long long)p.B * p.Hq * iq * jq;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s, p.drop, keep,
+                     blocks, iq, jq, p.Sq, p.Sk);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& sp, const void* q, const void* k,

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace attn {
 
@@ -20,11 +21,24 @@ void timing_end(hipStream_t s);
 // for [B, H, S, d] tensors; a sequence inside head-major packed tensors
 // [H, total, d] (B = 1, data pointers advanced to the sequence's first row)
 // has the packed totals as head strides.
+// Dropout on the attention probabilities: a probability is kept when its byte
+// of the Philox stream (see philox4x32_10 and dropout_block) is >= thr, and
+// kept values are multiplied by scale = 1 / (1 - thr / 256). thr = 0 means no
+// dropout.
+struct DropParams {
+  uint32_t seed_lo, seed_hi, offset, thr;
+  float scale;
+};
+
 struct Problem {
   int B, Hq, Hkv, Sq, Sk, d, causal;
   float scale;
   int hsq, hsk;     // head strides in rows
+  DropParams drop;
 };
+
+// keep[B, Hq, Sq, Sk] (1 = kept) of the dropout mask the kernels regenerate.
+hipError_t launch_dropout_mask(const Problem& p, unsigned char* keep, hipStream_t s);
 
 // ---- packed batches in one launch -------------------------------------------
 // A sequence of a head-major packed batch: its first packed query and key row

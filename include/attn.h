@@ -65,7 +65,8 @@ enum attn_status {
   ATTN_ERR_CAUSAL = -6,     /* causal not in {0, 1, 2} */
   ATTN_ERR_WORKSPACE = -7,  /* workspace smaller than the query says, or NULL when needed */
   ATTN_ERR_HIP = -8,        /* a HIP runtime call or kernel launch failed */
-  ATTN_ERR_SCALE = -9       /* scale not finite or not > 0 */
+  ATTN_ERR_SCALE = -9,      /* scale not finite or not > 0 */
+  ATTN_ERR_DROPOUT = -10    /* dropout probability not in [0, 1) or rounding to 1 */
 };
 
 enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
@@ -135,6 +136,36 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                     const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
                     int d, int causal, float scale, int dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* Dropout on the attention probabilities, regenerated identically by the
+ * forward and the backward ("AI 大模型之 FlashAttention_01", section
+ * "接口与实现约束": with dropout on, the mapping to random numbers is part of
+ * the contract between the two passes). The mapping is Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, SC 2011) keyed by the 64-bit `seed`: for query head h of
+ * batch b, the 4x4 block of query rows 4a..4a+3 and keys 4c..4c+3 (positions
+ * within the problem) takes counter (c, a, b*Hq + h, offset); byte t of output
+ * word w belongs to query 4a+w, key 4c+t. The probability P_ij is kept when
+ * its byte is >= thr = round(256 * dropout_p), and kept values are scaled by
+ * 1 / (1 - thr / 256): the effective dropout probability is thr / 256.
+ * dropout_p must lie in [0, 1) with thr <= 255 (else ATTN_ERR_DROPOUT). The
+ * forward keeps lse of the undropped probabilities; O = (P o Z) V with
+ * Z = keep / (1 - thr / 256). The backward with the same seed, offset and
+ * dropout_p returns the gradients of that O. bf16 only, dense [B, H, S, d]
+ * layout as attn_fwd/attn_bwd; the forward needs no workspace, the backward
+ * the one attn_bwd_workspace_bytes gives. `offset` selects an independent
+ * stream for the same seed (e.g. one per layer or step). */
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int d, int causal, float scale, float dropout_p, unsigned long long seed,
+                     unsigned int offset, void* stream);
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                     int d, int causal, float scale, float dropout_p, unsigned long long seed, unsigned int offset,
+                     void* workspace, size_t workspace_bytes, void* stream);
+/* The keep mask itself, as bytes keep[B, Hq, Sq, Sk] (1 = kept) on the device,
+ * from the same generator (for checking and debugging; causal masks are not
+ * applied). B, Hq, Sq >= 1, Sk >= 0. */
+int attn_dropout_mask(unsigned char* keep, int B, int Hq, int Sq, int Sk, float dropout_p,
+                      unsigned long long seed, unsigned int offset, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* attn_strerror(int status);

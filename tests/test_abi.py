@@ -190,3 +190,49 @@ def test_varlen_workspace_queries():
     assert attn.fwd_varlen_workspace_bytes([0, 5, 3], [0, 5, 6], 1, 1, 64, 0, bf) == 0   # invalid -> 0
     with pytest.raises(ValueError):
         attn.fwd_varlen_workspace_bytes([0, 5], [0, 5, 6], 1, 1, 64, 0, bf)
+
+
+# ---------------------------------------------------------------- dropout
+def _fwd_drop(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=16, Sk=16, d=64, causal=1,
+             scale=0.125, p=0.1, seed=1, offset=0, stream=None)
+    a.update(over)
+    return attn.lib().attn_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                       a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["p"], a["seed"],
+                                       a["offset"], a["stream"])
+
+
+def _bwd_drop(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2,
+             Sq=16, Sk=16, d=64, causal=1, scale=0.125, p=0.1, seed=1, offset=0, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(over)
+    return attn.lib().attn_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                       a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["causal"],
+                                       a["scale"], a["p"], a["seed"], a["offset"], a["ws"], a["ws_bytes"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, -1), ({"v": None}, -1), ({"Sq": 0}, -2), ({"Hq": 3}, -3), ({"d": 80}, -4),
+    ({"causal": 4}, -6), ({"scale": 0.0}, -9),
+    ({"p": -0.01}, -10), ({"p": 1.0}, -10), ({"p": 0.999}, -10), ({"p": float("nan")}, -10),
+])
+def test_fwd_dropout_validation(over, code):
+    assert _fwd_drop(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"lse": None}, -1), ({"dk": None}, -1), ({"Sk": -2}, -2), ({"p": 2.0}, -10), ({"p": float("inf")}, -10),
+    ({}, -7), ({"ws": FAKE, "ws_bytes": 4}, -7),
+])
+def test_bwd_dropout_validation(over, code):
+    assert _bwd_drop(**over) == code
+
+
+def test_dropout_mask_validation():
+    L = attn.lib()
+    assert L.attn_dropout_mask(None, 1, 1, 4, 4, 0.1, 1, 0, None) == -1
+    assert L.attn_dropout_mask(FAKE, 0, 1, 4, 4, 0.1, 1, 0, None) == -2
+    assert L.attn_dropout_mask(FAKE, 1, 1, 4, 4, 1.5, 1, 0, None) == -10
+    assert "dropout" in attn.strerror(-10)
