@@ -87,10 +87,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_bwd needs: the per-row terms D_i = dO_i . O_i
- * and lse_i * log2(e) (float32, [B, Hq, Sq'] with Sq' = Sq rounded up to 64)
- * and a transposed copy K^T (bf16 [B, Hkv, d, Sk'], Sk' = Sk rounded up to
- * 64), each region 256-byte aligned. The contents are scratch: nothing is
- * kept between calls. */
+ * and lse_i * log2(e) (float32, 2 * B * Hq * Sq' values with Sq' = Sq rounded
+ * up to 64, stored per 32 rows as [lse2 x 32 | D x 32]), rounded up to 256
+ * bytes. The contents are scratch: nothing is kept between calls. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                 int causal, int dtype);
 
