@@ -7,8 +7,10 @@ training workload). The same run also times the long-context causal forward
 (B=2, H=32, S=8192, d=128, 1% of query rows x30) and the grouped-query decode
 (B=16, Hq=32, Hkv=8, one query row against 32768 keys) and a packed batch of
 16 causal sequences of 512..3584 tokens (forward + backward through the
-variable-length entry points), which report as their own sub-objects. Inputs
-are resident in device memory before timing starts.
+variable-length entry points) and the long-context forward on MXFP8 operands
+(attn_fwd_fp8 on inputs quantised beforehand; the quantisers are timed on
+their own), which report as their own sub-objects. Inputs are resident in
+device memory before timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration          (a plain copy of known size,
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s fwd & fwd+bwd, bf16 d=128 causal S=8K; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 CSRC = os.path.join(ROOT, "exact_io_aware_38_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -45,6 +48,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
     "bwd_dq": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
     "bwd_pre": ["bwd_bf16.hip", "common.h", "kernels.h"],
+    "fwd_fp8": ["fwd_fp8.hip", "common.h", "kernels.h", "tiles.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
 # (the dense and the packed instantiations both match; a workload uses one)
@@ -54,6 +58,7 @@ KERNEL_SYMBOLS = {
     "bwd_dkdv": "bwd_dkdv_kernel<128,",
     "bwd_dq": "bwd_dq_kernel<128,",
     "bwd_pre": "bwd_pre_kernel<128,",
+    "fwd_fp8": "fwd_fp8_kernel<128>",
 }
 
 
@@ -83,6 +88,8 @@ def kernel_work(kernel: str, w) -> dict:
     e = 2  # bf16 bytes
     if kernel == "fwd_prefill_bf16":
         return {"bound": "mfma", "flops": fwd}
+    if kernel == "fwd_fp8":
+        return {"bound": "mfma", "flops": fwd, "peak": PEAK_FP8_TFLOPS}
     if kernel == "bwd_dkdv":
         return {"bound": "mfma", "flops": 2.0 * fwd}
     if kernel == "bwd_dq":
@@ -118,7 +125,7 @@ def roofline(kernel: str, w, avg_ms: float, work: dict = None) -> dict:
     work = kernel_work(kernel, w) if work is None else work
     if work["bound"] == "mfma":
         ach = work["flops"] / (avg_ms * 1e-3) / 1e12
-        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+        peak, unit = work.get("peak", PEAK_BF16_TFLOPS), "TFLOP/s"
     else:
         ach = work["bytes"] / (avg_ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
@@ -208,6 +215,39 @@ def bench_fwd(attn, steps, warmup):
             "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
             "roofline": roofline("fwd_prefill_bf16", w, kern["fwd_prefill_bf16"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
+
+
+def bench_fp8(attn, steps, warmup):
+    """The long-context forward on MXFP8 operands: the inputs are quantised
+    once before timing (as FP8 attention takes FP8 operands); the timed step
+    is attn_fwd_fp8 alone. The quantisers are timed separately."""
+    import torch
+    import synth
+    w = synth.get_workload("long_causal_d128")
+    t = _device_inputs(w)
+    q8, qs = attn.mxfp8_quantize_rows(t["q"])
+    k8, ks = attn.mxfp8_quantize_rows(t["k"])
+    vt8, vts = attn.mxfp8_quantize_vt(t["v"])
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
+    ms, kern = _time(lambda: attn.fwd_fp8(q8, qs, k8, ks, vt8, vts, causal=w.causal, scale=w.scale, out=o,
+                                          lse=lse), steps, warmup, attn)
+
+    def quant():
+        attn.mxfp8_quantize_rows(t["q"], codes=q8, scales=qs)
+        attn.mxfp8_quantize_rows(t["k"], codes=k8, scales=ks)
+        attn.mxfp8_quantize_vt(t["v"])
+
+    qms, qkern = _time(quant, max(3, steps // 4), 1, attn)
+    flops = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
+    return {"workload": w.name + "_mxfp8", "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d, "causal": w.causal,
+            "dtype": "e4m3 (MXFP8 operands), fp32 accumulation", "ms": round(ms, 4),
+            "tflops": round(flops / ms / 1e9, 2),
+            "frac_of_fp8_peak": round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline("fwd_fp8", w, kern["fwd_fp8"]),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+            "quantise_ms": round(qms, 4), "quantise_kernels_ms": {k: round(v, 4) for k, v in qkern.items()}}
 
 
 def bench_decode(attn, steps, warmup):
@@ -391,7 +431,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen"], default="all")
+    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen", "fp8"], default="all")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5,
                     metavar=("WORKLOAD", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -436,6 +476,10 @@ def main() -> int:
         result["fwd"] = bench_fwd(attn, args.steps, args.warmup)
         print(f"# fwd: {result['fwd']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+    if args.only in ("all", "fp8"):
+        result["fp8"] = bench_fp8(attn, args.steps, args.warmup)
+        print(f"# fp8: {result['fp8']['ms']} ms", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         result["decode"] = bench_decode(attn, max(args.steps, 20), args.warmup)
         print(f"# decode: {result['decode']['ms']} ms", file=sys.stderr, flush=True)
@@ -448,6 +492,9 @@ def main() -> int:
         result.update({"value": result["varlen"]["tflops"], "ms_per_step": result["varlen"]["ms"],
                        "config": {"workload": result["varlen"]["workload"]},
                        "roofline": result["varlen"]["roofline"]})
+    if args.only == "fp8":
+        result.update({"value": result["fp8"]["tflops"], "ms_per_step": result["fp8"]["ms"], "dtype": "e4m3",
+                       "config": {"workload": result["fp8"]["workload"]}, "roofline": result["fp8"]["roofline"]})
     if args.only == "fwd":
         result.update({"value": result["fwd"]["tflops"], "ms_per_step": result["fwd"]["ms"],
                        "config": {"workload": result["fwd"]["workload"]}, "roofline": result["fwd"]["roofline"]})

@@ -17,6 +17,7 @@ __all__ = [
     "fwd_workspace_bytes", "bwd_workspace_bytes", "strerror", "last_dispatch",
     "timing_start", "timing_stop", "fwd_varlen", "bwd_varlen", "fwd_varlen_workspace_bytes",
     "bwd_varlen_workspace_bytes", "fwd_dropout", "bwd_dropout", "dropout_mask",
+    "fp8_padded_keys", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fwd_fp8",
 ]
 
 ATTN_F32 = 0
@@ -78,6 +79,14 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_dropout.restype = _I
         L.attn_dropout_mask.argtypes = [_P, _I, _I, _I, _I] + _DROP + [_P]
         L.attn_dropout_mask.restype = _I
+        L.attn_fp8_padded_keys.argtypes = [_I]
+        L.attn_fp8_padded_keys.restype = _I
+        L.attn_mxfp8_quantize_rows.argtypes = [_P, _P, _P, ctypes.c_longlong, _I, _P]
+        L.attn_mxfp8_quantize_rows.restype = _I
+        L.attn_mxfp8_quantize_vt.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+        L.attn_mxfp8_quantize_vt.restype = _I
+        L.attn_fwd_fp8.argtypes = [_P] * 8 + _SHAPE + [_F, _P]
+        L.attn_fwd_fp8.restype = _I
         L.attn_strerror.argtypes = [_I]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_dispatch.argtypes = [ctypes.c_char_p, _Z]
@@ -391,3 +400,82 @@ def dropout_mask(B: int, Hq: int, Sq: int, Sk: int, *, dropout_p: float, seed: i
     if st != 0:
         raise AttnError(st, "attn_dropout_mask")
     return keep
+
+
+def fp8_padded_keys(Sk: int) -> int:
+    """Keys of the transposed FP8 V: Sk rounded up to a multiple of 64."""
+    n = int(lib().attn_fp8_padded_keys(int(Sk)))
+    if n < 0:
+        raise AttnError(n, "attn_fp8_padded_keys")
+    return n
+
+
+def mxfp8_quantize_rows(x, *, codes=None, scales=None, stream=None):
+    """bf16 [..., d] -> (E4M3 codes uint8 [..., d], E8M0 scales uint8 [..., d/32])."""
+    import torch
+    _check(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], d // 32), dtype=torch.uint8, device=x.device)
+    _check(codes, "codes")
+    _check(scales, "scales")
+    _want(codes, x.shape, torch.uint8, "codes")
+    _want(scales, (*x.shape[:-1], d // 32), torch.uint8, "scales")
+    st = lib().attn_mxfp8_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_mxfp8_quantize_rows")
+    return codes, scales
+
+
+def mxfp8_quantize_vt(v, *, stream=None):
+    """bf16 V [B, Hkv, Sk, d] -> (V^T codes uint8 [B, Hkv, d, Skp],
+    scales uint8 [B, Hkv, Skp/64, d, 2]), Skp = fp8_padded_keys(Sk)."""
+    import torch
+    _check(v, "v")
+    if v.dtype != torch.bfloat16:
+        raise TypeError("v must be bfloat16")
+    B, H, Sk, d = v.shape
+    skp = fp8_padded_keys(Sk)
+    codes = torch.empty((B, H, d, skp), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((B, H, skp // 64, d, 2), dtype=torch.uint8, device=v.device)
+    st = lib().attn_mxfp8_quantize_vt(_ptr(v), _ptr(codes), _ptr(scales), B * H, Sk, d, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_mxfp8_quantize_vt")
+    return codes, scales
+
+
+def fwd_fp8(q8, q_scales, k8, k_scales, vt8, vt_scales, *, causal: int = 0, scale: Optional[float] = None,
+            out=None, lse=None, need_lse: bool = True, stream=None):
+    """Forward on MXFP8 operands (as the two quantisers give them): returns
+    (o bf16 [B, Hq, Sq, d], lse float32 [B, Hq, Sq] or None)."""
+    import torch
+    for t, n in ((q8, "q8"), (q_scales, "q_scales"), (k8, "k8"), (k_scales, "k_scales"), (vt8, "vt8"),
+                 (vt_scales, "vt_scales"), (out, "out"), (lse, "lse")):
+        _check(t, n)
+    B, Hq, Sq, d = q8.shape
+    _, Hkv, Sk, _ = k8.shape
+    skp = fp8_padded_keys(Sk)
+    u8 = torch.uint8
+    _want(q8, (B, Hq, Sq, d), u8, "q8")
+    _want(q_scales, (B, Hq, Sq, d // 32), u8, "q_scales")
+    _want(k8, (B, Hkv, Sk, d), u8, "k8")
+    _want(k_scales, (B, Hkv, Sk, d // 32), u8, "k_scales")
+    _want(vt8, (B, Hkv, d, skp), u8, "vt8")
+    _want(vt_scales, (B, Hkv, skp // 64, d, 2), u8, "vt_scales")
+    _want(out, (B, Hq, Sq, d), torch.bfloat16, "out")
+    _want(lse, (B, Hq, Sq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and need_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    st = lib().attn_fwd_fp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(vt8), _ptr(vt_scales),
+                            _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, causal, sc, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
+    return out, lse

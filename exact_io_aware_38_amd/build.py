@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip", "fwd_fp8.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 arithmetic is switched off for all device code.
@@ -30,7 +30,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # scores every tile). The backward kernels need more than 256 registers per
 # lane; there the accumulators that only MFMAs touch are best left in AGPRs.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-PER_SOURCE = {"fwd_bf16.hip": VGPR_FORM, "fwd_f32.hip": VGPR_FORM}
+PER_SOURCE = {"fwd_bf16.hip": VGPR_FORM, "fwd_f32.hip": VGPR_FORM, "fwd_fp8.hip": VGPR_FORM}
 
 
 def _hipcc() -> str:

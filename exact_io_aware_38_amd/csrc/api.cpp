@@ -502,4 +502,54 @@ int attn_dropout_mask(unsigned char* keep, int B, int Hq, int Sq, int Sk, float 
   return ATTN_OK;
 }
 
+int attn_fp8_padded_keys(int Sk) {
+  if (Sk < 0 || Sk >= (1 << 24)) return ATTN_ERR_SHAPE;
+  return attn::fp8_padded_keys(Sk);
+}
+
+int attn_mxfp8_quantize_rows(const void* x, void* codes, void* scales, long long rows, int d, void* stream) {
+  if (rows < 0) return ATTN_ERR_SHAPE;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if (rows > (1LL << 31) - 1) return ATTN_ERR_SHAPE;
+  if (rows > 0 && (x == nullptr || codes == nullptr || scales == nullptr)) return ATTN_ERR_NULL;
+  if (attn::launch_mx_quant_rows(x, codes, scales, rows, d, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+  char line[128];
+  std::snprintf(line, sizeof(line), "attn_mxfp8_quantize_rows: %lld rows of d=%d", rows, d);
+  record(line);
+  return ATTN_OK;
+}
+
+int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int BH, int Sk, int d, void* stream) {
+  if (BH < 1 || Sk < 0 || Sk >= (1 << 24)) return ATTN_ERR_SHAPE;
+  if ((long long)BH * Sk > (1LL << 31) - 1) return ATTN_ERR_SHAPE;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if (Sk > 0 && (v == nullptr || vt_codes == nullptr || vt_scales == nullptr)) return ATTN_ERR_NULL;
+  if (attn::launch_mx_quant_vt(v, vt_codes, vt_scales, BH, Sk, d, (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  char line[128];
+  std::snprintf(line, sizeof(line), "attn_mxfp8_quantize_vt: %d heads x %d keys of d=%d (padded to %d)", BH, Sk, d,
+                attn::fp8_padded_keys(Sk));
+  record(line);
+  return ATTN_OK;
+}
+
+int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales, const void* vt8,
+                 const void* vt_scales, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                 int causal, float scale, void* stream) {
+  if (q8 == nullptr || q_scales == nullptr || o == nullptr ||
+      (Sk != 0 && (k8 == nullptr || k_scales == nullptr || vt8 == nullptr || vt_scales == nullptr)))
+    return ATTN_ERR_NULL;
+  const int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, ATTN_BF16);
+  if (st != ATTN_OK) return st;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
+  char text[400], line[480];
+  if (attn::launch_fwd_fp8(p, q8, q_scales, k8, k_scales, vt8, vt_scales, o, lse, (hipStream_t)stream, text,
+                           sizeof(text)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  std::snprintf(line, sizeof(line), "attn_fwd_fp8: %s", text);
+  record(line);
+  return ATTN_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,557 @@
+// Forward attention on MXFP8 inputs (gfx950 block-scaled FP8 MFMA).
+//
+// "Flash Attention FA1->FA4 / pre-training practice" §2.2: FA3 runs
+// attention in FP8, at twice the bf16 matrix rate, and keeps it accurate by
+// quantising per block. Here the blocks are the OCP Microscaling ones: 32
+// E4M3 values share one power-of-two scale (an E8M0 byte). gfx950's
+// v_mfma_scale_f32_32x32x64_f8f6f4 applies such scales itself: each row of
+// A and column of B takes one scale byte per 32 values of the reduction, so
+// the scales of Q, K and V cost nothing inside the loop.
+//
+// Operand formats (produced by the quantisers below):
+//  * Q, K: codes [B, H, S, d] (row-major, like the bf16 tensors), scales
+//    [B, H, S, d/32]: one per 32 channels of a row;
+//  * V, transposed: codes [B, Hkv, d, Skp] (Skp = Sk rounded up to 64, the
+//    padding zero), scales [B, Hkv, Skp/64, d, 2]: one per 32 keys of a
+//    channel, grouped per 64-key tile so that a tile's scales are 256
+//    contiguous bytes. V is blocked along the keys because the P V product
+//    sums over them, and it is stored transposed because V^T is the A
+//    operand of O^T = V^T P^T.
+//
+// The recurrence is the bf16 prefill's (online softmax over 64-key tiles,
+// two wavefronts per SIMD in opposite phases, a 4-stage LDS ring fed by LDS
+// DMA two tiles ahead), with these changes:
+//  * operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured with an
+//    in-bounds probe of the builtin): lane l holds row (A) or column (B)
+//    l % 32; its operand bytes 0..15 lie in k-block 0 (k 0..31), bytes 16..31
+//    in k-block 1 (k 32..63); the scale byte of lane half h applies to
+//    k-block h of that row or column, i.e. to bytes 16h .. 16h+15 of both
+//    lane halves; opsel n picks byte n of the scale register. Here lane half
+//    h supplies the h-th 16 values of each k-block, so each k-block is 32
+//    consecutive channels (one MX block of Q or K) or 32 consecutive keys
+//    (one MX block of V);
+//  * scores: S^T = K Q^T on 32x32x64 FP8 MFMAs (two per 32x32 block at
+//    d = 128). The A operand of block c takes key rows in the order
+//    kappa_c(r) = 32 c + 16 ((r >> 2) & 1) + 4 (r >> 3) + (r & 3), so that
+//    accumulator register i of block c in lane half H is key 32 c + 16 H + i;
+//  * probabilities: rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even) and fed
+//    from registers as the B operand of O^T = V^T P^T: byte 16 c + i of lane
+//    half H is key 32 c + 16 H + i, exactly the k slot the layout above gives
+//    it; the matching A operand is two 16-byte LDS reads of the V^T tile
+//    (keys 16 H .. +15 and 32 + 16 H .. +15). To keep small probabilities
+//    out of the E4M3 subnormals, P is formed relative to m - 6 (2^6 times the probability)
+//    and the reference max moves only when a row max grows by more than 2, so
+//    P stays <= 2^8 < 448; the denominator carries the same factor, so u / l
+//    is unchanged and lse subtracts it.
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+#include <cstdio>
+
+namespace attn {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint8_t u8;
+
+constexpr int F8_BC = 64;               // keys per tile
+constexpr float F8_RESCALE_T = 2.0f;    // log2 units
+constexpr float F8_PSHIFT = 6.0f;       // P = 2^6 exp2(s - m) <= 2^(6 + F8_RESCALE_T)
+constexpr int E8M0_ONE = 127;           // scale byte of 1.0
+
+struct Fp8Args {
+  const u8* q;
+  const u8* qs;
+  const u8* k;
+  const u8* ks;
+  const u8* vt;
+  const u8* vs;
+  bf16* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk, Skp, g, causal;
+  float c;                              // scale * log2(e)
+  int hw, n_hgroups, rows_per_wg, n_ptiles, total_wgs;
+};
+
+// D = 128 stage: [K tile | V^T tile | K scales | V scales]
+template <int D>
+struct Fp8Ring {
+  static constexpr int KT = F8_BC * D;          // K tile bytes (64 rows of D)
+  static constexpr int VT = D * F8_BC;          // V^T tile bytes (D rows of 64 keys)
+  static constexpr int KS = F8_BC * (D / 32);   // K scale bytes
+  static constexpr int VS = D * 2;              // V scale bytes
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = KT;
+  static constexpr int KS_OFF = KT + VT;
+  static constexpr int VS_OFF = KS_OFF + KS;
+  static constexpr int STAGE = VS_OFF + VS;
+  static constexpr int NSTAGE = 4;
+};
+
+// S^T / O^T product with per-lane E8M0 scales (byte OPA of sa for the A
+// operand's 32 values, byte OPB of sb for the B operand's); both formats E4M3.
+template <int OPA, int OPB>
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, int sa, i32x8 b, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPA, sa, OPB, sb);
+}
+
+// Key row that lane row r of the score A operand loads for key block c.
+__device__ __forceinline__ int kappa(int c, int r) { return 32 * c + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// LDS chunk swizzles (16-byte chunks XOR-permuted per row): K rows are 128
+// bytes, V^T rows 64. With them each 16-lane group of a 16-byte fragment read
+// touches 16 distinct 16-byte bank groups (the 16 key rows kappa_c(r),
+// r = 0..15 or 16..31, resp. 16 consecutive channels).
+__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
+__device__ __forceinline__ int swz_v(int row) { return (row >> 2) & 3; }
+
+__device__ __forceinline__ i32x8 cat_u32x4(u32x4 a, u32x4 b) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
+  static_assert(D == 128, "the FP8 path is built for d = 128");
+  using R = Fp8Ring<D>;
+  constexpr int DC = D / 64;                    // MFMAs per 32x32 score block
+  constexpr int MB = D / 32;                    // 32-channel blocks of the output
+  constexpr int NSB = D / 32;                   // scale bytes per Q or K row
+  static_assert(R::NSTAGE == 4, "the main loop is unrolled by the ring size");
+  static_assert(R::KT == 8 * 1024 && R::VT == 8 * 1024, "one 1 KB DMA instruction per wavefront per tensor");
+
+  __shared__ __attribute__((aligned(1024))) char smem[R::NSTAGE * R::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const bool phase_b = wid >= 4;
+
+  const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
+  const int ptile = a.n_ptiles - 1 - (W % a.n_ptiles);     // longest causal tiles first
+  int rest = W / a.n_ptiles;
+  const int hgrp = rest % a.n_hgroups;
+  rest /= a.n_hgroups;
+  const int hkv = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+
+  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
+  const int slot = (wid & 3) * 2 + (wid >> 2);
+  const int head = hkv * a.g + hgrp * a.hw + slot % a.hw;
+  const int p0 = ptile * a.rows_per_wg + 32 * (slot / a.hw);
+  const int pos = p0 + l32;
+  const bool colv = pos < a.Sq;
+  const int wg_last = min((ptile + 1) * a.rows_per_wg, a.Sq) - 1;
+  int kend = a.causal ? min(a.Sk, wg_last + off + 1) : a.Sk;
+  if (kend < 0) kend = 0;
+  const int ntiles = (kend + F8_BC - 1) / F8_BC;
+  const int mask_from = a.causal ? max(0, min(kend, p0 + off + 1)) : kend;
+  const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
+
+  // Q fragments (B operand of S^T): lane (hi, l32) holds row pos, channels
+  // 64 dc + 16 hi .. +15 (k-block 0) and 64 dc + 32 + 16 hi .. +15 (k-block
+  // 1). Lane half hi supplies the scale of k-block hi, i.e. of channel block
+  // 2 dc + hi, in byte 2 dc of qsc (the row's four scale bytes shifted right
+  // by 8 hi). Rows past Sq hold zeros (scale byte 0, not NaN).
+  i32x8 qf[DC];
+  int qsc;
+  {
+    const size_t row = ((size_t)b * a.Hq + head) * a.Sq + (colv ? pos : 0);
+    const u8* qp = a.q + row * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = colv ? cat_u32x4(*(const u32x4*)(qp + 64 * dc + 16 * hi), *(const u32x4*)(qp + 64 * dc + 32 + 16 * hi))
+                    : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    qsc = colv ? (int)((*(const uint32_t*)(a.qs + row * NSB)) >> (8 * hi)) : 0;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
+    qsc = settle(qsc);
+  }
+  const size_t kvh = (size_t)b * a.Hkv + hkv;
+  const u8* kg = a.k + kvh * (size_t)a.Sk * D;
+  const u8* ksg = a.ks + kvh * (size_t)a.Sk * NSB;
+  const u8* vtg = a.vt + kvh * (size_t)D * a.Skp;
+  const u8* vsg = a.vs + kvh * (size_t)(a.Skp / F8_BC) * (2 * D);
+
+  // LDS read offsets. K: block c, d-chunk dc, k-block hh (bytes 16 hh .. of
+  // the lane's 32): row kappa_c(l32), logical chunk 4 dc + 2 hh + hi. V^T:
+  // channel row 32 mb + l32 (mb is an immediate offset: it does not change
+  // the row's swizzle bits), logical chunk 2 hh + hi.
+  uint32_t kb[2][DC][2], vb[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int kr = kappa(c, l32);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        kb[c][dc][hh] = R::K_OFF + kr * D + (((4 * dc + 2 * hh + hi) ^ swz_k(kr)) << 4);
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) vb[hh] = R::V_OFF + l32 * F8_BC + (((2 * hh + hi) ^ swz_v(l32)) << 4);
+  const uint32_t ksb0 = R::KS_OFF + 4 * kappa(0, l32), ksb1 = R::KS_OFF + 4 * kappa(1, l32);
+  const uint32_t vsb = R::VS_OFF + 2 * l32 + hi;
+
+  // DMA geometry: wavefront wid writes the 1 KB of LDS at wid * 1024 of the K
+  // tile and of the V^T tile; lane i the 16-byte chunk P = 64 wid + i.
+  // K: row P / 8, physical chunk P % 8; V^T: channel P / 4, chunk P % 4.
+  uint32_t koff, voff;
+  {
+    const int P = wid * 64 + lane;
+    const int kr = P / 8, vr = P / 4;
+    koff = kr * D + (((P % 8) ^ swz_k(kr)) << 4);
+    voff = vr * a.Skp + (((P % 4) ^ swz_v(vr)) << 4);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const uint32_t ldsw = lds0 + wid * 1024;
+  // wavefronts 0 and 1 also load the tile's K scales and V scales (4 bytes a lane)
+  const bool scale_dma = wid < 2;
+
+  struct Dma {
+    u32x4 rk, rv, rs;
+  };
+  auto dma_for = [&](int t) __attribute__((always_inline)) {
+    Dma d;
+    const int tt = min(t, ntiles - 1);
+    const int key0 = tt * F8_BC;
+    d.rk = buffer_rsrc(kg + (size_t)key0 * D, (uint32_t)(kend - key0) * D);
+    d.rv = buffer_rsrc(vtg + key0, (uint32_t)(D * a.Skp - key0));
+    if (wid == 0) d.rs = buffer_rsrc(ksg + (size_t)key0 * NSB, (uint32_t)(kend - key0) * NSB);
+    else d.rs = buffer_rsrc(vsg + (size_t)tt * (2 * D), 2 * D);
+    return d;
+  };
+  // DMA instruction QI into ring slot SLOT: 0 = K, 1 = V^T, 2 = scales
+  auto issue_one = [&](auto slot_, auto qi_, const Dma& d) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_)::value;
+    constexpr int QI = decltype(qi_)::value;
+    if constexpr (QI == 0) dma16b_at<SLOT * R::STAGE + R::K_OFF>(d.rk, koff, 0u, ldsw);
+    else if constexpr (QI == 1) dma16b_at<SLOT * R::STAGE + R::V_OFF>(d.rv, voff, 0u, ldsw);
+    else if (scale_dma) {
+      if (wid == 0) dma4b_at<SLOT * R::STAGE + R::KS_OFF>(d.rs, 4 * lane, 0u, lds0);
+      else dma4b_at<SLOT * R::STAGE + R::VS_OFF>(d.rs, 4 * lane, 0u, lds0);
+    }
+  };
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+  float m2 = kNegInf, lsum = 0.f;
+  i32x8 pf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  f32x16 s[2];
+
+  // Step j (slot position POS = j mod 4): S(j) = K_j Q^T (4 MFMAs, two
+  // chains: pair i is key block i & 1, d-chunk i >> 1) interleaved with
+  // O^T += V_{j-1}^T P_{j-1}^T (one MFMA per 32-channel block), operand
+  // fragments one pair ahead; the DMA of tile j+2 is spread over the pairs.
+  auto mma = [&](auto pos_, auto do_s, auto do_pv, int j) __attribute__((always_inline)) {
+    constexpr int POS = decltype(pos_)::value;
+    constexpr bool DS = decltype(do_s)::value;
+    constexpr bool DP = decltype(do_pv)::value;
+    constexpr int SK = POS;                     // K of tile j
+    constexpr int SV = (POS + 3) % 4;           // V of tile j-1
+    constexpr int SD = (POS + 2) % 4;           // DMA target: tile j+2
+    const char* stk = smem + SK * R::STAGE;
+    const char* stv = smem + SV * R::STAGE;
+    auto kfrag = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      return cat_u32x4(*(const u32x4*)(stk + kb[i & 1][i >> 1][0]), *(const u32x4*)(stk + kb[i & 1][i >> 1][1]));
+    };
+    auto vfrag = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int mb = decltype(mc)::value;
+      return cat_u32x4(*(const u32x4*)(stv + vb[0] + mb * 32 * F8_BC), *(const u32x4*)(stv + vb[1] + mb * 32 * F8_BC));
+    };
+    Dma d;
+    if constexpr (DS) d = dma_for(j + 2);
+    int ksc[2] = {0, 0}, vsc[MB];
+    i32x8 kq[2], vq[2];
+    if constexpr (DS) {
+      ksc[0] = (int)(*(const uint32_t*)(stk + ksb0) >> (8 * hi));
+      ksc[1] = (int)(*(const uint32_t*)(stk + ksb1) >> (8 * hi));
+      kq[0] = kfrag(std::integral_constant<int, 0>{});
+    }
+    if constexpr (DP) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) vsc[mb] = (int)*(const u8*)(stv + vsb + mb * 64);
+      vq[0] = vfrag(std::integral_constant<int, 0>{});
+    }
+    __builtin_amdgcn_s_setprio(1);
+    static_for<4>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 1 < 4) {
+        if constexpr (DS) kq[(i + 1) & 1] = kfrag(std::integral_constant<int, i + 1>{});
+        if constexpr (DP) vq[(i + 1) & 1] = vfrag(std::integral_constant<int, i + 1>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DS)
+        s[i & 1] = mfma_f8<2 * (i >> 1), 2 * (i >> 1)>(kq[i & 1], ksc[i & 1], qf[i >> 1], qsc,
+                                                         i < 2 ? f32x16{} : s[i & 1]);
+      if constexpr (DP) acc[i] = mfma_f8<0, 0>(vq[i & 1], vsc[i], pf, E8M0_ONE, acc[i]);
+      if constexpr (DS && i < 3) issue_one(std::integral_constant<int, SD>{}, std::integral_constant<int, i>{}, d);
+    });
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int key0 = j * F8_BC;
+    float v[32];                                // v[u]: key key0 + 32 (u >> 4) + 16 hi + (u & 15)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = s[0][i];
+      v[16 + i] = s[1][i];
+    }
+    if (key0 + F8_BC > mask_from) {
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (key0 + 32 * (u >> 4) + 16 * hi + (u & 15) > lim) v[u] = kNegInf;
+    }
+    const float mx = max_halves(tree_max32(v)) * a.c;
+    const bool grow = mx > m2 + F8_RESCALE_T;
+    if (wave_any(grow)) {
+      const float mnew = grow ? mx : m2;
+      const float alpha = grow ? fast_exp2(m2 - mnew) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+      m2 = mnew;
+    }
+    const float msub = (m2 == kNegInf) ? 0.f : m2 - F8_PSHIFT;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = fast_exp2(__builtin_fmaf(v[u], a.c, -msub));
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w], v[4 * w + 1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2], v[4 * w + 3], x, true);
+    }
+    lsum += tree_sum32(v);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // step j: every wavefront's DMA of tile j has landed (each waits for its
+  // own: 2 or 3 instructions a step may still be in flight, those of tile
+  // j+1), and every wavefront is done with step j-1
+  auto sync = [&]() __attribute__((always_inline)) {
+    if (scale_dma) asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+  };
+  auto full = [&](auto pos_, int j) __attribute__((always_inline)) {
+    sync();
+    if (phase_b) softmax(j - 1);
+    mma(pos_, T_{}, T_{}, j);
+    if (!phase_b) softmax(j);
+  };
+
+  if (ntiles > 0) {
+    const Dma d0 = dma_for(0), d1 = dma_for(1);
+    static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I0{}, qi, d0); });
+    static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I1{}, qi, d1); });
+    sync();
+    mma(I0{}, T_{}, F_{}, 0);
+    if (!phase_b) softmax(0);
+  }
+  int j = 1;
+  for (; j + 3 < ntiles; j += 4) {
+    full(I1{}, j);
+    full(I2{}, j + 1);
+    full(I3{}, j + 2);
+    full(I0{}, j + 3);
+  }
+  if (j < ntiles) full(I1{}, j);
+  if (j + 1 < ntiles) full(I2{}, j + 1);
+  if (j + 2 < ntiles) full(I3{}, j + 2);
+  if (ntiles > 0) {
+    if (phase_b) softmax(ntiles - 1);
+    switch (ntiles & 3) {
+      case 0: mma(I0{}, F_{}, T_{}, ntiles); break;
+      case 1: mma(I1{}, F_{}, T_{}, ntiles); break;
+      case 2: mma(I2{}, F_{}, T_{}, ntiles); break;
+      default: mma(I3{}, F_{}, T_{}, ntiles); break;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const float lt = sum_halves(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m2 - F8_PSHIFT + __log2f(lt)) * kLn2 : kNegInf;
+  if (!colv) return;
+  const size_t orow = ((size_t)b * a.Hq + head) * a.Sq + pos;
+  bf16* op = a.o + orow * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 r;
+      r[0] = (bf16)(acc[mb][4 * q4 + 0] * inv);
+      r[1] = (bf16)(acc[mb][4 * q4 + 1] * inv);
+      r[2] = (bf16)(acc[mb][4 * q4 + 2] * inv);
+      r[3] = (bf16)(acc[mb][4 * q4 + 3] * inv);
+      *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi) = r;
+    }
+  if (a.lse != nullptr && hi == 0) a.lse[orow] = lse_v;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantisers. Block exponent: the smallest e with amax <= 448 * 2^e
+// (amax = f 2^E with f in [0.5, 1) and 448 = 0.875 * 2^9 give
+// e = E - 9 + (f > 0.875)), 0 for an all-zero block, clamped to [-127, 127];
+// elements are x * 2^-e (exact) rounded to E4M3, nearest even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float f = frexpf(amax, &E);
+  const int e = E - 9 + (f > 0.875f ? 1 : 0);
+  return max(-127, min(127, e));
+}
+
+// Four bf16 pairs scaled by 2^-e into 8 E4M3 bytes (two words).
+__device__ __forceinline__ u32x2 e4m3x8(const float* x, int e) {
+  u32x2 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int t = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * w], -e), ldexpf(x[4 * w + 1], -e), 0, false);
+    t = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * w + 2], -e), ldexpf(x[4 * w + 3], -e), t, true);
+    r[w] = (uint32_t)t;
+  }
+  return r;
+}
+
+// Rows of 32-element blocks: 4 lanes per block, 8 bf16 each.
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16* __restrict__ x, u8* __restrict__ codes,
+                                                            u8* __restrict__ scales, long long nblocks) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long blk = t >> 2;
+  const int part = (int)(t & 3);
+  const bool valid = blk < nblocks;
+  float xv[8];
+  u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+  if (valid) raw = *(const u32x4*)(x + blk * 32 + part * 8);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xv[2 * i] = __uint_as_float(raw[i] << 16);
+    xv[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(xv[2 * i]), fabsf(xv[2 * i + 1])));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = mx_exponent(amax);
+  if (!valid) return;
+  *(u32x2*)(codes + blk * 32 + part * 8) = e4m3x8(xv, e);
+  if (part == 0) scales[blk] = (u8)(e + 127);
+}
+
+// V [BH, Sk, D] bf16 -> V^T codes [BH, D, Skp] and scales [BH, Skp/64, D, 2]:
+// one workgroup per (head, 64-key tile); thread (c, kb) quantises the 32 keys
+// 32 kb .. of channel c. Keys past Sk count as zeros.
+template <int D>
+__global__ __launch_bounds__(2 * D) void mx_quant_vt_kernel(const bf16* __restrict__ v, u8* __restrict__ codes,
+                                                            u8* __restrict__ scales, int Sk, int Skp) {
+  constexpr int LD = D + 2;                      // padded LDS row (bf16 elements)
+  __shared__ bf16 tile[F8_BC * LD];
+  const int ntile = Skp / F8_BC;
+  const int t = blockIdx.x % ntile;
+  const size_t bh = blockIdx.x / ntile;
+  const int key0 = t * F8_BC;
+  const bf16* src = v + (bh * Sk + key0) * (size_t)D;
+  // stage the tile: F8_BC * D / 8 chunks of 8 bf16
+  for (int ch = threadIdx.x; ch < F8_BC * D / 8; ch += 2 * D) {
+    const int r = ch / (D / 8), c8 = (ch % (D / 8)) * 8;
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    if (key0 + r < Sk) raw = *(const u32x4*)(src + (size_t)r * D + c8);
+    bf16* dst = tile + r * LD + c8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(uint16_t*)(dst + 2 * i) = (uint16_t)(raw[i] & 0xffffu);
+      *(uint16_t*)(dst + 2 * i + 1) = (uint16_t)(raw[i] >> 16);
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x % D, kb = threadIdx.x / D;
+  float xv[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    xv[i] = (float)tile[(32 * kb + i) * LD + c];
+    amax = fmaxf(amax, fabsf(xv[i]));
+  }
+  const int e = mx_exponent(amax);
+  u8* dst = codes + (bh * D + c) * (size_t)Skp + key0 + 32 * kb;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) *(u32x2*)(dst + 8 * g) = e4m3x8(xv + 8 * g, e);
+  scales[((bh * ntile + t) * D + c) * 2 + kb] = (u8)(e + 127);
+}
+
+}  // namespace
+
+int fp8_padded_keys(int Sk) { return (Sk + F8_BC - 1) / F8_BC * F8_BC; }
+
+hipError_t launch_mx_quant_rows(const void* x, void* codes, void* scales, long long rows, int d, hipStream_t s) {
+  const long long nblocks = rows * (d / 32);
+  if (nblocks == 0) return hipSuccess;
+  const long long threads = nblocks * 4;
+  timing_begin(s, "mx_quant_rows");
+  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     (const bf16*)x, (u8*)codes, (u8*)scales, nblocks);
+  const hipError_t e = hipGetLastError();
+  timing_end(s);
+  return e;
+}
+
+hipError_t launch_mx_quant_vt(const void* v, void* codes, void* scales, int BH, int Sk, int d, hipStream_t s) {
+  const int Skp = fp8_padded_keys(Sk);
+  const long long grid = (long long)BH * (Skp / F8_BC);
+  if (grid == 0) return hipSuccess;
+  (void)d;                                       // validated: 128
+  timing_begin(s, "mx_quant_vt");
+  hipLaunchKernelGGL((mx_quant_vt_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, (const bf16*)v, (u8*)codes,
+                     (u8*)scales, Sk, Skp);
+  const hipError_t e = hipGetLastError();
+  timing_end(s);
+  return e;
+}
+
+hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* qs, const void* k8, const void* ks,
+                          const void* vt8, const void* vs, void* o, float* lse, hipStream_t s, char* log,
+                          size_t log_n) {
+  const PrefillPlan pl = plan_prefill(p);
+  Fp8Args a{};
+  a.q = (const u8*)q8;
+  a.qs = (const u8*)qs;
+  a.k = (const u8*)k8;
+  a.ks = (const u8*)ks;
+  a.vt = (const u8*)vt8;
+  a.vs = (const u8*)vs;
+  a.o = (bf16*)o;
+  a.lse = lse;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.Sq = p.Sq;
+  a.Sk = p.Sk;
+  a.Skp = fp8_padded_keys(p.Sk);
+  a.g = p.Hq / p.Hkv;
+  a.causal = p.causal;
+  a.c = p.scale * kLog2e;
+  a.hw = pl.hw;
+  a.n_hgroups = pl.n_hgroups;
+  a.rows_per_wg = pl.rows_per_wg;
+  a.n_ptiles = pl.n_ptiles;
+  a.total_wgs = pl.total_wgs;
+  if (log != nullptr && log_n > 0)
+    snprintf(log, log_n, "fwd_fp8<d=%d> grid=%d (%d query rows x %d heads per workgroup, 64-key tiles, MXFP8 MFMA)",
+             p.d, pl.total_wgs, pl.rows_per_wg, pl.hw);
+  if (a.total_wgs == 0) return hipSuccess;
+  timing_begin(s, "fwd_fp8");
+  hipLaunchKernelGGL((fwd_fp8_kernel<128>), dim3(a.total_wgs), dim3(512), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  timing_end(s);
+  return e;
+}
+
+}  // namespace attn

@@ -137,4 +137,15 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
                            const void* o, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, void* ws, hipStream_t s, char* log, size_t log_n);
 
+// ---- forward, MXFP8 ---------------------------------------------------------
+// Keys of the transposed FP8 V rounded up to the 64-key tile.
+int fp8_padded_keys(int Sk);
+// x bf16 [rows, d] -> E4M3 codes [rows, d] and E8M0 scales [rows, d/32].
+hipError_t launch_mx_quant_rows(const void* x, void* codes, void* scales, long long rows, int d, hipStream_t s);
+// v bf16 [BH, Sk, d] -> V^T codes [BH, d, Skp] and scales [BH, Skp/64, d, 2].
+hipError_t launch_mx_quant_vt(const void* v, void* codes, void* scales, int BH, int Sk, int d, hipStream_t s);
+hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* qs, const void* k8, const void* ks,
+                          const void* vt8, const void* vs, void* o, float* lse, hipStream_t s, char* log,
+                          size_t log_n);
+
 }  // namespace attn

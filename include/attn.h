@@ -166,6 +166,46 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
 int attn_dropout_mask(unsigned char* keep, int B, int Hq, int Sq, int Sk, float dropout_p,
                       unsigned long long seed, unsigned int offset, void* stream);
 
+/* ---- FP8 forward ("Flash Attention FA1->FA4 / pre-training practice", section
+ * 2.2: FA3 runs attention in FP8 at twice the bf16 matrix rate and keeps it
+ * accurate with per-block quantisation). Format: MXFP8 (OCP Microscaling
+ * v1.0): OCP E4M3 element codes (bias 7, max 448, S.1111.111 = NaN) in blocks
+ * of 32 that share one E8M0 scale byte s (scale 2^(s - 127)). Q and K are
+ * blocked along the head dimension, V along the keys. d = 128 only
+ * (ATTN_ERR_HEADDIM otherwise). All buffers are device memory the caller
+ * owns; nothing is allocated or kept. */
+
+/* Key count of the transposed FP8 V: Sk rounded up to a multiple of 64, or
+ * ATTN_ERR_SHAPE for Sk outside [0, 2^24). */
+int attn_fp8_padded_keys(int Sk);
+
+/* Quantise rows of bf16 (Q or K, [rows, d] contiguous, e.g. [B, H, S, d]) to
+ * codes [rows, d] (uint8) and scales [rows, d/32] (uint8). Per block of 32:
+ * e = the smallest integer with amax <= 448 * 2^e (0 for an all-zero block,
+ * clamped to [-127, 127]), scale byte e + 127, codes E4M3(x * 2^-e) rounded
+ * to nearest even (never saturating). rows >= 0; x 16-byte aligned. */
+int attn_mxfp8_quantize_rows(const void* x, void* codes, void* scales, long long rows, int d, void* stream);
+
+/* Quantise V (bf16 [BH, Sk, d]) along the keys into its transposed form:
+ * codes [BH, d, Skp] (Skp = attn_fp8_padded_keys(Sk); padding keys hold 0)
+ * and scales [BH, Skp/64, d, 2]: byte kb of channel c in 64-key tile t
+ * covers keys 64t + 32kb .. +31. Same block rule as above, keys past Sk
+ * counting as zeros. */
+int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int BH, int Sk, int d, void* stream);
+
+/* Forward on MXFP8 inputs: O (bf16 [B, Hq, Sq, d]) and lse (float [B, Hq, Sq],
+ * natural log, may be NULL) of exact attention of the dequantised inputs,
+ * with the same masks, GQA grouping, scale and empty-row rule as attn_fwd.
+ * q8/q_scales as attn_mxfp8_quantize_rows gives them for [B, Hq, Sq, d],
+ * k8/k_scales for [B, Hkv, Sk, d], vt8/vt_scales as attn_mxfp8_quantize_vt
+ * gives them for [B*Hkv, Sk, d]. The probabilities are rounded to E4M3
+ * before the P V product (the score product and the softmax run in fp32).
+ * Needs no workspace. Errors as attn_fwd; k8, k_scales, vt8, vt_scales may be
+ * NULL only when Sk == 0. */
+int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales, const void* vt8,
+                 const void* vt_scales, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                 int causal, float scale, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* attn_strerror(int status);
 

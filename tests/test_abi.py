@@ -236,3 +236,36 @@ def test_dropout_mask_validation():
     assert L.attn_dropout_mask(FAKE, 0, 1, 4, 4, 0.1, 1, 0, None) == -2
     assert L.attn_dropout_mask(FAKE, 1, 1, 4, 4, 1.5, 1, 0, None) == -10
     assert "dropout" in attn.strerror(-10)
+
+
+# ---------------------------------------------------------------- FP8
+def _fwd_fp8(**over):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, vt=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=16,
+             Sk=16, d=128, causal=1, scale=0.125, stream=None)
+    a.update(over)
+    return attn.lib().attn_fwd_fp8(a["q"], a["qs"], a["k"], a["ks"], a["vt"], a["vs"], a["o"], a["lse"], a["B"],
+                                   a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, -1), ({"qs": None}, -1), ({"k": None}, -1), ({"ks": None}, -1), ({"vt": None}, -1),
+    ({"vs": None}, -1), ({"o": None}, -1), ({"Sq": 0}, -2), ({"Sk": -1}, -2), ({"Hq": 2, "Sk": 1 << 24}, -2),
+    ({"Hq": 3}, -3), ({"d": 64}, -4), ({"d": 96}, -4), ({"causal": 3}, -6), ({"scale": 0.0}, -9),
+])
+def test_fwd_fp8_validation(over, code):
+    assert _fwd_fp8(**over) == code
+
+
+def test_mxfp8_quantizer_validation():
+    L = attn.lib()
+    assert L.attn_mxfp8_quantize_rows(None, FAKE, FAKE, 4, 128, None) == -1
+    assert L.attn_mxfp8_quantize_rows(FAKE, FAKE, FAKE, -1, 128, None) == -2
+    assert L.attn_mxfp8_quantize_rows(FAKE, FAKE, FAKE, 4, 64, None) == -4
+    assert L.attn_mxfp8_quantize_rows(None, None, None, 0, 128, None) == 0      # nothing to do
+    assert L.attn_mxfp8_quantize_vt(FAKE, None, FAKE, 2, 100, 128, None) == -1
+    assert L.attn_mxfp8_quantize_vt(FAKE, FAKE, FAKE, 0, 100, 128, None) == -2
+    assert L.attn_mxfp8_quantize_vt(FAKE, FAKE, FAKE, 2, 1 << 24, 128, None) == -2
+    assert L.attn_mxfp8_quantize_vt(FAKE, FAKE, FAKE, 2, 100, 96, None) == -4
+    assert [attn.fp8_padded_keys(n) for n in (0, 1, 64, 65, 2000)] == [0, 64, 64, 128, 2048]
+    assert L.attn_fp8_padded_keys(-1) == -2
