@@ -245,7 +245,7 @@ def bench_fp8(attn, steps, warmup):
             "tflops": round(flops / ms / 1e9, 2),
             "frac_of_fp8_peak": round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
             "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-            "roofline": roofline("fwd_fp8", w, kern["fwd_fp8"]),
+            "roofline": roofline("fwd_fp8", w.with_(name=w.name + "_mxfp8"), kern["fwd_fp8"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
             "quantise_ms": round(qms, 4), "quantise_kernels_ms": {k: round(v, 4) for k, v in qkern.items()}}
 
@@ -403,9 +403,35 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch
         print(kern, out["hbm_bytes_per_launch"])
 
 
+def _demangle(name: str) -> str:
+    if not name.startswith("_Z"):
+        return name
+    import shutil
+    import subprocess
+    tool = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    if tool is None:
+        return name
+    r = subprocess.run([tool, name], capture_output=True, text=True)
+    out = r.stdout.strip()
+    if out and out != name:
+        return out
+    # older demanglers do not know the bf16 type code: take the kernel's own
+    # identifier, the last <length><name> of the nested name
+    import re
+    m = re.match(r"_ZN(?:\d+[A-Za-z_]\w*?)*?(\d+)([A-Za-z_]\w*?)E", name)
+    if m is None:
+        return name
+    pos, last = 3, name
+    while pos < len(name) and name[pos].isdigit():
+        n = re.match(r"\d+", name[pos:]).group(0)
+        last = name[pos + len(n):pos + len(n) + int(n)]
+        pos += len(n) + int(n)
+    return last
+
+
 def _short_kernel_name(name: str) -> str:
     # "void attn::(anonymous namespace)::bwd_dq_kernel<128, true>(attn::...)" -> "bwd_dq_kernel<128, true>"
-    name = name.replace("void ", "").replace("attn::(anonymous namespace)::", "")
+    name = _demangle(name).replace("void ", "").replace("attn::(anonymous namespace)::", "")
     return name.split("(")[0].strip()
 
 
