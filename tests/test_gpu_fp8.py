@@ -14,9 +14,12 @@ is at least 2^6 L with L = sum_j exp(s_j - max_j s_j). Hence, per element,
   |o - o_ref| <= 2^-4 sum_j p_j |v_jc| + 2^-16 sum_j |v_jc| / L
                  + 2^-8 |o_ref| (bf16 output) + 1e-5 (fp32 sums),
 
-summed over the visible keys j. The test also reports the relative Frobenius
-error per head and requires <= 3e-2 (rounding errors of different keys are
-independent, so it sits near 2 %). lse does not depend on the rounding of P;
+summed over the visible keys j. The test also checks the relative Frobenius
+error per head, a statistical check: the rounding errors of different keys are
+independent, so it is close to the RMS relative error of E4M3 rounding, which
+for mantissas m spread log-uniformly over [1, 2) is 2^-4 sqrt(E[m^-2] / 3) =
+2^-4 sqrt(0.541 / 3) ~ 2.65 %; the bound is 1.5 times that, 4e-2 (observed
+1.4 % to 2.8 %). lse does not depend on the rounding of P;
 it moves by at most the largest score error, and a score is an fp32 dot
 product of d exact products, which any summation order with directed
 rounding keeps within d 2^-23 sum_c |q_c k_c| (= 2^-16 for d = 128). So
@@ -35,7 +38,7 @@ from parity import assert_finite, rel_fro, to_device, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
-FP8_REL_FRO = 3e-2
+FP8_REL_FRO = 4e-2
 
 
 def _say(*a):
@@ -275,4 +278,54 @@ def test_fwd_fp8_end_to_end_long_context_sampled(attn):
         bound = tol + 2.0 ** -8 * np.abs(o_ref) + 1e-5
         assert_finite("O", og)
         assert (err <= bound).all(), f"(b={b}, h={h}): {int((err > bound).sum())} elements outside the FP8 bound"
+        _check_fp8_lse(lg, lse_ref, ltol)
+
+
+def test_fwd_fp8_is_deterministic(attn):
+    import torch
+    _say("fwd_fp8 determinism")
+    w = synth.Workload("fp8_det", 1, 8, 2, 700, 900, 128, "bf16", 1, seed=23)
+    x = synth.make_inputs(w)
+    q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    ops = attn.mxfp8_quantize_rows(q) + attn.mxfp8_quantize_rows(k) + attn.mxfp8_quantize_vt(v)
+    o1, l1 = attn.fwd_fp8(*ops, causal=1)
+    o2, l2 = attn.fwd_fp8(*ops, causal=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_fp8_gqa_prefill_full_size_sampled(attn):
+    """The GQA prefill workload (Hq=32, Hkv=8, S=4096, causal) through the
+    GPU quantisers and the FP8 forward; sampled rows of one query head of
+    every KV head against the oracle's quantisation and FP8 attention."""
+    import torch
+    w = synth.get_workload("gqa_prefill")
+    _say("fwd_fp8 GQA prefill end to end (sampled)")
+    x = synth.make_inputs(w)
+    q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    ops = attn.mxfp8_quantize_rows(q) + attn.mxfp8_quantize_rows(k) + attn.mxfp8_quantize_vt(v)
+    o, lse = attn.fwd_fp8(*ops, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    g = w.Hq // w.Hkv
+    for hk in range(w.Hkv):
+        h = hk * g + int(rng.integers(g))
+        rows = np.unique(np.concatenate([[0, 1, 255, 256, w.Sq - 1], rng.choice(w.Sq, 12, replace=False)]))
+        qf = synth.to_f64(x["q"][:, h:h + 1], "bf16")
+        kf = synth.to_f64(x["k"][:, hk:hk + 1], "bf16")
+        vf = synth.to_f64(x["v"][:, hk:hk + 1], "bf16")
+        q8r, qsr, k8r, ksr, vt8r, _, vtsr = _oracle_quant(qf[:, :, rows], kf, vf, w.Sk)
+        o_ref, lse_ref = ofp8.attention_forward_fp8(q8r, qsr, k8r, ksr, vt8r, vtsr, causal=w.causal,
+                                                    scale=w.scale, rows=rows, Sq=w.Sq)
+        qd, kd = ofp8.mx_dequantize(q8r, qsr), ofp8.mx_dequantize(k8r, ksr)
+        vd = np.swapaxes(ofp8.mx_dequantize(vt8r, vtsr), -1, -2)
+        tol = _fp8_tolerance(qd, kd, vd, w.causal, w.scale, rows=rows, Sq=w.Sq)
+        ltol = _lse_tolerance(qd, kd, w.causal, w.scale, rows=rows, Sq=w.Sq)
+        idx = torch.from_numpy(rows).cuda()
+        og = to_host_f64(o[:, h:h + 1, idx])
+        lg = lse[:, h:h + 1, idx].cpu().numpy().astype(np.float64)
+        err = np.abs(og - o_ref)
+        bound = tol + 2.0 ** -8 * np.abs(o_ref) + 1e-5
+        assert_finite("O", og)
+        assert (err <= bound).all(), f"head {h}: {int((err > bound).sum())} elements outside the FP8 bound"
         _check_fp8_lse(lg, lse_ref, ltol)
