@@ -9,7 +9,7 @@ training workload). The same run also times the long-context causal forward
 16 causal sequences of 512..3584 tokens (forward + backward through the
 variable-length entry points) and the long-context forward on MXFP8 operands
 (attn_fwd_fp8 on inputs quantised beforehand; the quantisers are timed on
-their own), which report as their own sub-objects. Inputs are resident in
+their own) and the decode on MXFP8 operands, which report as their own sub-objects. Inputs are resident in
 device memory before timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "bwd_dq": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
     "bwd_pre": ["bwd_bf16.hip", "common.h", "kernels.h"],
     "fwd_fp8": ["fwd_fp8.hip", "common.h", "kernels.h", "tiles.h"],
+    "fwd_fp8_split": ["fwd_fp8.hip", "common.h", "kernels.h", "tiles.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
 # (the dense and the packed instantiations both match; a workload uses one)
@@ -59,6 +60,7 @@ KERNEL_SYMBOLS = {
     "bwd_dq": "bwd_dq_kernel<128,",
     "bwd_pre": "bwd_pre_kernel<128,",
     "fwd_fp8": "fwd_fp8_kernel<128>",
+    "fwd_fp8_split": "fwd_fp8_split_kernel<128>",
 }
 
 
@@ -100,6 +102,9 @@ def kernel_work(kernel: str, w) -> dict:
     if kernel == "fwd_split_bf16":
         kv = 2.0 * w.B * w.Hkv * w.Sk * w.d * e
         return {"bound": "hbm", "bytes": kv + w.B * w.Hq * w.Sq * w.d * e}
+    if kernel == "fwd_fp8_split":
+        kv = 2.0 * w.B * w.Hkv * w.Sk * w.d * (1 + 1 / 32)       # E4M3 codes + one scale byte per 32
+        return {"bound": "hbm", "bytes": kv + w.B * w.Hq * w.Sq * w.d * (1 + 1 / 32)}
     if kernel == "combine_split":
         return {"bound": "hbm", "bytes": w.B * w.Hq * w.Sq * (w.d * e + 4)}
     return {"bound": "mfma", "flops": 0.0}
@@ -248,6 +253,29 @@ def bench_fp8(attn, steps, warmup):
             "roofline": roofline("fwd_fp8", w.with_(name=w.name + "_mxfp8"), kern["fwd_fp8"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
             "quantise_ms": round(qms, 4), "quantise_kernels_ms": {k: round(v, 4) for k, v in qkern.items()}}
+
+
+def bench_fp8_decode(attn, steps, warmup):
+    """The GQA decode on MXFP8 operands (quantised before timing): K and V
+    cross HBM as E4M3 codes plus one scale byte per 32 values."""
+    import torch
+    import synth
+    w = synth.get_workload("gqa_decode")
+    t = _device_inputs(w)
+    ops = attn.mxfp8_quantize_rows(t["q"]) + attn.mxfp8_quantize_rows(t["k"]) + attn.mxfp8_quantize_vt(t["v"])
+    del t
+    o = torch.empty(w.B, w.Hq, w.Sq, w.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, attn.fwd_fp8_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal)),
+                     dtype=torch.uint8, device="cuda")
+    ms, kern = _time(lambda: attn.fwd_fp8(*ops, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws),
+                     steps, warmup, attn)
+    alg = kernel_work("fwd_fp8_split", w)["bytes"] + w.B * w.Hq * w.Sq * (w.d * 2 + 4)
+    return {"workload": w.name + "_mxfp8", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
+            "ms": round(ms, 4), "algorithmic_bytes": int(alg), "gbs": round(alg / ms / 1e6, 1),
+            "frac_of_peak": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "roofline": roofline("fwd_fp8_split", w.with_(name=w.name + "_mxfp8"), kern["fwd_fp8_split"]),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
 
 
 def bench_decode(attn, steps, warmup):
@@ -505,6 +533,9 @@ def main() -> int:
     if args.only in ("all", "fp8"):
         result["fp8"] = bench_fp8(attn, args.steps, args.warmup)
         print(f"# fp8: {result['fp8']['ms']} ms", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        result["fp8_decode"] = bench_fp8_decode(attn, max(args.steps, 20), args.warmup)
+        print(f"# fp8 decode: {result['fp8_decode']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         result["decode"] = bench_decode(attn, max(args.steps, 20), args.warmup)

@@ -17,7 +17,7 @@ __all__ = [
     "fwd_workspace_bytes", "bwd_workspace_bytes", "strerror", "last_dispatch",
     "timing_start", "timing_stop", "fwd_varlen", "bwd_varlen", "fwd_varlen_workspace_bytes",
     "bwd_varlen_workspace_bytes", "fwd_dropout", "bwd_dropout", "dropout_mask",
-    "fp8_padded_keys", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fwd_fp8",
+    "fp8_padded_keys", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fwd_fp8", "fwd_fp8_workspace_bytes",
 ]
 
 ATTN_F32 = 0
@@ -85,7 +85,9 @@ def lib() -> ctypes.CDLL:
         L.attn_mxfp8_quantize_rows.restype = _I
         L.attn_mxfp8_quantize_vt.argtypes = [_P, _P, _P, _I, _I, _I, _P]
         L.attn_mxfp8_quantize_vt.restype = _I
-        L.attn_fwd_fp8.argtypes = [_P] * 8 + _SHAPE + [_F, _P]
+        L.attn_fwd_fp8_workspace_bytes.argtypes = _SHAPE
+        L.attn_fwd_fp8_workspace_bytes.restype = _Z
+        L.attn_fwd_fp8.argtypes = [_P] * 8 + _SHAPE + [_F, _P, _Z, _P]
         L.attn_fwd_fp8.restype = _I
         L.attn_strerror.argtypes = [_I]
         L.attn_strerror.restype = ctypes.c_char_p
@@ -449,13 +451,17 @@ def mxfp8_quantize_vt(v, *, stream=None):
     return codes, scales
 
 
+def fwd_fp8_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal) -> int:
+    return int(lib().attn_fwd_fp8_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal))
+
+
 def fwd_fp8(q8, q_scales, k8, k_scales, vt8, vt_scales, *, causal: int = 0, scale: Optional[float] = None,
-            out=None, lse=None, need_lse: bool = True, stream=None):
+            out=None, lse=None, need_lse: bool = True, workspace=None, stream=None):
     """Forward on MXFP8 operands (as the two quantisers give them): returns
     (o bf16 [B, Hq, Sq, d], lse float32 [B, Hq, Sq] or None)."""
     import torch
     for t, n in ((q8, "q8"), (q_scales, "q_scales"), (k8, "k8"), (k_scales, "k_scales"), (vt8, "vt8"),
-                 (vt_scales, "vt_scales"), (out, "out"), (lse, "lse")):
+                 (vt_scales, "vt_scales"), (out, "out"), (lse, "lse"), (workspace, "workspace")):
         _check(t, n)
     B, Hq, Sq, d = q8.shape
     _, Hkv, Sk, _ = k8.shape
@@ -474,8 +480,13 @@ def fwd_fp8(q8, q_scales, k8, k_scales, vt8, vt_scales, *, causal: int = 0, scal
         out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None and need_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    ws_n = fwd_fp8_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal)
+    if workspace is None and ws_n > 0:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q8.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().attn_fwd_fp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(vt8), _ptr(vt_scales),
-                            _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, causal, sc, _stream(stream))
+                            _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, causal, sc, _ptr(workspace), ws_bytes,
+                            _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd_fp8")
     return out, lse

@@ -533,9 +533,14 @@ int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int B
   return ATTN_OK;
 }
 
+size_t attn_fwd_fp8_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal) {
+  if (check_common(B, Hq, Hkv, Sq, Sk, d, causal, 1.f, ATTN_BF16) != ATTN_OK || d != 128) return 0;
+  return attn::fp8_workspace_bytes(make_problem(B, Hq, Hkv, Sq, Sk, d, causal, 1.f));
+}
+
 int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales, const void* vt8,
                  const void* vt_scales, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
-                 int causal, float scale, void* stream) {
+                 int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (q8 == nullptr || q_scales == nullptr || o == nullptr ||
       (Sk != 0 && (k8 == nullptr || k_scales == nullptr || vt8 == nullptr || vt_scales == nullptr)))
     return ATTN_ERR_NULL;
@@ -543,9 +548,11 @@ int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const voi
   if (st != ATTN_OK) return st;
   if (d != 128) return ATTN_ERR_HEADDIM;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
+  const size_t need = attn::fp8_workspace_bytes(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
   char text[400], line[480];
-  if (attn::launch_fwd_fp8(p, q8, q_scales, k8, k_scales, vt8, vt_scales, o, lse, (hipStream_t)stream, text,
-                           sizeof(text)) != hipSuccess)
+  if (attn::launch_fwd_fp8(p, q8, q_scales, k8, k_scales, vt8, vt_scales, o, lse, workspace, (hipStream_t)stream,
+                           text, sizeof(text)) != hipSuccess)
     return ATTN_ERR_HIP;
   std::snprintf(line, sizeof(line), "attn_fwd_fp8: %s", text);
   record(line);

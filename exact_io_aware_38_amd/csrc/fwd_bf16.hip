@@ -779,6 +779,24 @@ hipError_t launch_dropout_mask(const Problem& p, unsigned char* keep, hipStream_
   return hipGetLastError();
 }
 
+hipError_t launch_combine_split(const Problem& p, const SplitPlan& sp, void* ws, void* o, float* lse,
+                                hipStream_t s) {
+  const size_t rows = (size_t)p.B * p.Hq * p.Sq;
+  const size_t o_bytes = (size_t)sp.nsplit * rows * p.d * sizeof(float);
+  const float* part_o = (const float*)ws;
+  const float* part_lse = (const float*)((const char*)ws + ((o_bytes + 255) / 256) * 256);
+  timing_begin(s, "combine_split");
+  if (p.d == 64)
+    hipLaunchKernelGGL((combine_split_kernel<64>), dim3(rows), dim3(64), 0, s, part_o, part_lse, (bf16*)o, lse,
+                       sp.nsplit, rows, p.Sq, p.hsq);
+  else
+    hipLaunchKernelGGL((combine_split_kernel<128>), dim3(rows), dim3(64), 0, s, part_o, part_lse, (bf16*)o, lse,
+                       sp.nsplit, rows, p.Sq, p.hsq);
+  const hipError_t e = hipGetLastError();
+  timing_end(s);
+  return e;
+}
+
 hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& sp, const void* q, const void* k,
                                  const void* v, void* o, float* lse, void* ws, hipStream_t s) {
   FwdArgs a = base_args(p, q, k, v, o, lse);

@@ -396,6 +396,179 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-key decode on MXFP8 operands: one 64-lane wavefront per (key slice,
+// KV head, batch); its 32 MFMA columns pack (query head of the group, query
+// row) pairs, so every K/V byte of the slice is read once for all of them.
+// Decode streams K and V once, so the operands go straight from HBM into
+// registers (range-checked buffer loads; the transposed V gives each lane
+// two contiguous 16-byte chunks per 32-channel block) and occupancy (about
+// eight wavefronts per CU) keeps enough loads in flight; the K fragments of
+// the next 64-key tile are loaded as soon as the score MFMAs have read the
+// current ones, the V fragments as soon as the P V MFMAs have. Writes the
+// slice's normalised partial output and lse for the merge kernel.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __restrict__ part_o,
+                                                           float* __restrict__ part_lse, int nsplit,
+                                                           int split_keys) {
+  static_assert(D == 128, "the FP8 path is built for d = 128");
+  constexpr int DC = D / 64;
+  constexpr int MB = D / 32;
+  constexpr int NSB = D / 32;
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int off = (a.causal == 2) ? (a.Sk - a.Sq) : 0;
+  const int W = blockIdx.x;
+  const int split = W % nsplit;
+  const int rest = W / nsplit;
+  const int hkv = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  // column n packs (query head of the group, query row): n = hg * Sq + row
+  const bool colv = l32 < a.g * a.Sq;
+  const int hq = hkv * a.g + (colv ? l32 / a.Sq : 0);
+  const int pos = colv ? l32 % a.Sq : 0;
+  const int kbeg = split * split_keys;
+  int kend = min(a.Sk, kbeg + split_keys);
+  if (a.causal) kend = min(kend, a.Sq - 1 + off + 1);
+  if (kend < kbeg) kend = kbeg;
+  const int ntiles = (kend - kbeg + F8_BC - 1) / F8_BC;
+  const int lim = a.causal ? min(kend - 1, pos + off) : kend - 1;
+  const int mask_from = a.causal ? max(kbeg, min(kend, off + 1)) : kend;
+
+  // Q fragments and scales as in the prefill kernel (unused columns hold zeros)
+  i32x8 qf[DC];
+  int qsc;
+  {
+    const size_t row = ((size_t)b * a.Hq + hq) * a.Sq + pos;
+    const u8* qp = a.q + row * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = colv ? cat_u32x4(*(const u32x4*)(qp + 64 * dc + 16 * hi), *(const u32x4*)(qp + 64 * dc + 32 + 16 * hi))
+                    : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    qsc = colv ? (int)((*(const uint32_t*)(a.qs + row * NSB)) >> (8 * hi)) : 0;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
+    qsc = settle(qsc);
+  }
+  const size_t kvh = (size_t)b * a.Hkv + hkv;
+  // whole-head buffers: K rows past Sk read zeros (their scores are masked)
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + kvh * (size_t)a.Sk * D), (short)0, a.Sk * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rks =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kvh * (size_t)a.Sk * NSB), (short)0, a.Sk * NSB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.vt + kvh * (size_t)D * a.Skp), (short)0, D * a.Skp, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.vs + kvh * (size_t)(a.Skp / F8_BC) * (2 * D)), (short)0, (a.Skp / F8_BC) * 2 * D, 0x00020000);
+  // per-lane offsets: K row kappa_c(l32) of the tile, channels 64 dc + 16 hi
+  // (+32); V^T row 32 mb + l32, keys 16 hi (+32) of the tile
+  const uint32_t kro0 = (uint32_t)kappa(0, l32) * D + 16 * hi;
+  const uint32_t kso0 = (uint32_t)kappa(0, l32) * NSB;
+  const uint32_t vro = (uint32_t)l32 * a.Skp + 16 * hi;
+
+  i32x8 kf[2][DC], vf[MB];
+  int ksc[2], vsc[MB];
+  auto load_k = [&](int t) __attribute__((always_inline)) {
+    const uint32_t key0 = (uint32_t)(kbeg + t * F8_BC);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t base = (key0 + 32 * c) * D + kro0;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        kf[c][dc] = cat_u32x4(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, base + 64 * dc, 0, 0)),
+                              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, base + 64 * dc + 32, 0, 0)));
+      ksc[c] = (int)(__builtin_amdgcn_raw_buffer_load_b32(rks, (key0 + 32 * c) * NSB + kso0, 0, 0) >> (8 * hi));
+    }
+  };
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    const uint32_t key0 = (uint32_t)(kbeg + t * F8_BC);
+    const uint32_t tile = key0 / F8_BC;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint32_t base = (uint32_t)(32 * mb) * a.Skp + vro + key0;
+      vf[mb] = cat_u32x4(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, base, 0, 0)),
+                         __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, base + 32, 0, 0)));
+      vsc[mb] = (int)__builtin_amdgcn_raw_buffer_load_b8(rvs, (tile * D + 32 * mb + l32) * 2 + hi, 0, 0);
+    }
+  };
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+  float m2 = kNegInf, lsum = 0.f;
+  if (ntiles > 0) {
+    load_k(0);
+    load_v(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    f32x16 s[2];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        s[c] = dc == 0 ? mfma_f8<0, 0>(kf[c][0], ksc[c], qf[0], qsc, f32x16{})
+                       : mfma_f8<2, 2>(kf[c][1], ksc[c], qf[1], qsc, s[c]);
+    if (t + 1 < ntiles) load_k(t + 1);
+    const int key0 = kbeg + t * F8_BC;
+    float v[32];                                // v[u]: key key0 + 32 (u >> 4) + 16 hi + (u & 15)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = s[0][i];
+      v[16 + i] = s[1][i];
+    }
+    if (key0 + F8_BC > mask_from) {
+      const int rel = lim - key0 - 16 * hi;
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (32 * (u >> 4) + (u & 15) > rel) v[u] = kNegInf;
+    }
+    const float mx = max_halves(tree_max32(v)) * a.c;
+    const bool grow = mx > m2 + F8_RESCALE_T;
+    if (wave_any(grow)) {
+      const float mnew = grow ? mx : m2;
+      const float alpha = grow ? fast_exp2(m2 - mnew) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+      m2 = mnew;
+    }
+    const float msub = (m2 == kNegInf) ? 0.f : m2 - F8_PSHIFT;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = fast_exp2(__builtin_fmaf(v[u], a.c, -msub));
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w], v[4 * w + 1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2], v[4 * w + 3], x, true);
+    }
+    lsum += tree_sum32(v);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f8<0, 0>(vf[mb], vsc[mb], pf, E8M0_ONE, acc[mb]);
+    if (t + 1 < ntiles) load_v(t + 1);
+  }
+
+  const float lt = sum_halves(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m2 - F8_PSHIFT + __log2f(lt)) * kLn2 : kNegInf;
+  if (!colv) return;
+  const size_t row = (((size_t)split * a.B + b) * a.Hq + hq) * a.Sq + pos;
+  float* pp = part_o + row * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 r;
+      r[0] = acc[mb][4 * q4 + 0] * inv;
+      r[1] = acc[mb][4 * q4 + 1] * inv;
+      r[2] = acc[mb][4 * q4 + 2] * inv;
+      r[3] = acc[mb][4 * q4 + 3] * inv;
+      *(f32x4*)(pp + 32 * mb + 8 * q4 + 4 * hi) = r;
+    }
+  if (hi == 0) part_lse[row] = lse_v;
+}
+
+// ---------------------------------------------------------------------------
 // MXFP8 quantisers. Block exponent: the smallest e with amax <= 448 * 2^e
 // (amax = f 2^E with f in [0.5, 1) and 448 = 0.875 * 2^9 give
 // e = E - 9 + (f > 0.875)), 0 for an all-zero block, clamped to [-127, 127];
@@ -516,8 +689,13 @@ hipError_t launch_mx_quant_vt(const void* v, void* codes, void* scales, int BH, 
   return e;
 }
 
+size_t fp8_workspace_bytes(const Problem& p) {
+  const SplitPlan sp = plan_split(p);
+  return sp.use ? sp.ws_bytes : 0;
+}
+
 hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* qs, const void* k8, const void* ks,
-                          const void* vt8, const void* vs, void* o, float* lse, hipStream_t s, char* log,
+                          const void* vt8, const void* vs, void* o, float* lse, void* ws, hipStream_t s, char* log,
                           size_t log_n) {
   const PrefillPlan pl = plan_prefill(p);
   Fp8Args a{};
@@ -538,6 +716,24 @@ hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* qs, cons
   a.g = p.Hq / p.Hkv;
   a.causal = p.causal;
   a.c = p.scale * kLog2e;
+  const SplitPlan sp = plan_split(p);
+  if (sp.use) {
+    // decode-shaped: every grouped query row of a KV head in one wavefront, keys split
+    const size_t rows = (size_t)p.B * p.Hq * p.Sq;
+    const size_t o_bytes = (size_t)sp.nsplit * rows * p.d * sizeof(float);
+    float* part_o = (float*)ws;
+    float* part_lse = (float*)((char*)ws + ((o_bytes + 255) / 256) * 256);
+    if (log != nullptr && log_n > 0)
+      snprintf(log, log_n, "fwd_fp8_split<d=%d> grid=%d (%d key slices of %d keys, MXFP8 MFMA) + combine_split rows=%zu",
+               p.d, sp.nsplit * p.B * p.Hkv, sp.nsplit, sp.split_keys, rows);
+    timing_begin(s, "fwd_fp8_split");
+    hipLaunchKernelGGL((fwd_fp8_split_kernel<128>), dim3(sp.nsplit * p.B * p.Hkv), dim3(64), 0, s, a, part_o,
+                       part_lse, sp.nsplit, sp.split_keys);
+    hipError_t e = hipGetLastError();
+    timing_end(s);
+    if (e != hipSuccess) return e;
+    return launch_combine_split(p, sp, ws, o, lse, s);
+  }
   a.hw = pl.hw;
   a.n_hgroups = pl.n_hgroups;
   a.rows_per_wg = pl.rows_per_wg;

@@ -126,6 +126,10 @@ SplitPlan plan_split(const Problem& p);
 hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& plan, const void* q,
                                  const void* k, const void* v, void* o, float* lse,
                                  void* ws, hipStream_t s);
+// The merge of a split launch's per-slice partials (in the workspace laid out
+// by plan_split) into o (bf16) and lse.
+hipError_t launch_combine_split(const Problem& p, const SplitPlan& plan, void* ws, void* o, float* lse,
+                                hipStream_t s);
 
 // ---- forward, fp32 ----------------------------------------------------------
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v,
@@ -144,8 +148,11 @@ int fp8_padded_keys(int Sk);
 hipError_t launch_mx_quant_rows(const void* x, void* codes, void* scales, long long rows, int d, hipStream_t s);
 // v bf16 [BH, Sk, d] -> V^T codes [BH, d, Skp] and scales [BH, Skp/64, d, 2].
 hipError_t launch_mx_quant_vt(const void* v, void* codes, void* scales, int BH, int Sk, int d, hipStream_t s);
+// Workspace of the FP8 forward: the split-key partials for decode-shaped
+// problems (the same rule and layout as the bf16 split path), else 0.
+size_t fp8_workspace_bytes(const Problem& p);
 hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* qs, const void* k8, const void* ks,
-                          const void* vt8, const void* vs, void* o, float* lse, hipStream_t s, char* log,
+                          const void* vt8, const void* vs, void* o, float* lse, void* ws, hipStream_t s, char* log,
                           size_t log_n);
 
 }  // namespace attn

@@ -193,6 +193,12 @@ int attn_mxfp8_quantize_rows(const void* x, void* codes, void* scales, long long
  * counting as zeros. */
 int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int BH, int Sk, int d, void* stream);
 
+/* Bytes of device workspace attn_fwd_fp8 needs (0 if none): decode-shaped
+ * problems (Hq/Hkv * Sq <= 32) split the keys over several wavefronts and
+ * keep per-split partial results there, as attn_fwd does. 0 for invalid
+ * arguments too; the call then reports the error. */
+size_t attn_fwd_fp8_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal);
+
 /* Forward on MXFP8 inputs: O (bf16 [B, Hq, Sq, d]) and lse (float [B, Hq, Sq],
  * natural log, may be NULL) of exact attention of the dequantised inputs,
  * with the same masks, GQA grouping, scale and empty-row rule as attn_fwd.
@@ -200,11 +206,13 @@ int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int B
  * k8/k_scales for [B, Hkv, Sk, d], vt8/vt_scales as attn_mxfp8_quantize_vt
  * gives them for [B*Hkv, Sk, d]. The probabilities are rounded to E4M3
  * before the P V product (the score product and the softmax run in fp32).
- * Needs no workspace. Errors as attn_fwd; k8, k_scales, vt8, vt_scales may be
- * NULL only when Sk == 0. */
+ * Dispatch as attn_fwd: tiled prefill, or split-key decode when
+ * Hq/Hkv * Sq <= 32 (then workspace must hold attn_fwd_fp8_workspace_bytes,
+ * else ATTN_ERR_WORKSPACE). Errors as attn_fwd; k8, k_scales, vt8, vt_scales
+ * may be NULL only when Sk == 0. */
 int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales, const void* vt8,
                  const void* vt_scales, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
-                 int causal, float scale, void* stream);
+                 int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* attn_strerror(int status);

@@ -241,20 +241,30 @@ def test_dropout_mask_validation():
 # ---------------------------------------------------------------- FP8
 def _fwd_fp8(**over):
     a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, vt=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=16,
-             Sk=16, d=128, causal=1, scale=0.125, stream=None)
+             Sk=16, d=128, causal=1, scale=0.125, ws=None, ws_bytes=0, stream=None)
     a.update(over)
     return attn.lib().attn_fwd_fp8(a["q"], a["qs"], a["k"], a["ks"], a["vt"], a["vs"], a["o"], a["lse"], a["B"],
-                                   a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"],
-                                   a["stream"])
+                                   a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["ws"],
+                                   a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("over,code", [
     ({"q": None}, -1), ({"qs": None}, -1), ({"k": None}, -1), ({"ks": None}, -1), ({"vt": None}, -1),
     ({"vs": None}, -1), ({"o": None}, -1), ({"Sq": 0}, -2), ({"Sk": -1}, -2), ({"Hq": 2, "Sk": 1 << 24}, -2),
     ({"Hq": 3}, -3), ({"d": 64}, -4), ({"d": 96}, -4), ({"causal": 3}, -6), ({"scale": 0.0}, -9),
+    # decode-shaped calls (Hq/Hkv * Sq <= 32) split the keys and need the partials workspace
+    ({"Sq": 1, "Sk": 4096}, -7), ({"Sq": 1, "Sk": 4096, "ws": FAKE, "ws_bytes": 8}, -7),
 ])
 def test_fwd_fp8_validation(over, code):
     assert _fwd_fp8(**over) == code
+
+
+def test_fwd_fp8_workspace_query():
+    # prefill-shaped: none; decode-shaped: the bf16 split path's partials, same rule
+    assert attn.fwd_fp8_workspace_bytes(1, 4, 2, 256, 256, 128, 1) == 0
+    n = attn.fwd_fp8_workspace_bytes(16, 32, 8, 1, 32768, 128, 0)
+    assert n > 0 and n == attn.fwd_workspace_bytes(16, 32, 8, 1, 32768, 128, 0, attn.ATTN_BF16)
+    assert attn.fwd_fp8_workspace_bytes(16, 32, 8, 1, 32768, 64, 0) == 0        # d = 64 is not built
 
 
 def test_mxfp8_quantizer_validation():

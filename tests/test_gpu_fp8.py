@@ -179,8 +179,15 @@ FWD = [
     (1, 4, 1, 130, 520, 1, 15),      # top-left with Sk > Sq: keys >= 130 never visible
     (1, 6, 2, 100, 100, 0, 16),      # 3 query heads per KV head
     (1, 32, 8, 64, 2000, 0, 17),     # 4 query heads per KV head, ragged 2000 keys
-    (1, 4, 4, 1, 700, 0, 18),        # one query row
+    (1, 4, 4, 1, 700, 0, 18),        # one query row (split-key decode)
     (1, 2, 2, 64, 64, 1, 19),        # exactly one tile
+    # split-key decode shapes (Hq/Hkv * Sq <= 32)
+    (2, 8, 2, 1, 1000, 0, 31),       # 4 query heads per KV head, one row each
+    (1, 32, 1, 1, 5000, 0, 32),      # 32 query heads share one KV head
+    (1, 4, 4, 3, 700, 2, 33),        # 3 rows per head, bottom-right mask
+    (3, 2, 1, 16, 2049, 1, 34),      # 32 packed rows, top-left mask, ragged keys
+    (1, 4, 1, 2, 64, 0, 35),         # a single key tile
+    (1, 8, 2, 1, 30, 0, 36),         # fewer keys than one tile
 ]
 
 
@@ -329,3 +336,38 @@ def test_fwd_fp8_gqa_prefill_full_size_sampled(attn):
         assert_finite("O", og)
         assert (err <= bound).all(), f"head {h}: {int((err > bound).sum())} elements outside the FP8 bound"
         _check_fp8_lse(lg, lse_ref, ltol)
+
+
+def test_fwd_fp8_decode_full_size_sampled(attn):
+    """The GQA decode workload (B=16, Hq=32, Hkv=8, one query row, 32768 keys)
+    through the GPU quantisers and the FP8 split-key decode, in the launch
+    configuration the benchmark times; every query head of four batches
+    against the oracle's quantisation and FP8 attention."""
+    import torch
+    w = synth.get_workload("gqa_decode")
+    _say("fwd_fp8 GQA decode end to end (sampled)")
+    x = synth.make_inputs(w)
+    q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    ops = attn.mxfp8_quantize_rows(q) + attn.mxfp8_quantize_rows(k) + attn.mxfp8_quantize_vt(v)
+    o, lse = attn.fwd_fp8(*ops, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert "fwd_fp8_split" in attn.last_dispatch()
+    g = w.Hq // w.Hkv
+    for b in (0, 5, 10, 15):
+        for hk in range(w.Hkv):
+            qf = synth.to_f64(x["q"][b:b + 1, hk * g:(hk + 1) * g], "bf16")
+            kf = synth.to_f64(x["k"][b:b + 1, hk:hk + 1], "bf16")
+            vf = synth.to_f64(x["v"][b:b + 1, hk:hk + 1], "bf16")
+            q8r, qsr, k8r, ksr, vt8r, _, vtsr = _oracle_quant(qf, kf, vf, w.Sk)
+            o_ref, lse_ref = ofp8.attention_forward_fp8(q8r, qsr, k8r, ksr, vt8r, vtsr, causal=0, scale=w.scale)
+            qd, kd = ofp8.mx_dequantize(q8r, qsr), ofp8.mx_dequantize(k8r, ksr)
+            vd = np.swapaxes(ofp8.mx_dequantize(vt8r, vtsr), -1, -2)
+            tol = _fp8_tolerance(qd, kd, vd, 0, w.scale)
+            ltol = _lse_tolerance(qd, kd, 0, w.scale)
+            og = to_host_f64(o[b:b + 1, hk * g:(hk + 1) * g])
+            lg = lse[b:b + 1, hk * g:(hk + 1) * g].cpu().numpy().astype(np.float64)
+            err = np.abs(og - o_ref)
+            bound = tol + 2.0 ** -8 * np.abs(o_ref) + 1e-5
+            assert_finite("O", og)
+            assert (err <= bound).all(), f"(b={b}, kv head {hk}): {int((err > bound).sum())} elements outside the bound"
+            _check_fp8_lse(lg, lse_ref, ltol)
