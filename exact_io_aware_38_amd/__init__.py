@@ -435,15 +435,16 @@ def mxfp8_quantize_rows(x, *, codes=None, scales=None, stream=None):
 
 
 def mxfp8_quantize_vt(v, *, stream=None):
-    """bf16 V [B, Hkv, Sk, d] -> (V^T codes uint8 [B, Hkv, d, Skp],
-    scales uint8 [B, Hkv, Skp/64, d, 2]), Skp = fp8_padded_keys(Sk)."""
+    """bf16 V [B, Hkv, Sk, d] -> (V^T codes tiled by 64 keys, uint8
+    [B, Hkv, Skp/64, d, 64], scales uint8 [B, Hkv, Skp/64, d, 2]),
+    Skp = fp8_padded_keys(Sk)."""
     import torch
     _check(v, "v")
     if v.dtype != torch.bfloat16:
         raise TypeError("v must be bfloat16")
     B, H, Sk, d = v.shape
     skp = fp8_padded_keys(Sk)
-    codes = torch.empty((B, H, d, skp), dtype=torch.uint8, device=v.device)
+    codes = torch.empty((B, H, skp // 64, d, 64), dtype=torch.uint8, device=v.device)
     scales = torch.empty((B, H, skp // 64, d, 2), dtype=torch.uint8, device=v.device)
     st = lib().attn_mxfp8_quantize_vt(_ptr(v), _ptr(codes), _ptr(scales), B * H, Sk, d, _stream(stream))
     if st != 0:
@@ -471,7 +472,7 @@ def fwd_fp8(q8, q_scales, k8, k_scales, vt8, vt_scales, *, causal: int = 0, scal
     _want(q_scales, (B, Hq, Sq, d // 32), u8, "q_scales")
     _want(k8, (B, Hkv, Sk, d), u8, "k8")
     _want(k_scales, (B, Hkv, Sk, d // 32), u8, "k_scales")
-    _want(vt8, (B, Hkv, d, skp), u8, "vt8")
+    _want(vt8, (B, Hkv, skp // 64, d, 64), u8, "vt8")
     _want(vt_scales, (B, Hkv, skp // 64, d, 2), u8, "vt_scales")
     _want(out, (B, Hq, Sq, d), torch.bfloat16, "out")
     _want(lse, (B, Hq, Sq), torch.float32, "lse")

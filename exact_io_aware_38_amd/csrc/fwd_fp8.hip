@@ -11,10 +11,11 @@
 // Operand formats (produced by the quantisers below):
 //  * Q, K: codes [B, H, S, d] (row-major, like the bf16 tensors), scales
 //    [B, H, S, d/32]: one per 32 channels of a row;
-//  * V, transposed: codes [B, Hkv, d, Skp] (Skp = Sk rounded up to 64, the
-//    padding zero), scales [B, Hkv, Skp/64, d, 2]: one per 32 keys of a
-//    channel, grouped per 64-key tile so that a tile's scales are 256
-//    contiguous bytes. V is blocked along the keys because the P V product
+//  * V, transposed and tiled by 64 keys: codes [B, Hkv, Skp/64, d, 64]
+//    (Skp = Sk rounded up to 64, the padding zero), scales
+//    [B, Hkv, Skp/64, d, 2]: one per 32 keys of a channel. A tile's codes are
+//    8 KB and its scales 256 bytes, each contiguous (a plain [d, Skp]
+//    transpose would read 64-byte pieces 32 KB apart in long sequences). V is blocked along the keys because the P V product
 //    sums over them, and it is stored transposed because V^T is the A
 //    operand of O^T = V^T P^T.
 //
@@ -87,6 +88,7 @@ struct Fp8Ring {
   static constexpr int KS_OFF = KT + VT;
   static constexpr int VS_OFF = KS_OFF + KS;
   static constexpr int STAGE = VS_OFF + VS;
+  static constexpr int VST = VT + VS;           // a V^T tile and its scales (decode ring slot)
   static constexpr int NSTAGE = 4;
 };
 
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
     const int P = wid * 64 + lane;
     const int kr = P / 8, vr = P / 4;
     koff = kr * D + (((P % 8) ^ swz_k(kr)) << 4);
-    voff = vr * a.Skp + (((P % 4) ^ swz_v(vr)) << 4);
+    voff = vr * F8_BC + (((P % 4) ^ swz_v(vr)) << 4);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const uint32_t ldsw = lds0 + wid * 1024;
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
     const int tt = min(t, ntiles - 1);
     const int key0 = tt * F8_BC;
     d.rk = buffer_rsrc(kg + (size_t)key0 * D, (uint32_t)(kend - key0) * D);
-    d.rv = buffer_rsrc(vtg + key0, (uint32_t)(D * a.Skp - key0));
+    d.rv = buffer_rsrc(vtg + (size_t)tt * (D * F8_BC), D * F8_BC);
     if (wid == 0) d.rs = buffer_rsrc(ksg + (size_t)key0 * NSB, (uint32_t)(kend - key0) * NSB);
     else d.rs = buffer_rsrc(vsg + (size_t)tt * (2 * D), 2 * D);
     return d;
@@ -412,9 +414,11 @@ __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __r
                                                            float* __restrict__ part_lse, int nsplit,
                                                            int split_keys) {
   static_assert(D == 128, "the FP8 path is built for d = 128");
+  using R = Fp8Ring<D>;
   constexpr int DC = D / 64;
   constexpr int MB = D / 32;
   constexpr int NSB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * R::VST];
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -457,18 +461,25 @@ __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __r
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + kvh * (size_t)a.Sk * D), (short)0, a.Sk * D, 0x00020000);
   const __amdgpu_buffer_rsrc_t rks =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kvh * (size_t)a.Sk * NSB), (short)0, a.Sk * NSB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.vt + kvh * (size_t)D * a.Skp), (short)0, D * a.Skp, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.vs + kvh * (size_t)(a.Skp / F8_BC) * (2 * D)), (short)0, (a.Skp / F8_BC) * 2 * D, 0x00020000);
-  // per-lane offsets: K row kappa_c(l32) of the tile, channels 64 dc + 16 hi
-  // (+32); V^T row 32 mb + l32, keys 16 hi (+32) of the tile
+  // per-lane offsets: K row kappa_c(l32) of the tile, channels 64 dc + 16 hi (+32)
   const uint32_t kro0 = (uint32_t)kappa(0, l32) * D + 16 * hi;
   const uint32_t kso0 = (uint32_t)kappa(0, l32) * NSB;
-  const uint32_t vro = (uint32_t)l32 * a.Skp + 16 * hi;
+  // V^T tiles go through a 2-slot LDS ring of this wavefront by LDS DMA, one
+  // tile ahead: instruction n (0..7) writes chunks 64 n + lane, i.e. channel
+  // row 16 n + lane / 4, physical chunk lane % 4 holding logical chunk
+  // (lane % 4) ^ swz_v(row) (the swizzle does not depend on n); the tile's
+  // 256 scale bytes follow the codes.
+  const uint32_t vdma = (uint32_t)(lane >> 2) * F8_BC + ((((lane & 3) ^ swz_v(lane >> 2))) << 4);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const u32x4 rvd = buffer_rsrc(a.vt + kvh * (size_t)D * a.Skp, (uint32_t)(D * a.Skp));
+  const u32x4 rvsd = buffer_rsrc(a.vs + kvh * (size_t)(a.Skp / F8_BC) * (2 * D), (uint32_t)((a.Skp / F8_BC) * 2 * D));
+  uint32_t vb[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) vb[hh] = l32 * F8_BC + (((2 * hh + hi) ^ swz_v(l32)) << 4);
+  const uint32_t vsb = R::VT + 2 * l32 + hi;
 
-  i32x8 kf[2][DC], vf[MB];
-  int ksc[2], vsc[MB];
+  i32x8 kf[2][DC];
+  int ksc[2];
   auto load_k = [&](int t) __attribute__((always_inline)) {
     const uint32_t key0 = (uint32_t)(kbeg + t * F8_BC);
 #pragma unroll
@@ -481,16 +492,14 @@ __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __r
       ksc[c] = (int)(__builtin_amdgcn_raw_buffer_load_b32(rks, (key0 + 32 * c) * NSB + kso0, 0, 0) >> (8 * hi));
     }
   };
-  auto load_v = [&](int t) __attribute__((always_inline)) {
+  auto dma_v = [&](int t, auto slot_) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_)::value;
     const uint32_t key0 = (uint32_t)(kbeg + t * F8_BC);
-    const uint32_t tile = key0 / F8_BC;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint32_t base = (uint32_t)(32 * mb) * a.Skp + vro + key0;
-      vf[mb] = cat_u32x4(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, base, 0, 0)),
-                         __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, base + 32, 0, 0)));
-      vsc[mb] = (int)__builtin_amdgcn_raw_buffer_load_b8(rvs, (tile * D + 32 * mb + l32) * 2 + hi, 0, 0);
-    }
+    static_for<8>([&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      dma16b_at<SLOT * R::VST + n * 1024>(rvd, vdma + (key0 / F8_BC) * (D * F8_BC), (uint32_t)(n * 1024), lds0);
+    });
+    dma4b_at<SLOT * R::VST + R::VT>(rvsd, (key0 / F8_BC) * (2 * D) + 4 * lane, 0u, lds0);
   };
 
   f32x16 acc[MB];
@@ -499,9 +508,20 @@ __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __r
   float m2 = kNegInf, lsum = 0.f;
   if (ntiles > 0) {
     load_k(0);
-    load_v(0);
+    dma_v(0, std::integral_constant<int, 0>{});
   }
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, auto slot_) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_)::value;
+    // K(t) (registers) and V(t) (slot SLOT) have landed; V(t+1) goes out now,
+    // K(t+1) once the score MFMAs have read K(t)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) kf[c][dc] = settle(kf[c][dc]);
+      ksc[c] = settle(ksc[c]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (t + 1 < ntiles) dma_v(t + 1, std::integral_constant<int, SLOT ^ 1>{});
     f32x16 s[2];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
@@ -543,10 +563,22 @@ __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __r
       pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2], v[4 * w + 3], x, true);
     }
     lsum += tree_sum32(v);
+    const char* sv = smem + SLOT * R::VST;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f8<0, 0>(vf[mb], vsc[mb], pf, E8M0_ONE, acc[mb]);
-    if (t + 1 < ntiles) load_v(t + 1);
+    for (int mb = 0; mb < MB; ++mb) {
+      const i32x8 vq = cat_u32x4(*(const u32x4*)(sv + vb[0] + mb * 32 * F8_BC),
+                                 *(const u32x4*)(sv + vb[1] + mb * 32 * F8_BC));
+      const int vs = (int)*(const u8*)(sv + vsb + mb * 64);
+      acc[mb] = mfma_f8<0, 0>(vq, vs, pf, E8M0_ONE, acc[mb]);
+    }
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    tile(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -619,7 +651,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16* __restri
   if (part == 0) scales[blk] = (u8)(e + 127);
 }
 
-// V [BH, Sk, D] bf16 -> V^T codes [BH, D, Skp] and scales [BH, Skp/64, D, 2]:
+// V [BH, Sk, D] bf16 -> V^T codes [BH, Skp/64, D, 64] and scales [BH, Skp/64, D, 2]:
 // one workgroup per (head, 64-key tile); thread (c, kb) quantises the 32 keys
 // 32 kb .. of channel c. Keys past Sk count as zeros.
 template <int D>
@@ -654,7 +686,7 @@ __global__ __launch_bounds__(2 * D) void mx_quant_vt_kernel(const bf16* __restri
     amax = fmaxf(amax, fabsf(xv[i]));
   }
   const int e = mx_exponent(amax);
-  u8* dst = codes + (bh * D + c) * (size_t)Skp + key0 + 32 * kb;
+  u8* dst = codes + ((bh * ntile + t) * D + c) * (size_t)F8_BC + 32 * kb;
 #pragma unroll
   for (int g = 0; g < 4; ++g) *(u32x2*)(dst + 8 * g) = e4m3x8(xv + 8 * g, e);
   scales[((bh * ntile + t) * D + c) * 2 + kb] = (u8)(e + 127);

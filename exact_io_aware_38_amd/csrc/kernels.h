@@ -146,7 +146,8 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
 int fp8_padded_keys(int Sk);
 // x bf16 [rows, d] -> E4M3 codes [rows, d] and E8M0 scales [rows, d/32].
 hipError_t launch_mx_quant_rows(const void* x, void* codes, void* scales, long long rows, int d, hipStream_t s);
-// v bf16 [BH, Sk, d] -> V^T codes [BH, d, Skp] and scales [BH, Skp/64, d, 2].
+// v bf16 [BH, Sk, d] -> V^T codes tiled by 64 keys [BH, Skp/64, d, 64] and scales
+// [BH, Skp/64, d, 2].
 hipError_t launch_mx_quant_vt(const void* v, void* codes, void* scales, int BH, int Sk, int d, hipStream_t s);
 // Workspace of the FP8 forward: the split-key partials for decode-shaped
 // problems (the same rule and layout as the bf16 split path), else 0.

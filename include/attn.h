@@ -186,11 +186,12 @@ int attn_fp8_padded_keys(int Sk);
  * to nearest even (never saturating). rows >= 0; x 16-byte aligned. */
 int attn_mxfp8_quantize_rows(const void* x, void* codes, void* scales, long long rows, int d, void* stream);
 
-/* Quantise V (bf16 [BH, Sk, d]) along the keys into its transposed form:
- * codes [BH, d, Skp] (Skp = attn_fp8_padded_keys(Sk); padding keys hold 0)
- * and scales [BH, Skp/64, d, 2]: byte kb of channel c in 64-key tile t
- * covers keys 64t + 32kb .. +31. Same block rule as above, keys past Sk
- * counting as zeros. */
+/* Quantise V (bf16 [BH, Sk, d]) along the keys into its transposed form,
+ * tiled by 64 keys: codes [BH, Skp/64, d, 64] (Skp = attn_fp8_padded_keys(Sk);
+ * element (t, c, j) is key 64t + j of channel c; padding keys hold 0) and
+ * scales [BH, Skp/64, d, 2]: byte kb of channel c in tile t covers keys
+ * 64t + 32kb .. +31. Same block rule as above, keys past Sk counting as
+ * zeros. Each tile's codes (8 KB at d = 128) and scales are contiguous. */
 int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int BH, int Sk, int d, void* stream);
 
 /* Bytes of device workspace attn_fwd_fp8 needs (0 if none): decode-shaped

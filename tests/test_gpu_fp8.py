@@ -60,8 +60,17 @@ def _u8(t):
     return t.cpu().numpy()
 
 
+def _tile64(a):
+    """[B, H, d, Skp] -> the library's [B, H, Skp/64, d, 64] (64-key tiles)."""
+    B, H, d, n = a.shape
+    return np.ascontiguousarray(a.reshape(B, H, d, n // 64, 64).transpose(0, 1, 3, 2, 4))
+
+
 def _oracle_quant(q, k, v, Skp):
-    """The oracle's MXFP8 operands in the library's layouts (float64 inputs)."""
+    """The oracle's MXFP8 operands (float64 inputs): Q and K codes and scales,
+    V^T codes in the oracle's natural [B, H, d, Skp] and in the library's
+    tiled layout, V^T scales in the library's [B, H, Skp/64, d, 2] and the
+    natural [B, H, d, Skp/32]."""
     q8, qs = ofp8.mx_quantize(q, axis=-1)
     k8, ks = ofp8.mx_quantize(k, axis=-1)
     B, H, Sk, d = v.shape
@@ -166,6 +175,7 @@ def test_quantize_vt_bit_exact(attn, B, H, S, seed):
     v = synth.to_f64(xv, "bf16")
     _, _, _, _, vt8, vts, _ = _oracle_quant(np.zeros((1, 1, 1, 128)), np.zeros((1, 1, 1, 128)), v, Skp)
     assert np.array_equal(_u8(scales), vts)
+    vt8 = _tile64(vt8)
     assert np.array_equal(_u8(codes), vt8), f"{int((_u8(codes) != vt8).sum())} codes differ"
 
 
@@ -199,7 +209,7 @@ def _fwd_case(attn, B, Hq, Hkv, Sq, Sk, causal, seed, outliers=0.0):
     f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v")}
     Skp = attn.fp8_padded_keys(Sk)
     q8, qs, k8, ks, vt8, vts, vts_nat = _oracle_quant(f["q"], f["k"], f["v"], Skp)
-    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (q8, qs, k8, ks, vt8, vts)]
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (q8, qs, k8, ks, _tile64(vt8), vts)]
     o, lse = attn.fwd_fp8(*dev, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
     o_ref, lse_ref = ofp8.attention_forward_fp8(q8, qs, k8, ks, vt8, vts_nat, causal=causal, scale=w.scale)
@@ -239,7 +249,7 @@ def test_fwd_fp8_empty_rows_and_no_keys(attn):
     zs = torch.full((1, 2, 5, 4), 127, dtype=torch.uint8, device="cuda")
     k = torch.zeros((1, 2, 0, 128), dtype=torch.uint8, device="cuda")
     ks = torch.zeros((1, 2, 0, 4), dtype=torch.uint8, device="cuda")
-    vt = torch.zeros((1, 2, 128, 0), dtype=torch.uint8, device="cuda")
+    vt = torch.zeros((1, 2, 0, 128, 64), dtype=torch.uint8, device="cuda")
     vs = torch.zeros((1, 2, 0, 128, 2), dtype=torch.uint8, device="cuda")
     o, lse = attn.fwd_fp8(z, zs, k, ks, vt, vs, causal=0, scale=0.1)
     torch.cuda.synchronize()
