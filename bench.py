@@ -485,7 +485,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen", "fp8"], default="all")
+    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen", "fp8", "fp8_decode"],
+                    default="all")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5,
                     metavar=("WORKLOAD", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -534,6 +535,7 @@ def main() -> int:
         result["fp8"] = bench_fp8(attn, args.steps, args.warmup)
         print(f"# fp8: {result['fp8']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+    if args.only in ("all", "fp8_decode"):
         result["fp8_decode"] = bench_fp8_decode(attn, max(args.steps, 20), args.warmup)
         print(f"# fp8 decode: {result['fp8_decode']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
@@ -549,6 +551,11 @@ def main() -> int:
         result.update({"value": result["varlen"]["tflops"], "ms_per_step": result["varlen"]["ms"],
                        "config": {"workload": result["varlen"]["workload"]},
                        "roofline": result["varlen"]["roofline"]})
+    if args.only == "fp8_decode":
+        result.update({"value": result["fp8_decode"]["gbs"], "unit": "GB/s", "dtype": "e4m3",
+                       "ms_per_step": result["fp8_decode"]["ms"],
+                       "config": {"workload": result["fp8_decode"]["workload"]},
+                       "roofline": result["fp8_decode"]["roofline"]})
     if args.only == "fp8":
         result.update({"value": result["fp8"]["tflops"], "ms_per_step": result["fp8"]["ms"], "dtype": "e4m3",
                        "config": {"workload": result["fp8"]["workload"]}, "roofline": result["fp8"]["roofline"]})
