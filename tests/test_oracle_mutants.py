@@ -100,3 +100,49 @@ def test_unmutated_copy_passes_all_pins(monkeypatch):
         monkeypatch.setattr(pins, n, getattr(mod, n))
     for fn, kw in PIN_CALLS:
         fn(**kw)
+
+
+# ------------------------------------------------------------------ FP8 oracle
+import oracle.fp8 as fp8_mod          # noqa: E402
+import test_oracle_fp8 as fp8_pins    # noqa: E402
+
+FP8_MUTANTS = {
+    "e4m3_exponent_bias_8": ("np.exp2(ex.astype(np.float64) - 7.0)", "np.exp2(ex.astype(np.float64) - 8.0)"),
+    "e4m3_subnormals_one_binade_low": ("man / 8.0 * 2.0 ** -6", "man / 8.0 * 2.0 ** -7"),
+    "encode_ties_away_from_zero": ("q = np.rint(a / step)", "q = np.floor(a / step + 0.5)"),
+    "encode_subnormal_floor_off_by_one": ("E = np.maximum(E, -6.0)", "E = np.maximum(E, -7.0)"),
+    "block_exponent_saturating_floor_rule": ("e = E - 9 + (1 if f > 0.875 else 0)", "e = E - 9"),
+    "block_exponent_wasteful_by_one": ("e = E - 9 + (1 if f > 0.875 else 0)", "e = E - 8 + (1 if f > 0.875 else 0)"),
+    "dequantize_scale_bias_128": ("np.exp2(sm.astype(np.float64) - 127.0)", "np.exp2(sm.astype(np.float64) - 128.0)"),
+    "fp8_attention_uses_padding_keys": ("v = np.swapaxes(mx_dequantize(vt8, vs, axis=-1), -1, -2)[:, :, :Sk, :]",
+                                        "v = np.swapaxes(mx_dequantize(vt8, vs, axis=-1), -1, -2)[:, :, -Sk:, :]"),
+}
+
+FP8_PINS = [getattr(fp8_pins, n) for n in dir(fp8_pins) if n.startswith("test_")]
+
+
+def _fp8_mutant_module(old, new):
+    src = inspect.getsource(fp8_mod)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle.fp8_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "<oracle_fp8_mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_pins_catch_mutant(name, monkeypatch):
+    monkeypatch.setattr(fp8_pins, "fp8", _fp8_mutant_module(*FP8_MUTANTS[name]))
+    failures = 0
+    for fn in FP8_PINS:
+        try:
+            fn()
+        except (Exception, pytest.fail.Exception):
+            failures += 1
+    assert failures > 0, f"no FP8 pin caught mutant {name}"
+
+
+def test_fp8_unmutated_copy_passes_all_pins(monkeypatch):
+    monkeypatch.setattr(fp8_pins, "fp8", _fp8_mutant_module("import math", "import math"))
+    for fn in FP8_PINS:
+        fn()
