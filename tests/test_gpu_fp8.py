@@ -381,3 +381,39 @@ def test_fwd_fp8_decode_full_size_sampled(attn):
             assert_finite("O", og)
             assert (err <= bound).all(), f"(b={b}, kv head {hk}): {int((err > bound).sum())} elements outside the bound"
             _check_fp8_lse(lg, lse_ref, ltol)
+
+
+@pytest.mark.parametrize("Sq", [1, 64])
+@pytest.mark.parametrize("path", ["bf16", "fp8"])
+def test_maximum_key_count_closed_form(attn, path, Sq):
+    """Sk = 2^24 - 1 keys (the largest the library accepts; a bf16 head of K
+    or V is then 4 GiB minus 256 bytes, so every 32-bit byte offset is in
+    use). With K = 0 every visible key has probability 1/Sk, so O is the mean
+    of V and lse = ln(Sk). V is zero except value 1 in every channel of the
+    last 100 keys and 2 more in channel 0 of the first 50: O[0] = 200/Sk,
+    O[c > 0] = 100/Sk, exactly representable sums in fp32 (all below 2^24),
+    and in E4M3 (1 and 3 times a power-of-two block scale). Sq = 1 runs the
+    split-key decode kernels, Sq = 64 (256 grouped rows) the prefill ones."""
+    import torch
+    Sk = (1 << 24) - 1
+    _say(f"Sq = {Sq}, Sk = {Sk} ({path})")
+    B, Hq, Hkv, d = 1, 4, 1, 128
+    q = torch.randn((B, Hq, Sq, d), device="cuda").to(torch.bfloat16)
+    k = torch.zeros((B, Hkv, Sk, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((B, Hkv, Sk, d), dtype=torch.bfloat16, device="cuda")
+    v[:, :, Sk - 100:, :] = 1.0
+    v[:, :, :50, 0] = 2.0
+    if path == "bf16":
+        o, lse = attn.fwd(q, k, v, causal=0)
+    else:
+        ops = attn.mxfp8_quantize_rows(q) + attn.mxfp8_quantize_rows(k) + attn.mxfp8_quantize_vt(v)
+        del k, v
+        o, lse = attn.fwd_fp8(*ops, causal=0)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert ("split" in attn.last_dispatch()) == (Sq == 1)
+    ref = np.full((B, Hq, Sq, d), 100.0 / Sk)
+    ref[..., 0] = 200.0 / Sk
+    assert np.abs(o - ref).max() <= 2.0 ** -8 * ref.max(), (o[0, 0, 0, :4], ref[0, 0, 0, :4])
+    assert np.abs(lse - np.log(Sk)).max() <= 1e-3
