@@ -601,23 +601,26 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
   if (row >= rows) return;
   const size_t orow = (row / Sq) * (size_t)hsq + row % Sq;   // (b, h, i) in the output's layout
   const int lane = threadIdx.x;
+  // the slices' lse spread over the lanes, then a wavefront max
   float m = kNegInf;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[(size_t)s * rows + row]);
+  for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, part_lse[(size_t)s * rows + row]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   constexpr int PER = D / 64;
   float accv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) accv[j] = 0.f;
   float tot = 0.f;
   if (m != kNegInf) {
+    // no branch on the weight: an empty slice has lse = -inf (weight 0) and a
+    // zero partial, so the loads of several slices can be in flight together
+#pragma unroll 4
     for (int s = 0; s < nsplit; ++s) {
-      const float ls = part_lse[(size_t)s * rows + row];
-      const float w = __expf(ls - m);      // exp(-inf) = 0 for empty slices
+      const float w = __expf(part_lse[(size_t)s * rows + row] - m);
       tot += w;
-      if (w != 0.f) {
-        const float* po = part_o + ((size_t)s * rows + row) * D;
+      const float* po = part_o + ((size_t)s * rows + row) * D + lane * PER;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) accv[j] += w * po[lane * PER + j];
-      }
+      for (int j = 0; j < PER; ++j) accv[j] += w * po[j];
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
