@@ -401,13 +401,13 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
 // Split-key decode on MXFP8 operands: one 64-lane wavefront per (key slice,
 // KV head, batch); its 32 MFMA columns pack (query head of the group, query
 // row) pairs, so every K/V byte of the slice is read once for all of them.
-// Decode streams K and V once, so the operands go straight from HBM into
-// registers (range-checked buffer loads; the transposed V gives each lane
-// two contiguous 16-byte chunks per 32-channel block) and occupancy (about
-// eight wavefronts per CU) keeps enough loads in flight; the K fragments of
-// the next 64-key tile are loaded as soon as the score MFMAs have read the
-// current ones, the V fragments as soon as the P V MFMAs have. Writes the
-// slice's normalised partial output and lse for the merge kernel.
+// Decode streams K and V once and is bound by the loads in flight (about
+// eight wavefronts per CU): K fragments go straight from HBM into registers
+// (range-checked buffer loads), those of the next 64-key tile as soon as
+// the score MFMAs have read the current ones; V^T tiles (contiguous 8 KB in
+// the tiled layout) go through a 2-slot LDS ring of the wavefront, the next
+// one issued by LDS DMA at the start of each tile. Writes the slice's
+// normalised partial output and lse for the merge kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __restrict__ part_o,
