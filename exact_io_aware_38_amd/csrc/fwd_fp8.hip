@@ -20,8 +20,11 @@
 //    operand of O^T = V^T P^T.
 //
 // The recurrence is the bf16 prefill's (online softmax over 64-key tiles,
-// two wavefronts per SIMD in opposite phases, a 4-stage LDS ring fed by LDS
-// DMA two tiles ahead), with these changes:
+// two wavefronts per SIMD in opposite phases, an LDS ring fed by LDS DMA),
+// with these changes:
+//  * the ring has 8 stages and the DMA runs three tiles ahead, so the
+//    workgroup needs a barrier only every other step (the barrier held the
+//    eight wavefronts in lockstep around the softmax; halving it saves 3 %);
 //  * operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured with an
 //    in-bounds probe of the builtin): lane l holds row (A) or column (B)
 //    l % 32; its operand bytes 0..15 lie in k-block 0 (k 0..31), bytes 16..31
@@ -89,7 +92,7 @@ struct Fp8Ring {
   static constexpr int VS_OFF = KS_OFF + KS;
   static constexpr int STAGE = VS_OFF + VS;
   static constexpr int VST = VT + VS;           // a V^T tile and its scales (decode ring slot)
-  static constexpr int NSTAGE = 4;
+  static constexpr int NSTAGE = 8;
 };
 
 // S^T / O^T product with per-lane E8M0 scales (byte OPA of sa for the A
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
   constexpr int DC = D / 64;                    // MFMAs per 32x32 score block
   constexpr int MB = D / 32;                    // 32-channel blocks of the output
   constexpr int NSB = D / 32;                   // scale bytes per Q or K row
-  static_assert(R::NSTAGE == 4, "the main loop is unrolled by the ring size");
+  static_assert(R::NSTAGE == 8, "the main loop is unrolled by the ring size");
   static_assert(R::KT == 8 * 1024 && R::VT == 8 * 1024, "one 1 KB DMA instruction per wavefront per tensor");
 
   __shared__ __attribute__((aligned(1024))) char smem[R::NSTAGE * R::STAGE];
@@ -253,8 +256,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
     constexpr bool DS = decltype(do_s)::value;
     constexpr bool DP = decltype(do_pv)::value;
     constexpr int SK = POS;                     // K of tile j
-    constexpr int SV = (POS + 3) % 4;           // V of tile j-1
-    constexpr int SD = (POS + 2) % 4;           // DMA target: tile j+2
+    constexpr int SV = (POS + 7) % 8;           // V of tile j-1
+    constexpr int SD = (POS + 3) % 8;           // DMA target: tile j+3
     const char* stk = smem + SK * R::STAGE;
     const char* stv = smem + SV * R::STAGE;
     auto kfrag = [&](auto ic) __attribute__((always_inline)) {
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
       return cat_u32x4(*(const u32x4*)(stv + vb[0] + mb * 32 * F8_BC), *(const u32x4*)(stv + vb[1] + mb * 32 * F8_BC));
     };
     Dma d;
-    if constexpr (DS) d = dma_for(j + 2);
+    if constexpr (DS) d = dma_for(j + 3);
     int ksc[2] = {0, 0}, vsc[MB];
     i32x8 kq[2], vq[2];
     if constexpr (DS) {
@@ -334,45 +337,55 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // step j: every wavefront's DMA of tile j has landed (each waits for its
-  // own: 2 or 3 instructions a step may still be in flight, those of tile
-  // j+1), and every wavefront is done with step j-1
+  // Even step j: every wavefront's DMA of tiles j and j+1 has landed (each
+  // waits for its own: 2 or 3 instructions may still be in flight, those of
+  // tile j+2), and every wavefront is done with step j-1. Odd steps need no
+  // barrier: their tiles were covered by the previous one, and the slot a
+  // step's DMA overwrites (tile j-5, ring of 8, DMA three tiles ahead) was
+  // last read in step j-4, which every wavefront had finished at the last
+  // barrier.
   auto sync = [&]() __attribute__((always_inline)) {
     if (scale_dma) asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
   };
   auto full = [&](auto pos_, int j) __attribute__((always_inline)) {
-    sync();
+    if constexpr (decltype(pos_)::value % 2 == 0) sync();
     if (phase_b) softmax(j - 1);
     mma(pos_, T_{}, T_{}, j);
     if (!phase_b) softmax(j);
   };
 
   if (ntiles > 0) {
-    const Dma d0 = dma_for(0), d1 = dma_for(1);
+    const Dma d0 = dma_for(0), d1 = dma_for(1), d2 = dma_for(2);
     static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I0{}, qi, d0); });
     static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I1{}, qi, d1); });
+    static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I2{}, qi, d2); });
     sync();
     mma(I0{}, T_{}, F_{}, 0);
     if (!phase_b) softmax(0);
   }
   int j = 1;
-  for (; j + 3 < ntiles; j += 4) {
-    full(I1{}, j);
-    full(I2{}, j + 1);
-    full(I3{}, j + 2);
-    full(I0{}, j + 3);
+  for (; j + 7 < ntiles; j += 8) {
+    static_for<8>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      full(std::integral_constant<int, (k + 1) % 8>{}, j + k);
+    });
   }
-  if (j < ntiles) full(I1{}, j);
-  if (j + 1 < ntiles) full(I2{}, j + 1);
-  if (j + 2 < ntiles) full(I3{}, j + 2);
+  static_for<7>([&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    if (j + k < ntiles) full(std::integral_constant<int, k + 1>{}, j + k);
+  });
   if (ntiles > 0) {
     if (phase_b) softmax(ntiles - 1);
-    switch (ntiles & 3) {
+    switch (ntiles & 7) {
       case 0: mma(I0{}, F_{}, T_{}, ntiles); break;
       case 1: mma(I1{}, F_{}, T_{}, ntiles); break;
       case 2: mma(I2{}, F_{}, T_{}, ntiles); break;
-      default: mma(I3{}, F_{}, T_{}, ntiles); break;
+      case 3: mma(I3{}, F_{}, T_{}, ntiles); break;
+      case 4: mma(std::integral_constant<int, 4>{}, F_{}, T_{}, ntiles); break;
+      case 5: mma(std::integral_constant<int, 5>{}, F_{}, T_{}, ntiles); break;
+      case 6: mma(std::integral_constant<int, 6>{}, F_{}, T_{}, ntiles); break;
+      default: mma(std::integral_constant<int, 7>{}, F_{}, T_{}, ntiles); break;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
