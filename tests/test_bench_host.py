@@ -1,0 +1,77 @@
+"""Host logic of the benchmark (CPU only): the work each kernel is credited
+with, the roofline arithmetic, the counter staleness rule, the stats
+summary, and the one-GPU guard."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_nominal_flops_match_the_formula():
+    # 4 B H Sq Sk d, halved for causal
+    assert bench.nominal_fwd_flops(2, 32, 8192, 8192, 128, 1) == 2 * 32 * 8192 * 8192 * 128 * 2
+    assert bench.nominal_fwd_flops(1, 1, 256, 256, 64, 0) == 4 * 256 * 256 * 64
+
+
+def test_kernel_work_per_launch():
+    w = synth.get_workload("train_causal_d128")
+    fwd = bench.nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
+    assert bench.kernel_work("fwd_prefill_bf16", w) == {"bound": "mfma", "flops": fwd}
+    assert bench.kernel_work("bwd_dkdv", w)["flops"] == 2 * fwd          # S, dP, dV, dK: 8 d per pair
+    assert bench.kernel_work("bwd_dq", w)["flops"] == 0.5 * fwd          # dQ only: 2 d per pair
+    assert bench.kernel_work("fwd_fp8", w)["peak"] == bench.PEAK_FP8_TFLOPS
+    d = synth.get_workload("gqa_decode")
+    kv = 2 * d.B * d.Hkv * d.Sk * d.d
+    assert bench.kernel_work("fwd_split_bf16", d)["bytes"] == 2 * kv + d.B * d.Hq * d.Sq * d.d * 2
+    f8 = bench.kernel_work("fwd_fp8_split", d)["bytes"]
+    assert f8 == pytest.approx(kv * (1 + 1 / 32) + d.B * d.Hq * d.Sq * d.d * (1 + 1 / 32))
+
+
+def test_roofline_arithmetic():
+    w = synth.get_workload("long_causal_d128")
+    r = bench.roofline("fwd_prefill_bf16", w, 1.0)
+    flops = bench.nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == bench.PEAK_BF16_TFLOPS
+    assert r["achieved"] == pytest.approx(flops / 1e-3 / 1e12, rel=1e-4)
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
+    d = synth.get_workload("gqa_decode")
+    r = bench.roofline("fwd_split_bf16", d, 0.5)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.PEAK_HBM_GBS
+    assert r["achieved"] == pytest.approx(bench.kernel_work("fwd_split_bf16", d)["bytes"] / 0.5e-3 / 1e9, rel=1e-4)
+
+
+def test_traffic_is_null_for_stale_or_missing_counters(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.traffic_for("fwd_fp8", "long_causal_d128_mxfp8") is None        # missing
+    path = tmp_path / "counters_fwd_fp8__long_causal_d128_mxfp8.json"
+    path.write_text(json.dumps({"source_sha": bench.source_hash("fwd_fp8"), "hbm_bytes_per_launch": 123}))
+    assert bench.traffic_for("fwd_fp8", "long_causal_d128_mxfp8") == 123           # current
+    path.write_text(json.dumps({"source_sha": "0" * 16, "hbm_bytes_per_launch": 123}))
+    assert bench.traffic_for("fwd_fp8", "long_causal_d128_mxfp8") is None        # kernel changed since
+
+
+def test_stats_summary_table(tmp_path):
+    csv_path = tmp_path / "kernel_stats.csv"
+    csv_path.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+                        '"void attn::(anonymous namespace)::fwd_fp8_kernel<128>(attn::(anonymous namespace)::Fp8Args)",'
+                        '25,23157637,926305.48,96.47,844962,1038135,56008.9\n'
+                        '"_ZN4attn12_GLOBAL__N_120mx_quant_rows_kernelEPKDF16bPhS3_x",14,489691,34977.9,2.04,33396,37114,1047.8\n')
+    out = tmp_path / "s.md"
+    bench.summarize_stats(str(csv_path), "t", str(out), "cmd")
+    text = out.read_text()
+    assert "| fwd_fp8_kernel<128> | 25 | 926.3 | 845.0 | 1038.1 | 96.5% |" in text
+    assert "| mx_quant_rows_kernel | 14 | 35.0 |" in text
+    assert "cmd" in text
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
