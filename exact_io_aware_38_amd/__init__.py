@@ -152,6 +152,11 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# Pointer alignment the library requires (include/attn.h): 4 bytes for lse and
+# the FP8 scale arrays, 16 bytes for every other tensor and the workspace.
+_ALIGN4 = {"lse", "scales", "q_scales", "k_scales", "vt_scales"}
+
+
 def _check(t, name: str):
     if t is None:
         return
@@ -159,6 +164,10 @@ def _check(t, name: str):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    align = 4 if name in _ALIGN4 else 16
+    if t.data_ptr() % align != 0:
+        raise ValueError(f"{name} must start at a {align}-byte aligned address (a view with an odd "
+                         "storage offset is not)")
 
 
 def _want(t, shape, dtype, name: str):

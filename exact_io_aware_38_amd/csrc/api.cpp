@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <cstdint>
 #include <string>
 #include <vector>
 
@@ -59,6 +60,13 @@ void record(const char* text) {
   std::snprintf(g_dispatch, sizeof(g_dispatch), "%s", text);
   if (log_enabled()) std::fprintf(stderr, "[attn] %s\n", g_dispatch);
 }
+
+// Alignment contract of include/attn.h: tensors and workspaces move in
+// 16-byte vectors, lse and FP8 scale arrays in 4-byte words. NULL passes (the
+// NULL checks come first and are per entry point).
+bool misaligned(const void* p, uintptr_t a) { return p != nullptr && ((uintptr_t)p & (a - 1)) != 0; }
+template <typename... P>
+bool any16(P... p) { return (misaligned(p, 16) || ...); }
 
 int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale, int dtype) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 0) return ATTN_ERR_SHAPE;
@@ -272,6 +280,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_HIP: return "HIP runtime error while launching";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_DROPOUT: return "dropout probability must lie in [0, 1) and round below 256/256";
+    case ATTN_ERR_ALIGN: return "misaligned pointer: tensors and workspace need 16 bytes, lse and scales 4";
     default: return "unknown status";
   }
 }
@@ -296,6 +305,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (q == nullptr || o == nullptr || (Sk != 0 && (k == nullptr || v == nullptr))) return ATTN_ERR_NULL;
   const int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
+  if (any16(q, k, v, o, workspace) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
   if (fwd_ws(p, dtype) > 0 && (workspace == nullptr || workspace_bytes < fwd_ws(p, dtype))) return ATTN_ERR_WORKSPACE;
   char text[480], line[512];
@@ -322,6 +332,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (any16(q, k, v, o, dout, dq, dk, dv, workspace) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
   const size_t need = attn::bwd_workspace_bytes(p);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -352,6 +363,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   const bool any_q = cu_seqlens_q[B] > 0, any_k = cu_seqlens_k[B] > 0;
   if ((any_q && (q == nullptr || o == nullptr)) || (any_q && any_k && (k == nullptr || v == nullptr)))
     return ATTN_ERR_NULL;
+  if (any16(q, k, v, o, workspace) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   const size_t need = attn_fwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
   const hipStream_t s = (hipStream_t)stream;
@@ -419,6 +431,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   if ((any_q && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr)) ||
       (any_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
     return ATTN_ERR_NULL;
+  if (any16(q, k, v, o, dout, dq, dk, dv, workspace) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   const size_t need = attn_bwd_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, d, causal, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
   // a sequence with keys but no query still takes part: its dK and dV rows
@@ -447,6 +460,7 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float
   if (q == nullptr || o == nullptr || (Sk != 0 && (k == nullptr || v == nullptr))) return ATTN_ERR_NULL;
   int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, ATTN_BF16);
   if (st != ATTN_OK) return st;
+  if (any16(q, k, v, o) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
   st = make_drop(dropout_p, seed, offset, p.drop);
   if (st != ATTN_OK) return st;
@@ -472,6 +486,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
     return ATTN_ERR_NULL;
   int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, ATTN_BF16);
   if (st != ATTN_OK) return st;
+  if (any16(q, k, v, o, dout, dq, dk, dv, workspace) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
   st = make_drop(dropout_p, seed, offset, p.drop);
   if (st != ATTN_OK) return st;
@@ -512,6 +527,7 @@ int attn_mxfp8_quantize_rows(const void* x, void* codes, void* scales, long long
   if (d != 128) return ATTN_ERR_HEADDIM;
   if (rows > (1LL << 31) - 1) return ATTN_ERR_SHAPE;
   if (rows > 0 && (x == nullptr || codes == nullptr || scales == nullptr)) return ATTN_ERR_NULL;
+  if (any16(x, codes)) return ATTN_ERR_ALIGN;
   if (attn::launch_mx_quant_rows(x, codes, scales, rows, d, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
   char line[128];
   std::snprintf(line, sizeof(line), "attn_mxfp8_quantize_rows: %lld rows of d=%d", rows, d);
@@ -524,6 +540,7 @@ int attn_mxfp8_quantize_vt(const void* v, void* vt_codes, void* vt_scales, int B
   if ((long long)BH * Sk > (1LL << 31) - 1) return ATTN_ERR_SHAPE;
   if (d != 128) return ATTN_ERR_HEADDIM;
   if (Sk > 0 && (v == nullptr || vt_codes == nullptr || vt_scales == nullptr)) return ATTN_ERR_NULL;
+  if (any16(v, vt_codes)) return ATTN_ERR_ALIGN;
   if (attn::launch_mx_quant_vt(v, vt_codes, vt_scales, BH, Sk, d, (hipStream_t)stream) != hipSuccess)
     return ATTN_ERR_HIP;
   char line[128];
@@ -547,6 +564,9 @@ int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const voi
   const int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, ATTN_BF16);
   if (st != ATTN_OK) return st;
   if (d != 128) return ATTN_ERR_HEADDIM;
+  if (any16(q8, k8, vt8, o, workspace) || misaligned(q_scales, 4) || misaligned(k_scales, 4) ||
+      misaligned(vt_scales, 4) || misaligned(lse, 4))
+    return ATTN_ERR_ALIGN;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
   const size_t need = attn::fp8_workspace_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;

@@ -453,9 +453,12 @@ __global__ __launch_bounds__(64) void fwd_split_kernel(FwdArgs a) {
   }
   const size_t kvh = (size_t)b * a.Hkv + hkv;
   // whole-head buffers: rows past Sk read zeros (their scores are masked or,
-  // for V, multiplied by P = 0)
+  // for V, multiplied by P = 0). The byte range is an unsigned 32-bit count
+  // (Sk < 2^24 rows of up to 256 bytes), passed bit for bit to the builtin's
+  // int parameter.
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.k + kvh * (size_t)a.hsk * D), (short)0, a.Sk * RB, 0x00020000);
+      (void*)(a.k + kvh * (size_t)a.hsk * D), (short)0, __builtin_bit_cast(int, (uint32_t)a.Sk * (uint32_t)RB),
+      0x00020000);
   const u32x4 rv = buffer_rsrc(a.v + kvh * (size_t)a.hsk * D, (uint32_t)a.Sk * RB);
   // K fragment dc of key row l32: byte l32*RB + 16*hi + 32*dc of the tile
   const uint32_t kl = l32 * RB + 16 * hi;

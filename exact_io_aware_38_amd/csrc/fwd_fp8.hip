@@ -469,7 +469,9 @@ __global__ __launch_bounds__(64) void fwd_fp8_split_kernel(Fp8Args a, float* __r
     qsc = settle(qsc);
   }
   const size_t kvh = (size_t)b * a.Hkv + hkv;
-  // whole-head buffers: K rows past Sk read zeros (their scores are masked)
+  // whole-head buffers: K rows past Sk read zeros (their scores are masked).
+  // The int byte ranges cannot overflow: Sk < 2^24 and a code row is
+  // D = 128 bytes, so Sk * D < 2^31 (scale rows are 4 bytes).
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + kvh * (size_t)a.Sk * D), (short)0, a.Sk * D, 0x00020000);
   const __amdgpu_buffer_rsrc_t rks =

@@ -29,6 +29,14 @@
  * explicit rule for fully masked rows that "AI 大模型之 FlashAttention_01"
  * (section "工程实操") asks an interface to define.
  *
+ * Alignment: the kernels move data in 16-byte vectors, so every tensor
+ * pointer (q, k, v, o, dout, dq, dk, dv, the FP8 code arrays, the bf16 input
+ * of the quantisers) and the workspace must be 16-byte aligned; lse and the
+ * FP8 scale arrays must be 4-byte aligned. A misaligned pointer returns
+ * ATTN_ERR_ALIGN before anything is launched. (Memory from hipMalloc or a
+ * PyTorch allocation is 256-byte aligned; a view that starts at an odd
+ * element offset may not be.)
+ *
  * Restrictions (the kernels are specialised, as that page's limitations
  * section notes for high-performance attention kernels): d in {64, 128};
  * Hq a multiple of Hkv (grouped heads are contiguous); scale finite and > 0;
@@ -66,7 +74,8 @@ enum attn_status {
   ATTN_ERR_WORKSPACE = -7,  /* workspace smaller than the query says, or NULL when needed */
   ATTN_ERR_HIP = -8,        /* a HIP runtime call or kernel launch failed */
   ATTN_ERR_SCALE = -9,      /* scale not finite or not > 0 */
-  ATTN_ERR_DROPOUT = -10    /* dropout probability not in [0, 1) or rounding to 1 */
+  ATTN_ERR_DROPOUT = -10,   /* dropout probability not in [0, 1) or rounding to 1 */
+  ATTN_ERR_ALIGN = -11      /* a data pointer lacks the alignment stated above */
 };
 
 enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
@@ -119,9 +128,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * in the forward and zero dk/dv rows in the backward; one without keys gives
  * o = 0, lse = -inf, dq = 0. Every other argument means what it means for
  * attn_fwd/attn_bwd (the per-sequence shape checks apply to each sequence;
- * Hq * total_q and Hkv * total_k must stay below 2^31). The library launches
- * the kernels once per non-empty sequence, in order, on the given stream, so
- * one workspace of the size the query returns serves them all. */
+ * Hq * total_q and Hkv * total_k must stay below 2^31). All launches go to
+ * the given stream. Forward: decode-shaped sequences (Hq/Hkv * length <= 32)
+ * and every ATTN_F32 sequence run first, one split-key (or fp32) launch per
+ * sequence in batch order, each reusing the start of the one workspace; the
+ * remaining bf16 sequences then run as packed grids of up to 64 sequences
+ * each (largest work first), which need no workspace. Backward: packed grids
+ * of up to 64 sequences (bwd_pre, dK/dV, dQ kernels per grid) over every
+ * sequence with queries or keys, in the same order; the workspace holds the
+ * lse2/D rows of every sequence at once. So one workspace of the size the
+ * query returns serves the whole call. */
 size_t attn_fwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
                                        int Hq, int Hkv, int d, int causal, int dtype);
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -218,9 +234,12 @@ int attn_fwd_fp8(const void* q8, const void* q_scales, const void* k8, const voi
 /* Static text for a status code (never NULL). */
 const char* attn_strerror(int status);
 
-/* Copies into buf (host memory, n bytes, NUL-terminated) a description of
- * the kernels the calling thread's last successful attn_fwd/attn_bwd
- * launched: kernel names, grid and tile shapes. Returns the full length of
+/* Dispatch record. "AI 大模型之 FlashAttention_01", section "性能验证方法",
+ * asks that a benchmark confirm which kernel actually ran and keep a log of
+ * the dispatch decision; this is that record.
+ * Copies into buf (host memory, n bytes, NUL-terminated) a description of
+ * the kernels the calling thread's last successful call launched: kernel
+ * names, grid and tile shapes. Returns the full length of
  * the description (like snprintf), or a negative status if buf is NULL with
  * n > 0. When the environment variable ATTN_LOG is set to 1 the same line is
  * also printed to stderr on every call. */

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     codes = {0: "success", -1: "NULL", -2: "shape", -3: "multiple", -4: "head dim", -5: "dtype",
-             -6: "causal", -7: "workspace", -8: "HIP", -9: "scale"}
+             -6: "causal", -7: "workspace", -8: "HIP", -9: "scale", -10: "dropout", -11: "misaligned"}
     for c, word in codes.items():
         assert word.lower() in attn.strerror(c).lower()
     assert "unknown" in attn.strerror(-99)
@@ -279,3 +279,60 @@ def test_mxfp8_quantizer_validation():
     assert L.attn_mxfp8_quantize_vt(FAKE, FAKE, FAKE, 2, 100, 96, None) == -4
     assert [attn.fp8_padded_keys(n) for n in (0, 1, 64, 65, 2000)] == [0, 64, 64, 128, 2048]
     assert L.attn_fp8_padded_keys(-1) == -2
+
+
+# ---------------------------------------------------------------- pointer alignment
+ODD16 = FAKE + 8        # 8-byte but not 16-byte aligned
+ODD4 = FAKE + 2         # not even 4-byte aligned
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "ws"])
+def test_fwd_rejects_misaligned_tensors(name):
+    over = {name: ODD16}
+    if name == "ws":
+        over["ws_bytes"] = 1 << 20
+    assert _fwd(**over) == -11
+    assert _fwd(lse=ODD4) == -11
+    assert _fwd(lse=FAKE + 4) != -11      # lse needs only 4 bytes
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "do", "dq", "dk", "dv", "ws"])
+def test_bwd_rejects_misaligned_tensors(name):
+    assert _bwd(**{name: ODD16, "ws_bytes": 1 << 20} if name == "ws" else {name: ODD16}) == -11
+    assert _bwd(lse=ODD4) == -11
+
+
+def test_other_entry_points_reject_misaligned_tensors():
+    assert _fwd_varlen(q=ODD16) == -11
+    assert _bwd_varlen(dk=ODD16) == -11
+    assert _fwd_drop(v=ODD16) == -11
+    assert _bwd_drop(dq=ODD16) == -11
+    assert _fwd_fp8(k=ODD16) == -11
+    assert _fwd_fp8(ks=ODD4) == -11
+    assert _fwd_fp8(ks=FAKE + 4) != -11    # scale arrays need only 4 bytes
+    L = attn.lib()
+    assert L.attn_mxfp8_quantize_rows(ODD16, FAKE, FAKE, 4, 128, None) == -11
+    assert L.attn_mxfp8_quantize_vt(FAKE, ODD16, FAKE, 2, 100, 128, None) == -11
+
+
+class _FakeTensor:
+    """Stands in for a GPU tensor in the binding's argument checks (no device needed)."""
+
+    def __init__(self, ptr):
+        self._ptr = ptr
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return self._ptr
+
+
+def test_binding_checks_alignment_before_calling():
+    attn._check(_FakeTensor(FAKE), "q")
+    attn._check(_FakeTensor(FAKE + 4), "lse")
+    with pytest.raises(ValueError, match="16-byte"):
+        attn._check(_FakeTensor(ODD16), "q")
+    with pytest.raises(ValueError, match="4-byte"):
+        attn._check(_FakeTensor(ODD4), "lse")
