@@ -12,12 +12,22 @@ variable-length entry points) and the long-context forward on MXFP8 operands
 their own) and the decode on MXFP8 operands, which report as their own sub-objects. Inputs are resident in
 device memory before timing starts.
 
+Further sub-objects time the forward alone on the other specified
+workloads: the single-head fp32 problem, the four multi-head d=64 variants
+(non-causal, causal, ragged keys, ragged causal; with the causal/non-causal
+time ratios) and the grouped-query prefill. Every timed entry reports the mean
+over the timed steps and the spread of the per-step times (median, p10, p90,
+min, max).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration          (a plain copy of known size,
                                                     for counter calibration)
        python bench.py --summarize-counters WORKLOAD FETCH_DIR WRITE_DIR
                        COPY_FETCH_DIR COPY_WRITE_DIR   (turn rocprofv3 --pmc
                        output into per-kernel HBM-traffic summaries in profiles/)
+       python bench.py --summarize-pmc WORKLOAD TITLE DIR [DIR ...]
+                       (per-kernel shader counters of rocprofv3 --pmc runs,
+                       with MFMA utilisation and instruction mix, in profiles/)
 """
 from __future__ import annotations
 
@@ -38,6 +48,9 @@ METRIC = "attention TFLOP/s fwd & fwd+bwd, bf16 d=128 causal S=8K; % of MFMA pea
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector, published
+N_SIMD = 1024                 # 256 CUs x 4 SIMDs
+N_XCD = 8
 CSRC = os.path.join(ROOT, "exact_io_aware_38_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -50,6 +63,7 @@ KERNEL_SOURCES = {
     "bwd_pre": ["bwd_bf16.hip", "common.h", "kernels.h"],
     "fwd_fp8": ["fwd_fp8.hip", "common.h", "kernels.h", "tiles.h"],
     "fwd_fp8_split": ["fwd_fp8.hip", "common.h", "kernels.h", "tiles.h"],
+    "fwd_f32": ["fwd_f32.hip", "common.h", "kernels.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
 # (the dense and the packed instantiations both match; a workload uses one)
@@ -62,6 +76,8 @@ KERNEL_SYMBOLS = {
     "fwd_fp8": "fwd_fp8_kernel<128>",
     "fwd_fp8_split": "fwd_fp8_split_kernel<128>",
 }
+# the same for the d = 64 instantiations (multi-head d = 64 workloads)
+KERNEL_SYMBOLS_D64 = {k: v.replace("<128", "<64") for k, v in KERNEL_SYMBOLS.items()}
 
 
 def source_hash(kernel: str) -> str:
@@ -90,6 +106,8 @@ def kernel_work(kernel: str, w) -> dict:
     e = 2  # bf16 bytes
     if kernel == "fwd_prefill_bf16":
         return {"bound": "mfma", "flops": fwd}
+    if kernel == "fwd_f32":
+        return {"bound": "alu", "flops": fwd, "peak": PEAK_F32_VALU_TFLOPS}
     if kernel == "fwd_fp8":
         return {"bound": "mfma", "flops": fwd, "peak": PEAK_FP8_TFLOPS}
     if kernel == "bwd_dkdv":
@@ -128,7 +146,7 @@ def traffic_for(kernel: str, workload: str):
 
 def roofline(kernel: str, w, avg_ms: float, work: dict = None) -> dict:
     work = kernel_work(kernel, w) if work is None else work
-    if work["bound"] == "mfma":
+    if work["bound"] in ("mfma", "alu"):
         ach = work["flops"] / (avg_ms * 1e-3) / 1e12
         peak, unit = work.get("peak", PEAK_BF16_TFLOPS), "TFLOP/s"
     else:
@@ -147,9 +165,21 @@ def _device_inputs(w):
     out = {}
     for n in ("q", "k", "v", "do"):
         if n in x:
-            out[n] = torch.from_numpy(x[n].view(np.int16)).cuda().view(torch.bfloat16)
+            if w.dtype == "bf16":
+                out[n] = torch.from_numpy(x[n].view(np.int16)).cuda().view(torch.bfloat16)
+            else:
+                out[n] = torch.from_numpy(np.ascontiguousarray(x[n], dtype=np.float32)).cuda()
     del x
     return out
+
+
+def spread(per_step_ms) -> dict:
+    """Median, p10, p90, min and max of the per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(per_step_ms, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "min_ms": round(float(a.min()), 4),
+            "max_ms": round(float(a.max()), 4), "n": int(a.size)}
 
 
 def _fwd_workspace(attn, w):
@@ -158,23 +188,29 @@ def _fwd_workspace(attn, w):
     return torch.empty(max(1, n), dtype=torch.uint8, device="cuda")
 
 
+_LAST_SPREAD = {}
+
+
 def _time(fn, steps: int, warmup: int, attn, per_step: bool = False):
     """Mean ms per step from events around the timed loop, and each kernel's
-    device time: mean per launch, or (per_step) summed over a step."""
+    device time: mean per launch, or (per_step) summed over a step. An event
+    recorded after every step also gives each step's own time; their spread
+    is left in _LAST_SPREAD."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     attn.timing_start()
-    start.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         fn()
-    end.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     kern = attn.timing_stop()
-    ms = start.elapsed_time(end) / steps
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    _LAST_SPREAD.clear()
+    _LAST_SPREAD.update(spread([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
     if per_step:
         return ms, {k: v[1] / steps for k, v in kern.items()}
     return ms, {k: v[1] / v[0] for k, v in kern.items()}
@@ -201,25 +237,48 @@ def bench_step(attn, steps, warmup):
     fwd = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
     total = 3.5 * fwd
     dom = max(kern, key=kern.get)
-    return w, ms, total, kern, dom
+    return w, ms, total, kern, dom, dict(_LAST_SPREAD)
 
 
-def bench_fwd(attn, steps, warmup):
+def bench_fwd(attn, steps, warmup, name: str = "long_causal_d128"):
+    """attn_fwd alone on one of the specified workloads (inputs resident)."""
     import torch
     import synth
-    w = synth.get_workload("long_causal_d128")
+    w = synth.get_workload(name)
     t = _device_inputs(w)
     o = torch.empty_like(t["q"])
     lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
     fws = _fwd_workspace(attn, w)
     ms, kern = _time(lambda: attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o,
                                       lse=lse, workspace=fws), steps, warmup, attn)
+    sp = dict(_LAST_SPREAD)
     flops = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
-    return {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d, "causal": w.causal,
-            "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
-            "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-            "roofline": roofline("fwd_prefill_bf16", w, kern["fwd_prefill_bf16"]),
+    dom = max(kern, key=kern.get)
+    peak = PEAK_F32_VALU_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    return {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
+            "causal": w.causal, "dtype": w.dtype, "ms": round(ms, 4), "spread": sp,
+            "tflops": round(flops / ms / 1e9, 2), "frac_of_peak": round(flops / ms / 1e9 / peak, 4),
+            "roofline": roofline(dom, w, kern[dom]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
+
+
+# the four multi-head d = 64 variants: non-causal, causal, ragged keys, ragged causal
+C2_VARIANTS = {"noncausal": "multihead_d64", "causal": "multihead_d64_causal",
+               "ragged": "multihead_d64_ragged", "ragged_causal": "multihead_d64_ragged_causal"}
+
+
+def bench_multihead_d64(attn, steps, warmup):
+    """The four d = 64 prefill variants and the causal/non-causal time ratios
+    (skipping the tiles above the diagonal should make causal about twice as
+    fast at the same shape)."""
+    import torch
+    out = {}
+    for key, name in C2_VARIANTS.items():
+        out[key] = bench_fwd(attn, steps, warmup, name)
+        torch.cuda.empty_cache()
+    out["noncausal_over_causal_time"] = round(out["noncausal"]["ms"] / out["causal"]["ms"], 3)
+    out["ragged_noncausal_over_causal_time"] = round(out["ragged"]["ms"] / out["ragged_causal"]["ms"], 3)
+    return out
 
 
 def bench_fp8(attn, steps, warmup):
@@ -237,6 +296,7 @@ def bench_fp8(attn, steps, warmup):
     lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
     ms, kern = _time(lambda: attn.fwd_fp8(q8, qs, k8, ks, vt8, vts, causal=w.causal, scale=w.scale, out=o,
                                           lse=lse), steps, warmup, attn)
+    sp = dict(_LAST_SPREAD)
 
     def quant():
         attn.mxfp8_quantize_rows(t["q"], codes=q8, scales=qs)
@@ -246,7 +306,7 @@ def bench_fp8(attn, steps, warmup):
     qms, qkern = _time(quant, max(3, steps // 4), 1, attn)
     flops = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
     return {"workload": w.name + "_mxfp8", "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d, "causal": w.causal,
-            "dtype": "e4m3 (MXFP8 operands), fp32 accumulation", "ms": round(ms, 4),
+            "dtype": "e4m3 (MXFP8 operands), fp32 accumulation", "ms": round(ms, 4), "spread": sp,
             "tflops": round(flops / ms / 1e9, 2),
             "frac_of_fp8_peak": round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
             "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -270,9 +330,10 @@ def bench_fp8_decode(attn, steps, warmup):
                      dtype=torch.uint8, device="cuda")
     ms, kern = _time(lambda: attn.fwd_fp8(*ops, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws),
                      steps, warmup, attn)
+    sp = dict(_LAST_SPREAD)
     alg = kernel_work("fwd_fp8_split", w)["bytes"] + w.B * w.Hq * w.Sq * (w.d * 2 + 4)
     return {"workload": w.name + "_mxfp8", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
-            "ms": round(ms, 4), "algorithmic_bytes": int(alg), "gbs": round(alg / ms / 1e6, 1),
+            "ms": round(ms, 4), "spread": sp, "algorithmic_bytes": int(alg), "gbs": round(alg / ms / 1e6, 1),
             "frac_of_peak": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
             "roofline": roofline("fwd_fp8_split", w.with_(name=w.name + "_mxfp8"), kern["fwd_fp8_split"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
@@ -289,10 +350,11 @@ def bench_decode(attn, steps, warmup):
                      dtype=torch.uint8, device="cuda")
     ms, kern = _time(lambda: attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o,
                                       lse=lse, workspace=ws), steps, warmup, attn)
+    sp = dict(_LAST_SPREAD)
     e = 2
     alg = 2 * w.B * w.Hkv * w.Sk * w.d * e + 2 * w.B * w.Hq * w.Sq * w.d * e + w.B * w.Hq * w.Sq * 4
     return {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
-            "ms": round(ms, 4), "algorithmic_bytes": alg, "gbs": round(alg / ms / 1e6, 1),
+            "ms": round(ms, 4), "spread": sp, "algorithmic_bytes": alg, "gbs": round(alg / ms / 1e6, 1),
             "frac_of_peak": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
             "roofline": roofline("fwd_split_bf16", w, kern["fwd_split_bf16"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
@@ -325,6 +387,7 @@ def bench_varlen(attn, steps, warmup):
                         dq=dq, dk=dk, dv=dv, workspace=ws)
 
     ms, kern = _time(step, steps, warmup, attn, per_step=True)
+    sp = dict(_LAST_SPREAD)
     total = sum(3.5 * nominal_fwd_flops(1, w.Hq, n, n, w.d, w.causal) for n in lens)
     # every kernel runs once per step (at most 64 sequences per launch), so its
     # time per step is its time per launch; the work is summed over sequences
@@ -337,7 +400,7 @@ def bench_varlen(attn, steps, warmup):
     ws_name = w.name
     return {"workload": w.name, "sequences": len(lens), "total_tokens": cq[-1], "min_len": min(lens),
             "max_len": max(lens), "H": w.Hq, "d": w.d, "causal": w.causal,
-            "step": "attn_fwd_varlen + attn_bwd_varlen", "ms": round(ms, 4),
+            "step": "attn_fwd_varlen + attn_bwd_varlen", "ms": round(ms, 4), "spread": sp,
             "tokens_per_s": round(cq[-1] / ms * 1e3, 1), "tflops": round(total / ms / 1e9, 2),
             "frac_of_peak": round(total / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
             "roofline": roofline(dom, synth.Workload(ws_name, 1, w.Hq, w.Hkv, 0, 0, w.d, w.dtype, w.causal, 0),
@@ -345,27 +408,79 @@ def bench_varlen(attn, steps, warmup):
             "kernels_ms_per_step": {k: round(v, 4) for k, v in kern.items()}}
 
 
+def host_description() -> dict:
+    """What the CPU baseline ran on: model, logical CPUs, the CPUs this process
+    may use, and the BLAS threads the oracle's matrix products use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = None
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity": affinity, "blas_threads": blas}
+
+
 def cpu_baseline(w, heads: int = 4) -> dict:
-    """The FP64 oracle as it stands, on a few heads of the training workload."""
+    """The FP64 oracle as it stands, on a bounded sample of each measured
+    workload: fwd + bwd on a few heads of the training workload (the headline
+    figure), the forward on one head of the long-context workload, and the
+    whole grouped-query decode."""
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    host = host_description()
     x = synth.make_inputs(w)
     f = {n: synth.to_f64(x[n][:, :heads], "bf16") for n in ("q", "k", "v", "do")}
+    del x
     t0 = time.perf_counter()
     oracle.attention_forward(f["q"], f["k"], f["v"], causal=w.causal, scale=w.scale)
     oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], causal=w.causal, scale=w.scale)
     dt = time.perf_counter() - t0
+    del f
     flops = 3.5 * nominal_fwd_flops(w.B, heads, w.Sq, w.Sk, w.d, w.causal)
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+    extra = {}
+    # long-context forward: one head (its x30 rows included)
+    lw = synth.get_workload("long_causal_d128")
+    x = synth.make_inputs(lw)
+    f = {n: synth.to_f64(x[n][:1, :1], "bf16") for n in ("q", "k", "v")}
+    del x
+    t1 = time.perf_counter()
+    oracle.attention_forward(f["q"], f["k"], f["v"], causal=lw.causal, scale=lw.scale)
+    dl = time.perf_counter() - t1
+    fl = nominal_fwd_flops(1, 1, lw.Sq, lw.Sk, lw.d, lw.causal)
+    extra["long_causal_d128_fwd"] = {"value": round(fl / dl / 1e12, 5), "unit": "TFLOP/s", "seconds": round(dl, 2),
+                                     "sample": "1 of 64 (batch, head) pairs, attention_forward"}
+    del f
+    # grouped-query decode: the whole workload
+    dw = synth.get_workload("gqa_decode")
+    x = synth.make_inputs(dw)
+    f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v")}
+    del x
+    t2 = time.perf_counter()
+    oracle.attention_forward(f["q"], f["k"], f["v"], causal=dw.causal, scale=dw.scale)
+    dd = time.perf_counter() - t2
+    alg = 2 * dw.B * dw.Hkv * dw.Sk * dw.d * 2 + 2 * dw.B * dw.Hq * dw.Sq * dw.d * 2 + dw.B * dw.Hq * dw.Sq * 4
+    extra["gqa_decode_fwd"] = {"value": round(alg / dd / 1e9, 3), "unit": "GB/s", "seconds": round(dd, 2),
+                               "sample": "the whole workload (bf16-equivalent bytes), attention_forward"}
+    del f
+    cores = host["blas_threads"] or host["affinity"] or os.cpu_count() or 1
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{heads} of {w.Hq} heads of {w.name} (S={w.Sq}, d={w.d}, causal), "
-                      "attention_forward + attention_backward in float64 NumPy"}
+                      "attention_forward + attention_backward in float64 NumPy",
+            "host": host, "other_workloads": extra}
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
@@ -431,6 +546,83 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch
         print(kern, out["hbm_bytes_per_launch"])
 
 
+def summarize_pmc(workload: str, title: str, dirs, command: str, out_md: str = None) -> str:
+    """Per-kernel shader counters from rocprofv3 --pmc runs (one directory per
+    pass, each pass within the hardware's counter limits), averaged over the
+    kernel's dispatches, with the figures derived from them:
+
+    * clock: GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 / dispatch duration;
+    * MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs; a
+      32x32x16 bf16 MFMA counts 32 cycles) / (GRBM_GUI_ACTIVE / 8 * 1024), the
+      MfmaUtil expression of rocprofiler's counter definitions;
+    * VALU busy: SQ_ACTIVE_INST_VALU / 256 CUs / (GRBM_GUI_ACTIVE / 8), its
+      VALUBusy expression;
+    * executed MFMA work: SQ_INSTS_VALU_MFMA_MOPS_BF16 (or _F8) x 512 FLOP;
+    * transcendental share: SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_VALU;
+    * LDS bank conflicts: SQ_LDS_BANK_CONFLICT cycles per CU cycle.
+
+    Writes profiles/pmc__<workload>.md (or out_md) and returns its path."""
+    per = {}         # short kernel name -> counter -> [values]
+    durs = {}
+    for d in dirs:
+        for r in _read_counter_csv(d):
+            k = _short_kernel_name(r.get("Kernel_Name", ""))
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            try:
+                durs.setdefault(k, {})[(d, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            except (KeyError, ValueError):
+                pass
+
+    def mean(k, c):
+        v = per.get(k, {}).get(c)
+        return sum(v) / len(v) if v else None
+
+    lines = [f"# rocprofv3 shader counters: {title}", "",
+             "Commands (run from the repository root on one MI355X; one counter pass per run):", "", "```",
+             command, "```", "",
+             "Values are per dispatch, averaged over the dispatches of each kernel. Derived: clock = "
+             "GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x "
+             "1024 SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / 8 x 256 CUs); executed MFMA "
+             "TFLOP = MOPS x 512; TRANS share = SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_VALU; LDS bank-conflict "
+             "cycles per CU cycle = SQ_LDS_BANK_CONFLICT / (GRBM_GUI_ACTIVE / 8 x 256).", ""]
+    names = sorted(per, key=lambda k: -(sum(durs.get(k, {}).values()) / max(1, len(durs.get(k, {})))))
+    for k in names:
+        c = per[k]
+        dv = list(durs.get(k, {}).values())
+        dur_us = sum(dv) / len(dv) / 1e3 if dv else None
+        lines += [f"## {k}", "", "| counter | mean per dispatch |", "|---|---|"]
+        for n in sorted(c):
+            lines.append(f"| {n} | {mean(k, n):.6g} |")
+        lines += ["", "| derived | value |", "|---|---|"]
+        if dur_us:
+            lines.append(f"| dispatch duration (us) | {dur_us:.1f} |")
+        gui = mean(k, "GRBM_GUI_ACTIVE")
+        if gui and dur_us:
+            lines.append(f"| clock (GHz) | {gui / N_XCD / (dur_us * 1e3):.3f} |")
+        if gui and mean(k, "SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            lines.append(f"| MFMA busy (%) | {100 * mean(k, 'SQ_VALU_MFMA_BUSY_CYCLES') / (gui / N_XCD * N_SIMD):.1f} |")
+        if gui and mean(k, "SQ_ACTIVE_INST_VALU") is not None:
+            lines.append(f"| VALU busy (%) | {100 * mean(k, 'SQ_ACTIVE_INST_VALU') / (gui / N_XCD * N_SIMD / 4):.1f} |")
+        for mops, label in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", "bf16"), ("SQ_INSTS_VALU_MFMA_MOPS_F8", "fp8")):
+            m = mean(k, mops)
+            if m is not None:
+                lines.append(f"| executed MFMA work, {label} (TFLOP) | {m * 512 / 1e12:.4f} |")
+                if dur_us:
+                    lines.append(f"| executed MFMA rate, {label} (TFLOP/s) | {m * 512 / (dur_us * 1e-6) / 1e12:.1f} |")
+        t, v = mean(k, "SQ_INSTS_VALU_TRANS_F32"), mean(k, "SQ_INSTS_VALU")
+        if t is not None and v:
+            lines.append(f"| TRANS share of VALU instructions (%) | {100 * t / v:.1f} |")
+        b = mean(k, "SQ_LDS_BANK_CONFLICT")
+        if b is not None and gui:
+            lines.append(f"| LDS bank-conflict cycles per CU cycle | {b / (gui / N_XCD * N_SIMD / 4):.4f} |")
+        lines.append("")
+    out_md = out_md or os.path.join(PROFILES, f"pmc__{workload}.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
+    return out_md
+
+
 def _demangle(name: str) -> str:
     if not name.startswith("_Z"):
         return name
@@ -485,8 +677,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen", "fp8", "fp8_decode"],
-                    default="all")
+    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen", "fp8", "fp8_decode", "f32",
+                                       "d64", "gqa_prefill"], default="all")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="WORKLOAD TITLE DIR [DIR ...]")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5,
                     metavar=("WORKLOAD", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -499,6 +693,11 @@ def main() -> int:
         return 0
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats, command=args.command)
+        return 0
+    if args.summarize_pmc:
+        if len(args.summarize_pmc) < 3:
+            ap.error("--summarize-pmc needs WORKLOAD TITLE DIR [DIR ...]")
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2:], command=args.command)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -517,9 +716,9 @@ def main() -> int:
               "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic"}
     if args.only in ("all", "step"):
-        w, ms, total, kern, dom = bench_step(attn, args.steps, args.warmup)
+        w, ms, total, kern, dom, sp = bench_step(attn, args.steps, args.warmup)
         print(f"# step: {ms:.3f} ms, kernels {kern}", file=sys.stderr, flush=True)
-        result.update({"value": round(total / ms / 1e9, 2), "ms_per_step": round(ms, 4),
+        result.update({"value": round(total / ms / 1e9, 2), "ms_per_step": round(ms, 4), "spread": sp,
                        "frac_of_peak": round(total / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.Sq, "d": w.d,
                                   "causal": w.causal, "step": "attn_fwd + attn_bwd",
@@ -530,6 +729,17 @@ def main() -> int:
     if args.only in ("all", "fwd"):
         result["fwd"] = bench_fwd(attn, args.steps, args.warmup)
         print(f"# fwd: {result['fwd']['ms']} ms", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if args.only in ("all", "f32"):
+        result["single_head_f32"] = bench_fwd(attn, max(args.steps, 20), args.warmup, "single_head_f32")
+        print(f"# single-head fp32: {result['single_head_f32']['ms']} ms", file=sys.stderr, flush=True)
+    if args.only in ("all", "d64"):
+        result["multihead_d64"] = bench_multihead_d64(attn, args.steps, args.warmup)
+        print("# multi-head d64: " + ", ".join(f"{k} {result['multihead_d64'][k]['ms']} ms" for k in C2_VARIANTS),
+              file=sys.stderr, flush=True)
+    if args.only in ("all", "gqa_prefill"):
+        result["gqa_prefill"] = bench_fwd(attn, args.steps, args.warmup, "gqa_prefill")
+        print(f"# gqa prefill: {result['gqa_prefill']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if args.only in ("all", "fp8"):
         result["fp8"] = bench_fp8(attn, args.steps, args.warmup)
@@ -559,16 +769,22 @@ def main() -> int:
     if args.only == "fp8":
         result.update({"value": result["fp8"]["tflops"], "ms_per_step": result["fp8"]["ms"], "dtype": "e4m3",
                        "config": {"workload": result["fp8"]["workload"]}, "roofline": result["fp8"]["roofline"]})
-    if args.only == "fwd":
-        result.update({"value": result["fwd"]["tflops"], "ms_per_step": result["fwd"]["ms"],
-                       "config": {"workload": result["fwd"]["workload"]}, "roofline": result["fwd"]["roofline"]})
+    for key, sub in (("fwd", "fwd"), ("f32", "single_head_f32"), ("gqa_prefill", "gqa_prefill")):
+        if args.only == key:
+            r = result[sub]
+            result.update({"value": r["tflops"], "ms_per_step": r["ms"], "spread": r["spread"],
+                           "dtype": r["dtype"], "config": {"workload": r["workload"]}, "roofline": r["roofline"]})
+    if args.only == "d64":
+        r = result["multihead_d64"]["causal"]
+        result.update({"value": r["tflops"], "ms_per_step": r["ms"], "spread": r["spread"],
+                       "config": {"workload": r["workload"]}, "roofline": r["roofline"]})
     if args.only == "decode":
         result.update({"value": result["decode"]["gbs"], "unit": "GB/s", "ms_per_step": result["decode"]["ms"],
                        "config": {"workload": result["decode"]["workload"]},
                        "roofline": result["decode"]["roofline"]})
     if not args.no_cpu_baseline and args.only in ("all", "step"):
         import synth
-        print("# cpu baseline (oracle, one head) ...", file=sys.stderr, flush=True)
+        print("# cpu baseline (oracle on sampled heads) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(synth.get_workload("train_causal_d128"))
     else:
         result["cpu_baseline"] = None

@@ -75,3 +75,36 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_spread_statistics():
+    s = bench.spread([1.0, 2.0, 3.0, 4.0, 100.0])
+    assert s["median_ms"] == 3.0 and s["min_ms"] == 1.0 and s["max_ms"] == 100.0 and s["n"] == 5
+    assert s["p10_ms"] == pytest.approx(1.4) and s["p90_ms"] == pytest.approx(61.6)
+
+
+def test_shader_counter_summary(tmp_path):
+    # two passes over the same kernel, as two rocprofv3 --pmc runs write them
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size","Kernel_Id",'
+           '"Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count","Accum_VGPR_Count",'
+           '"SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+    k = '"void attn::(anonymous namespace)::bwd_dkdv_kernel<128, true>(attn::(anonymous namespace)::BwdArgs)"'
+    a = tmp_path / "a"
+    b = tmp_path / "b"
+    a.mkdir()
+    b.mkdir()
+    # 1 ms dispatch; 8 XCDs x 2e6 cycles -> 2 GHz; MFMA busy half of 1024 SIMDs x 2e6 cycles
+    (a / "c_counter_collection.csv").write_text(
+        hdr + f'1,1,"A",1,1,1,1,1,{k},512,0,0,8,0,16,"GRBM_GUI_ACTIVE",16000000,0,1000000\n'
+        f'1,1,"A",1,1,1,1,1,{k},512,0,0,8,0,16,"SQ_VALU_MFMA_BUSY_CYCLES",1024000000,0,1000000\n')
+    (b / "c_counter_collection.csv").write_text(
+        hdr + f'1,1,"A",1,1,1,1,1,{k},512,0,0,8,0,16,"SQ_INSTS_VALU_TRANS_F32",25,0,1000000\n'
+        f'1,1,"A",1,1,1,1,1,{k},512,0,0,8,0,16,"SQ_INSTS_VALU",100,0,1000000\n'
+        f'1,1,"A",1,1,1,1,1,{k},512,0,0,8,0,16,"SQ_INSTS_VALU_MFMA_MOPS_BF16",2000000000,0,1000000\n')
+    out = bench.summarize_pmc("w", "title", [str(a), str(b)], "cmd", out_md=str(tmp_path / "p.md"))
+    text = open(out).read()
+    assert "## bwd_dkdv_kernel<128, true>" in text
+    assert "| clock (GHz) | 2.000 |" in text
+    assert "| MFMA busy (%) | 50.0 |" in text
+    assert "| TRANS share of VALU instructions (%) | 25.0 |" in text
+    assert "| executed MFMA work, bf16 (TFLOP) | 1.0240 |" in text
