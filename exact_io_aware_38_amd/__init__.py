@@ -18,10 +18,12 @@ __all__ = [
     "timing_start", "timing_stop", "fwd_varlen", "bwd_varlen", "fwd_varlen_workspace_bytes",
     "bwd_varlen_workspace_bytes", "fwd_dropout", "bwd_dropout", "dropout_mask",
     "fp8_padded_keys", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fwd_fp8", "fwd_fp8_workspace_bytes",
+    "fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20      # the library's static scratch per GPU (attn_fwd_noalloc)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn.so")
 _lib: Optional[ctypes.CDLL] = None
@@ -62,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_workspace_bytes.restype = _Z
         L.attn_fwd.argtypes = [_P, _P, _P, _P, _P] + _SHAPE + [_F, _I, _P, _Z, _P]
         L.attn_fwd.restype = _I
+        L.attn_fwd_noalloc.argtypes = [_P, _P, _P, _P, _P] + _SHAPE + [_F, _I, _P]
+        L.attn_fwd_noalloc.restype = _I
         L.attn_bwd.argtypes = [_P] * 9 + _SHAPE + [_F, _I, _P, _Z, _P]
         L.attn_bwd.restype = _I
         L.attn_fwd_varlen_workspace_bytes.argtypes = _VSHAPE + [_I]
@@ -214,6 +218,29 @@ def fwd(q, k, v, *, causal: int = 0, scale: Optional[float] = None, out=None, ls
                         causal, sc, dt, _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def fwd_noalloc(q, k, v, out, lse=None, *, causal: int = 0, scale: Optional[float] = None, stream=None):
+    """attn_fwd_noalloc: the forward into caller-given ``out`` (and ``lse``, or
+    None) with the library's static scratch instead of a workspace; the
+    library allocates nothing. Calls that overlap on one GPU race on that
+    scratch."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse")):
+        _check(t, n)
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    dt = _dtype_code(q)
+    _want(k, (B, Hkv, Sk, d), q.dtype, "k")
+    _want(v, (B, Hkv, Sk, d), q.dtype, "v")
+    _want(out, q.shape, q.dtype, "out")
+    _want(lse, (B, Hq, Sq), torch.float32, "lse")
+    sc = float(scale) if scale is not None else 1.0 / float(d) ** 0.5
+    st = lib().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, causal,
+                                sc, dt, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_noalloc")
     return out, lse
 
 

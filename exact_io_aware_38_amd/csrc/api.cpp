@@ -281,6 +281,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_DROPOUT: return "dropout probability must lie in [0, 1) and round below 256/256";
     case ATTN_ERR_ALIGN: return "misaligned pointer: tensors and workspace need 16 bytes, lse and scales 4";
+    case ATTN_ERR_SCRATCH: return "problem needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -312,6 +313,27 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (fwd_launch(p, dtype, q, k, v, o, lse, workspace, (hipStream_t)stream, text, sizeof(text)) != hipSuccess)
     return ATTN_ERR_HIP;
   std::snprintf(line, sizeof(line), "attn_fwd: %s", text);
+  record(line);
+  return ATTN_OK;
+}
+
+static_assert(attn::NOALLOC_SCRATCH_BYTES == ATTN_NOALLOC_SCRATCH_BYTES, "one scratch size");
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int d, int causal, float scale, int dtype, void* stream) {
+  if (q == nullptr || o == nullptr || (Sk != 0 && (k == nullptr || v == nullptr))) return ATTN_ERR_NULL;
+  const int st = check_common(B, Hq, Hkv, Sq, Sk, d, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (any16(q, k, v, o) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
+  const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
+  const size_t need = fwd_ws(p, dtype);
+  if (need > attn::NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (need > 0 && attn::noalloc_scratch(&scratch) != hipSuccess) return ATTN_ERR_HIP;
+  char text[440], line[512];
+  if (fwd_launch(p, dtype, q, k, v, o, lse, scratch, (hipStream_t)stream, text, sizeof(text)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  std::snprintf(line, sizeof(line), "attn_fwd_noalloc%s: %s", need > 0 ? " (static scratch)" : "", text);
   record(line);
   return ATTN_OK;
 }

@@ -34,9 +34,40 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <type_traits>
 
+// Scratch of attn_fwd_noalloc: the split path's per-slice partials for
+// callers that cannot allocate device memory. Every GPU the library runs on
+// holds its own copy of this array until the process ends; host code never
+// passes the array's name to a kernel (in host code it is only a handle), but
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[attn::NOALLOC_SCRATCH_BYTES];
+
 namespace attn {
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -126,6 +126,12 @@ SplitPlan plan_split(const Problem& p);
 hipError_t launch_fwd_split_bf16(const Problem& p, const SplitPlan& plan, const void* q,
                                  const void* k, const void* v, void* o, float* lse,
                                  void* ws, hipStream_t s);
+// Fixed scratch for callers that cannot allocate (attn_fwd_noalloc): a
+// static device array of this many bytes per GPU, holding the split path's
+// partials. noalloc_scratch() returns its address on the current device,
+// looked up once per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
 // The merge of a split launch's per-slice partials (in the workspace laid out
 // by plan_split) into o (bf16) and lse.
 hipError_t launch_combine_split(const Problem& p, const SplitPlan& plan, void* ws, void* o, float* lse,

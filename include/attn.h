@@ -75,7 +75,8 @@ enum attn_status {
   ATTN_ERR_HIP = -8,        /* a HIP runtime call or kernel launch failed */
   ATTN_ERR_SCALE = -9,      /* scale not finite or not > 0 */
   ATTN_ERR_DROPOUT = -10,   /* dropout probability not in [0, 1) or rounding to 1 */
-  ATTN_ERR_ALIGN = -11      /* a data pointer lacks the alignment stated above */
+  ATTN_ERR_ALIGN = -11,     /* a data pointer lacks the alignment stated above */
+  ATTN_ERR_SCRATCH = -12    /* attn_fwd_noalloc: more scratch needed than its static buffer holds */
 };
 
 enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
@@ -94,6 +95,25 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and dispatch as attn_fwd, minus the workspace: the
+ * split-key decode path keeps its per-slice partials in a static device array
+ * of the library (ATTN_NOALLOC_SCRATCH_BYTES = 16 MiB per GPU, held until the
+ * process ends) instead of a caller's workspace; the prefill and fp32 paths
+ * need none. No call here allocates or frees device memory. A problem whose
+ * partials need more than the array holds (attn_fwd_workspace_bytes above
+ * 16 MiB, e.g. decode with B * Hq * Sq * nsplit past about 32K rows at
+ * d = 128) returns ATTN_ERR_SCRATCH before anything is launched. Every call
+ * on one GPU uses that GPU's one array, and every partial a call reads was
+ * written by that call, so nothing needs clearing between calls; but calls
+ * that overlap on one GPU (concurrent streams or threads) race on it: run them
+ * in order on one stream. The caller's current device must be the stream's. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+                     int dtype, void* stream);
 
 /* Bytes of device workspace attn_bwd needs: the per-row terms D_i = dO_i . O_i
  * and lse_i * log2(e) (float32, 2 * B * Hq * Sq' values with Sq' = Sq rounded

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     codes = {0: "success", -1: "NULL", -2: "shape", -3: "multiple", -4: "head dim", -5: "dtype",
-             -6: "causal", -7: "workspace", -8: "HIP", -9: "scale", -10: "dropout", -11: "misaligned"}
+             -6: "causal", -7: "workspace", -8: "HIP", -9: "scale", -10: "dropout", -11: "misaligned", -12: "scratch"}
     for c, word in codes.items():
         assert word.lower() in attn.strerror(c).lower()
     assert "unknown" in attn.strerror(-99)
@@ -336,3 +336,30 @@ def test_binding_checks_alignment_before_calling():
         attn._check(_FakeTensor(ODD16), "q")
     with pytest.raises(ValueError, match="4-byte"):
         attn._check(_FakeTensor(ODD4), "lse")
+
+
+# ---------------------------------------------------------------- forward on the static scratch
+def _fwd_noalloc(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=16, Sk=16, d=64,
+             causal=0, scale=0.125, dtype=attn.ATTN_BF16, stream=None)
+    a.update(over)
+    return attn.lib().attn_fwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                       a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, -1), ({"k": None}, -1), ({"B": 0}, -2), ({"Hq": 6, "Hkv": 4}, -3), ({"d": 96}, -4),
+    ({"dtype": 7}, -5), ({"causal": 3}, -6), ({"scale": 0.0}, -9), ({"o": FAKE + 8}, -11),
+    # decode whose split partials exceed the 16 MiB static scratch (checked before any HIP call)
+    ({"B": 1024, "Hq": 32, "Hkv": 8, "Sq": 1, "Sk": 4096, "d": 128}, -12),
+])
+def test_fwd_noalloc_validation(over, code):
+    assert _fwd_noalloc(**over) == code
+
+
+def test_noalloc_scratch_limit_matches_the_workspace_query():
+    # the limit is the same 16 MiB the header states; the training-size decode fits
+    assert attn.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert 0 < attn.fwd_workspace_bytes(16, 32, 8, 1, 32768, 128, 0, attn.ATTN_BF16) <= attn.NOALLOC_SCRATCH_BYTES
+    big = attn.fwd_workspace_bytes(1024, 32, 8, 1, 4096, 128, 0, attn.ATTN_BF16)
+    assert big > attn.NOALLOC_SCRATCH_BYTES
