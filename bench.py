@@ -605,7 +605,7 @@ def summarize_pmc(workload: str, title: str, dirs, command: str, out_md: str = N
             lines.append(f"| VALU busy (%) | {100 * mean(k, 'SQ_ACTIVE_INST_VALU') / (gui / N_XCD * N_SIMD / 4):.1f} |")
         for mops, label in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", "bf16"), ("SQ_INSTS_VALU_MFMA_MOPS_F8", "fp8")):
             m = mean(k, mops)
-            if m is not None:
+            if m:
                 lines.append(f"| executed MFMA work, {label} (TFLOP) | {m * 512 / 1e12:.4f} |")
                 if dur_us:
                     lines.append(f"| executed MFMA rate, {label} (TFLOP/s) | {m * 512 / (dur_us * 1e-6) / 1e12:.1f} |")
