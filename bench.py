@@ -59,6 +59,8 @@ KERNEL_SOURCES = {
     "fwd_prefill_bf16": ["fwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
     "fwd_split_bf16": ["fwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
     "bwd_dkdv": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
+    "bwd_dkdvq": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
+    "dq_convert": ["bwd_bf16.hip", "common.h", "kernels.h"],
     "bwd_dq": ["bwd_bf16.hip", "common.h", "kernels.h", "tiles.h"],
     "bwd_pre": ["bwd_bf16.hip", "common.h", "kernels.h"],
     "fwd_fp8": ["fwd_fp8.hip", "common.h", "kernels.h", "tiles.h"],
@@ -66,18 +68,30 @@ KERNEL_SOURCES = {
     "fwd_f32": ["fwd_f32.hip", "common.h", "kernels.h"],
 }
 # substrings of the (demangled) device kernel names, as rocprofv3 reports them
-# (the dense and the packed instantiations both match; a workload uses one)
+# (the dense and the packed instantiations both match; a workload uses one).
+# The dK/dV kernel's last template argument tells the fused form (dQ added
+# atomically, "bwd_dkdvq") from the two-pass one.
 KERNEL_SYMBOLS = {
     "fwd_prefill_bf16": "fwd_prefill_kernel<128,",
     "fwd_split_bf16": "fwd_split_kernel<128>",
     "bwd_dkdv": "bwd_dkdv_kernel<128,",
+    "bwd_dkdvq": "bwd_dkdv_kernel<128,",
     "bwd_dq": "bwd_dq_kernel<128,",
     "bwd_pre": "bwd_pre_kernel<128,",
+    "dq_convert": "dq_convert_kernel<128>",
     "fwd_fp8": "fwd_fp8_kernel<128>",
     "fwd_fp8_split": "fwd_fp8_split_kernel<128>",
 }
-# the same for the d = 64 instantiations (multi-head d = 64 workloads)
-KERNEL_SYMBOLS_D64 = {k: v.replace("<128", "<64") for k, v in KERNEL_SYMBOLS.items()}
+
+
+def kernel_matches(kernel: str, name: str) -> bool:
+    """Whether a demangled rocprofv3 kernel name is an instance of `kernel`."""
+    name = _short_kernel_name(name)
+    if KERNEL_SYMBOLS[kernel] not in name:
+        return False
+    if kernel in ("bwd_dkdv", "bwd_dkdvq"):
+        return name.replace(" ", "").endswith("true>") == (kernel == "bwd_dkdvq")
+    return True
 
 
 def source_hash(kernel: str) -> str:
@@ -93,14 +107,16 @@ def nominal_fwd_flops(B, Hq, Sq, Sk, d, causal) -> float:
     return f / 2 if causal else f
 
 
-def kernel_work(kernel: str, w) -> dict:
+def kernel_work(kernel: str, w, fused: bool = False) -> dict:
     """Algorithmic work one launch of `kernel` does on workload w.
 
     Forward: 4*d FLOP per visible (query, key) pair, causal counted as half of
     the pairs. Backward: 10*d per pair over five GEMMs (S recompute, dV, dP, dK,
-    dQ); the dK/dV kernel does four of them (8*d), the dQ kernel is credited
-    only with dQ (2*d) since its S and dP are a second recomputation. Decode
-    and the preprocess pass are bound by bytes: each tensor crosses HBM once.
+    dQ); the fused dK/dV/dQ kernel does all five, the two-pass form's dK/dV
+    kernel four of them (8*d) and its dQ kernel is credited only with dQ (2*d)
+    since its S and dP are a second recomputation. Decode, the preprocess pass
+    (which on the fused path also clears the float32 dQ sums) and the dQ
+    conversion are bound by bytes: each tensor crosses HBM once.
     """
     fwd = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
     e = 2  # bf16 bytes
@@ -112,11 +128,16 @@ def kernel_work(kernel: str, w) -> dict:
         return {"bound": "mfma", "flops": fwd, "peak": PEAK_FP8_TFLOPS}
     if kernel == "bwd_dkdv":
         return {"bound": "mfma", "flops": 2.0 * fwd}
+    if kernel == "bwd_dkdvq":
+        return {"bound": "mfma", "flops": 2.5 * fwd}
+    if kernel == "dq_convert":
+        rows = w.B * w.Hq * w.Sq
+        return {"bound": "hbm", "bytes": rows * w.d * (4.0 + e)}
     if kernel == "bwd_dq":
         return {"bound": "mfma", "flops": 0.5 * fwd}
     if kernel == "bwd_pre":
         rows = w.B * w.Hq * w.Sq
-        return {"bound": "hbm", "bytes": 2.0 * rows * w.d * e + 3.0 * rows * 4}
+        return {"bound": "hbm", "bytes": 2.0 * rows * w.d * e + 3.0 * rows * 4 + (rows * w.d * 4.0 if fused else 0)}
     if kernel == "fwd_split_bf16":
         kv = 2.0 * w.B * w.Hkv * w.Sk * w.d * e
         return {"bound": "hbm", "bytes": kv + w.B * w.Hq * w.Sq * w.d * e}
@@ -216,7 +237,7 @@ def _time(fn, steps: int, warmup: int, attn, per_step: bool = False):
     return ms, {k: v[1] / v[0] for k, v in kern.items()}
 
 
-def bench_step(attn, steps, warmup):
+def bench_step(attn, steps, warmup, fused: bool = False):
     import torch
     import synth
     w = synth.get_workload("train_causal_d128")
@@ -224,14 +245,15 @@ def bench_step(attn, steps, warmup):
     o = torch.empty_like(t["q"])
     lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
-    ws = torch.empty(max(1, attn.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal,
-                                                     attn.ATTN_BF16)), dtype=torch.uint8, device="cuda")
+    wsq = attn.bwd_fused_workspace_bytes if fused else attn.bwd_workspace_bytes
+    ws = torch.empty(max(1, wsq(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, attn.ATTN_BF16)), dtype=torch.uint8,
+                     device="cuda")
     fws = _fwd_workspace(attn, w)
 
     def step():
         attn.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=fws)
         attn.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal, scale=w.scale,
-                 dq=dq, dk=dk, dv=dv, workspace=ws)
+                 dq=dq, dk=dk, dv=dv, workspace=ws, fused=fused)
 
     ms, kern = _time(step, steps, warmup, attn)
     fwd = nominal_fwd_flops(w.B, w.Hq, w.Sq, w.Sk, w.d, w.causal)
@@ -528,9 +550,9 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch
     write = per_kernel(_read_counter_csv(write_dir), "WRITE_SIZE")
     ff, fcopy = copy_factor(_read_counter_csv(copy_fetch_dir), "FETCH_SIZE")
     wf, wcopy = copy_factor(_read_counter_csv(copy_write_dir), "WRITE_SIZE")
-    for kern, sym in KERNEL_SYMBOLS.items():
-        fk = [v for k, vs in fetch.items() if sym in k for v in vs]
-        wk = [v for k, vs in write.items() if sym in k for v in vs]
+    for kern in KERNEL_SYMBOLS:
+        fk = [v for k, vs in fetch.items() if kernel_matches(kern, k) for v in vs]
+        wk = [v for k, vs in write.items() if kernel_matches(kern, k) for v in vs]
         if not fk or not wk or ff is None or wf is None:
             continue
         f_kib = sorted(fk)[len(fk) // 2]
@@ -677,7 +699,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "fwd", "decode", "varlen", "fp8", "fp8_decode", "f32",
+    ap.add_argument("--only", choices=["all", "step", "step_fused", "fwd", "decode", "varlen", "fp8", "fp8_decode", "f32",
                                        "d64", "gqa_prefill"], default="all")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
                     help="WORKLOAD TITLE DIR [DIR ...]")
@@ -725,6 +747,15 @@ def main() -> int:
                                   "nominal_tflop_per_step": round(total / 1e12, 4)},
                        "roofline": roofline(dom, w, kern[dom]),
                        "kernels_ms": {k: round(v, 4) for k, v in kern.items()}})
+        torch.cuda.empty_cache()
+    if args.only in ("all", "step_fused"):
+        # the single-pass backward with atomically summed dQ on the same step, for comparison
+        w2, ms2, total2, kern2, dom2, sp2 = bench_step(attn, max(3, args.steps // 4), 2, fused=True)
+        result["step_fused"] = {
+            "step": "attn_fwd + attn_bwd_fused", "ms": round(ms2, 4), "spread": sp2,
+            "tflops": round(total2 / ms2 / 1e9, 2), "frac_of_peak": round(total2 / ms2 / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline(dom2, w2, kern2[dom2]), "kernels_ms": {k: round(v, 4) for k, v in kern2.items()}}
+        print(f"# step, fused backward: {ms2:.3f} ms, kernels {kern2}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if args.only in ("all", "fwd"):
         result["fwd"] = bench_fwd(attn, args.steps, args.warmup)

@@ -18,7 +18,7 @@ __all__ = [
     "timing_start", "timing_stop", "fwd_varlen", "bwd_varlen", "fwd_varlen_workspace_bytes",
     "bwd_varlen_workspace_bytes", "fwd_dropout", "bwd_dropout", "dropout_mask",
     "fp8_padded_keys", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fwd_fp8", "fwd_fp8_workspace_bytes",
-    "fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "bwd_fused_workspace_bytes",
 ]
 
 ATTN_F32 = 0
@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_noalloc.restype = _I
         L.attn_bwd.argtypes = [_P] * 9 + _SHAPE + [_F, _I, _P, _Z, _P]
         L.attn_bwd.restype = _I
+        L.attn_bwd_fused.argtypes = [_P] * 9 + _SHAPE + [_F, _I, _P, _Z, _P]
+        L.attn_bwd_fused.restype = _I
+        L.attn_bwd_fused_workspace_bytes.argtypes = _SHAPE + [_I]
+        L.attn_bwd_fused_workspace_bytes.restype = _Z
         L.attn_fwd_varlen_workspace_bytes.argtypes = _VSHAPE + [_I]
         L.attn_fwd_varlen_workspace_bytes.restype = _Z
         L.attn_bwd_varlen_workspace_bytes.argtypes = _VSHAPE + [_I]
@@ -141,6 +145,10 @@ def fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype) -> int:
 
 def bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype))
+
+
+def bwd_fused_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype) -> int:
+    return int(lib().attn_bwd_fused_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dtype))
 
 
 def _dtype_code(t) -> int:
@@ -245,8 +253,12 @@ def fwd_noalloc(q, k, v, out, lse=None, *, causal: int = 0, scale: Optional[floa
 
 
 def bwd(q, k, v, o, lse, dout, *, causal: int = 0, scale: Optional[float] = None, dq=None, dk=None,
-        dv=None, workspace=None, stream=None):
-    """(dq, dk, dv) for the forward that produced o and lse (bf16 only)."""
+        dv=None, workspace=None, stream=None, fused: bool = False):
+    """(dq, dk, dv) for the forward that produced o and lse (bf16 only).
+
+    The default is the two-pass backward (attn_bwd), the same bits on every
+    run; ``fused=True`` runs the single pass with atomically accumulated dQ
+    (attn_bwd_fused), slower on MI355X and kept for comparison."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout"),
                  (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace")):
@@ -263,15 +275,15 @@ def bwd(q, k, v, o, lse, dout, *, causal: int = 0, scale: Optional[float] = None
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    ws_n = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, causal, dt)
+    ws_n = (bwd_fused_workspace_bytes if fused else bwd_workspace_bytes)(B, Hq, Hkv, Sq, Sk, d, causal, dt)
     if workspace is None and ws_n > 0:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                        _ptr(dv), B, Hq, Hkv, Sq, Sk, d, causal, sc, dt, _ptr(workspace), ws_bytes,
-                        _stream(stream))
+    fn = lib().attn_bwd_fused if fused else lib().attn_bwd
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), B, Hq, Hkv, Sq, Sk, d, causal, sc, dt, _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_fused" if fused else "attn_bwd")
     return dq, dk, dv
 
 

@@ -344,9 +344,12 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d, i
   return attn::bwd_workspace_bytes(make_problem(B, Hq, Hkv, Sq, Sk, d, causal, 1.f));
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
-             float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// attn_bwd and attn_bwd_fused: the two-kernel pass or the single pass with
+// atomically accumulated dQ.
+int bwd_entry(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+              int dtype, void* workspace, size_t workspace_bytes, void* stream, bool fused) {
   // k, v, dk and dv are neither read nor written when there is no key
   if (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr ||
       (Sk != 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
@@ -356,14 +359,35 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (any16(q, k, v, o, dout, dq, dk, dv, workspace) || misaligned(lse, 4)) return ATTN_ERR_ALIGN;
   const attn::Problem p = make_problem(B, Hq, Hkv, Sq, Sk, d, causal, scale);
-  const size_t need = attn::bwd_workspace_bytes(p);
+  const size_t need = fused ? attn::bwd_fused_workspace_bytes(p) : attn::bwd_workspace_bytes(p);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   char text[512];
-  const hipError_t e = attn::launch_bwd_bf16(p, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+  const hipError_t e = attn::launch_bwd_bf16(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, fused,
                                              (hipStream_t)stream, text, sizeof(text));
   if (e != hipSuccess) return ATTN_ERR_HIP;
   record(text);
   return ATTN_OK;
+}
+}  // namespace
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+             float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale, dtype, workspace,
+                   workspace_bytes, stream, false);
+}
+
+size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int dtype) {
+  if (check_common(B, Hq, Hkv, Sq, Sk, d, causal, 1.f, dtype) != ATTN_OK) return 0;
+  if (dtype != ATTN_BF16) return 0;
+  return attn::bwd_fused_workspace_bytes(make_problem(B, Hq, Hkv, Sq, Sk, d, causal, 1.f));
+}
+
+int attn_bwd_fused(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+                   float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale, dtype, workspace,
+                   workspace_bytes, stream, true);
 }
 
 size_t attn_fwd_varlen_workspace_bytes(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
@@ -515,7 +539,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
   const size_t need = attn::bwd_workspace_bytes(p);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   char text[448], line[512];
-  if (attn::launch_bwd_bf16(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, (hipStream_t)stream, text,
+  if (attn::launch_bwd_bf16(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, false, (hipStream_t)stream, text,
                             sizeof(text)) != hipSuccess)
     return ATTN_ERR_HIP;
   std::snprintf(line, sizeof(line), "attn_bwd_dropout (keep when byte >= %u of 256): %s", p.drop.thr, text);

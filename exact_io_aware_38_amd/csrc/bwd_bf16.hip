@@ -21,6 +21,17 @@
 // The dK/dV and dQ passes both rebuild S and dP, which costs two GEMMs more
 // than a single pass with atomic dQ but keeps the result deterministic.
 //
+// Fused path (attn_bwd_fused): the dK/dV pass also forms dQ = dS K for its
+// 128 keys and adds it into a float32 workspace with vector atomic adds, so S
+// and dP are rebuilt once; bwd_pre clears the workspace first and dq_convert
+// scales and rounds it into dq afterwards. The order in which workgroups add
+// into a dQ row varies from run to run, so the float32 sums (and at times the
+// bf16 result) do too. On this chip it is the slower form: every (128-key
+// tile, query row) pair costs d float32 atomic adds, about 1.1e9 for the
+// 8K-token training shape, and float32 atomic adds retire at roughly 3.4e11
+// per second chip-wide (a tenth of the rate of plain stores of the same
+// pattern), which alone takes longer than the whole two-kernel backward.
+//
 // Mapping to CDNA4: in the dK/dV pass the two wavefronts that share a SIMD
 // split each tile's work (scores and elementwise terms on one, the gradient
 // products on the other), so one's vector work runs under the other's MFMAs.
@@ -81,6 +92,7 @@ struct BwdArgs {
   bf16* dk;
   bf16* dv;
   float* ld;      // [B, Hq, sqp / 32][64]: lse2 of 32 rows, then D of the same rows
+  float* dqacc;   // fused path: [B, Hq, sqp, D] float32 sums of dS K (NULL on the two-kernel path)
   int B, Hq, Hkv, Sq, Sk, g, causal;
   int hsq, hsk;   // head strides in rows (see Problem)
   int sqp;        // Sq rounded up to 64
@@ -162,6 +174,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
   }
 #pragma unroll
   for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
+  if (a.dqacc != nullptr && prow < rows) {
+    // fused path: clear this row's dQ sums (padding rows too; nothing reads them)
+    float* z = a.dqacc + prow * D + c * 8;
+    *(f32x4*)z = f32x4{0.f, 0.f, 0.f, 0.f};
+    *(f32x4*)(z + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (prow < rows && c == 0) {
     float l2 = __builtin_huge_valf(), dl = 0.f;
     if (valid) {
@@ -197,7 +215,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
 // ---------------------------------------------------------------------------
 // DROP (here and in the dQ kernel): dropout with the forward's mask, so that
 // dV takes P Z and dS = P (Z dP - D), Z = keep / (1 - p).
-template <int D, bool CAUSAL, typename Tab, bool DROP>
+// FUSED: the gradient wavefronts also form dQ = dS K of each query tile over
+// the workgroup's 128 keys and add it into a.dqacc. Wavefront w takes the
+// 32-channel block w mod (D/32) of dQ and the key chunks 8 (D/32) / 4 of its
+// share (all 128 keys at D = 128, half of them at D = 64): its B operand (K
+// for 16 keys x 32 channels per MFMA) is loaded into registers once, its A
+// operand (dS, 32 queries x 16 keys) is read transposed from the exchange
+// buffer of all four key blocks. The 16 sums per lane are added with vector
+// atomics after the step's MFMAs; the barrier's wait leaves them in flight
+// (vector memory operations complete in issue order, so waiting until at most
+// that many are outstanding covers the tile DMA issued before them).
+template <int D, bool CAUSAL, typename Tab, bool DROP, bool FUSED>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
   constexpr int DC = D / 16;
   constexpr int MB = D / 32;
@@ -251,7 +279,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
   // the last one down to the first one that sees a key of this workgroup.
   // Walking down keeps every workgroup of a head on the same tile at the same
   // time (they all start at the last tile), so each tile is fetched into L2
-  // once and then served to all of them.
+  // once and then served to all of them. (On the fused path this also has the
+  // workgroups of a head add into the same dQ rows at about the same time; a
+  // walk rotated per key tile was measured no faster, since the atomic adds
+  // are bound by their chip-wide rate, not by contention.)
   auto advance = [&](int& hq, int& q0) __attribute__((always_inline)) {
     q0 -= BT;
     if (q0 < qt_lo * BT) {
@@ -263,11 +294,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
   // have landed for every wavefront (the gradient wavefronts wait for all
   // their DMA, the barrier makes it visible to all), the exchange slot of
   // tile j - 1 is complete, and every wavefront is done with step j - 1.
+  constexpr int NATOM = 16;                     // fused path: atomic adds per gradient wavefront and step
+  bool atoms_out = false;                       // some are in flight (gradient wavefronts)
   auto sync = [&]() __attribute__((always_inline)) {
-    if (grad)
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    else
+    if (grad) {
+      if (FUSED && atoms_out)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NATOM) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -494,6 +531,37 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
   }
   const uint32_t xr = X_OFF + kb * XB + lane * 16;
 
+  // Fused dQ. Channel block dblk = kb mod MB, key chunks kc0 .. kc0 + NKC - 1
+  // (16 keys each, chunk kc in key block kc / 2). B operand: lane l holds
+  // channel 32 dblk + (l mod 32) and keys 16 kc + 8 (l / 32) + 0..7, loaded once.
+  // A operand (dS, rows = the tile's 32 queries): two transposing 4-key reads
+  // per MFMA from the exchange entries the score wavefronts wrote, where the
+  // lane of key kk (and half h) holds queries 4 c .. 4 c + 3 for chunk
+  // c = 2 (v / 4) + h of its registers v; within a 16-lane group lane L reads
+  // key kk0 + L / 4 at query chunk c = 4 (group & 1) + (L & 3), so that output
+  // lane j holds query 16 (group & 1) + j.
+  constexpr int NKC = 2 * MB;                   // key chunks per wavefront
+  const int dblk = kb % MB;
+  const int kc0 = (kb / MB) * NKC;
+  bf16x8 ktf[FUSED ? NKC : 1];
+  uint32_t xq = 0;
+  if constexpr (FUSED) {
+    const bf16* kcol = a.k + ((size_t)b * a.Hkv + hkv) * a.hsk * D + 32 * dblk + l32;
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = k0 + 16 * (kc0 + i) + 8 * hi + e;
+        ktf[i][e] = kk < a.Sk ? kcol[(size_t)kk * D] : (bf16)0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) ktf[i] = settle(ktf[i]);
+    const int L = lane & 15, c = 4 * ((lane >> 4) & 1) + (L & 3);
+    xq = X_OFF + 2048 + (8 * hi + (L >> 2)) * 16 + 512 * (c & 1) + 1024 * (c >> 2) + 8 * ((c >> 1) & 1);
+  }
+  int ghq = hkv * a.g, gq0 = (n_qt - 1) * BT;   // query tile whose gradients the step forms
+
   f32x16 dkt[MB], dvt[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -518,13 +586,27 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
       dsf[0] = *(const bf16x8*)(xs + 2 * 1024);
       dsf[1] = *(const bf16x8*)(xs + 3 * 1024);
       const char* tile = lds + SG * SLOT;
-      // op k: chain k % 2MB (dV^T for < MB, dK^T above), query chunk k / 2MB
-      auto frag = [&](int k) __attribute__((always_inline)) {
-        const int ch = k % (2 * MB), qc = k / (2 * MB);
+      // gradient op g: chain g % 2MB (dV^T for < MB, dK^T above), query chunk g / 2MB
+      auto gfrag = [&](int g) __attribute__((always_inline)) {
+        const int ch = g % (2 * MB), qc = g / (2 * MB);
         const char* t = tile + (ch < MB ? TB : 0) + qc * 16 * RB;
         return cat4(lds_read_tr((const bf16*)(t + vb[ch % MB][0])), lds_read_tr((const bf16*)(t + vb[ch % MB][1])));
       };
-      constexpr int NOPS = 4 * MB;
+      // fused dQ op i: key chunk kc0 + i of the exchange slot of tile j - 1
+      const char* xs_q = lds + xq + ((POS + 1) & 1) * XSLOT;
+      auto qfrag = [&](int i) __attribute__((always_inline)) {
+        const int kc = kc0 + i;
+        const char* t = xs_q + (kc >> 1) * XB + (kc & 1) * 256;
+        return cat4(lds_read_tr((const bf16*)t), lds_read_tr((const bf16*)(t + 64)));
+      };
+      constexpr int NG = 4 * MB;                  // dV^T and dK^T MFMAs
+      constexpr int NQ = FUSED ? NKC : 0;         // dQ MFMAs, one after every two gradient ones
+      constexpr int NOPS = NG + NQ;
+      // op k -> (is a dQ op, index within its kind)
+      auto is_q = [](int k) constexpr { return FUSED && k % 3 == 2; };
+      auto idx = [](int k) constexpr { return FUSED ? (k % 3 == 2 ? k / 3 : k - (k + 1) / 3) : k; };
+      auto frag = [&](int k) __attribute__((always_inline)) { return is_q(k) ? qfrag(idx(k)) : gfrag(idx(k)); };
+      f32x16 dqa;
       bf16x8 f[3];
       f[0] = frag(0);
       f[1] = frag(1);
@@ -532,12 +614,28 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k + 2 < NOPS) f[(k + 2) % 3] = frag(k + 2);
         __builtin_amdgcn_sched_barrier(0);      // keep the reads two MFMAs ahead of their use
-        constexpr int ch = k % (2 * MB), qc = k / (2 * MB);
-        if constexpr (ch < MB)
-          dvt[ch] = mfma32(f[k % 3], pf[qc], dvt[ch]);
-        else
-          dkt[ch - MB] = mfma32(f[k % 3], dsf[qc], dkt[ch - MB]);
+        constexpr int g = idx(k);
+        if constexpr (is_q(k)) {
+          dqa = mfma32(f[k % 3], ktf[g], g == 0 ? f32x16{} : dqa);
+        } else {
+          constexpr int ch = g % (2 * MB), qc = g / (2 * MB);
+          if constexpr (ch < MB)
+            dvt[ch] = mfma32(f[k % 3], pf[qc], dvt[ch]);
+          else
+            dkt[ch - MB] = mfma32(f[k % 3], dsf[qc], dkt[ch - MB]);
+        }
       });
+      if constexpr (FUSED) {
+        static_assert(NQ > 0 && NOPS % 3 == 0, "every third op is a dQ op");
+        // accumulator register i: query gq0 + 8 (i / 4) + 4 hi + (i % 4), channel 32 dblk + l32
+        float* dst = a.dqacc + ((size_t)(b * a.Hq + ghq) * a.sqp + gq0 + 4 * hi) * D + 32 * dblk + l32;
+#pragma unroll
+        for (int i = 0; i < NATOM; ++i)
+          __hip_atomic_fetch_add(dst + (8 * (i >> 2) + (i & 3)) * D, dqa[i], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        atoms_out = true;
+        advance(ghq, gq0);
+      }
     }
   };
   if (n > 0) {
@@ -944,8 +1042,26 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
   }
 }
 
+// dq = bf16(scale * dqacc) for the rows of the problem (fused path): one thread
+// per 8 channels of a row.
+template <int D>
+__global__ __launch_bounds__(256) void dq_convert_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = t / LPR;                   // (b Hq + h) Sq + i
+  const int c = (int)(t % LPR);
+  if (row >= (size_t)a.B * a.Hq * a.Sq) return;
+  const size_t head = row / a.Sq;
+  const size_t pos = row % a.Sq;
+  const float* src = a.dqacc + (head * a.sqp + pos) * D + c * 8;
+  const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+  const float s = a.scale;
+  *(bf16x8*)(a.dq + (head * a.hsq + pos) * D + c * 8) =
+      to_bf16x8(x0[0] * s, x0[1] * s, x0[2] * s, x0[3] * s, x1[0] * s, x1[1] * s, x1[2] * s, x1[3] * s);
+}
+
 struct WsLayout {
-  size_t ld, total;
+  size_t ld, dqacc, total;     // byte offsets of lse2/D and of the fused path's dQ sums; total bytes
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -954,16 +1070,19 @@ WsLayout ws_layout(const Problem& p) {
   const size_t sqp = (size_t)((p.Sq + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
   WsLayout w{};
   w.ld = 0;
-  w.total = align256((size_t)p.B * p.Hq * sqp * 2 * sizeof(float));
+  w.dqacc = align256((size_t)p.B * p.Hq * sqp * 2 * sizeof(float));
+  w.total = w.dqacc + align256((size_t)p.B * p.Hq * sqp * p.d * sizeof(float));
   return w;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool FUSED>
 void launch_dkdv(const BwdArgs& a, hipStream_t s) {
   if (a.drop.thr != 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NoTable, true>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NoTable, true, FUSED>), dim3(a.total_kv), dim3(512), 0, s, a,
+                       NoTable{});
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NoTable, false>), dim3(a.total_kv), dim3(512), 0, s, a, NoTable{});
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, NoTable, false, FUSED>), dim3(a.total_kv), dim3(512), 0, s, a,
+                       NoTable{});
 }
 
 template <int D, bool CAUSAL>
@@ -978,6 +1097,7 @@ template <int D>
 hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   const size_t rows = (size_t)a.B * a.Hq * a.sqp;
   constexpr int RPB = 256 / (D / 8);
+  const bool fused = a.dqacc != nullptr;
   hipError_t e = hipSuccess;
   if (rows > 0) {
     timing_begin(s, "bwd_pre");
@@ -987,12 +1107,38 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
     timing_end(s);
     if (e != hipSuccess) return e;
   }
+  if (fused) {
+    if (a.total_kv > 0) {
+      timing_begin(s, "bwd_dkdvq");
+      if (a.causal)
+        launch_dkdv<D, true, true>(a, s);
+      else
+        launch_dkdv<D, false, true>(a, s);
+      e = hipGetLastError();
+      timing_end(s);
+      if (e != hipSuccess) return e;
+    }
+    // with no key at all the sums stay at the zeros bwd_pre wrote: dq = 0
+    const size_t threads = (size_t)a.B * a.Hq * a.Sq * (D / 8);
+    timing_begin(s, "dq_convert");
+    hipLaunchKernelGGL((dq_convert_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    timing_end(s);
+    if (e != hipSuccess) return e;
+    if (log != nullptr && log_n > 0)
+      snprintf(log, log_n,
+               "attn_bwd: bwd_pre<d=%d> grid=%zu (clears the dQ sums); "
+               "bwd_dkdv<d=%d, fused dQ> grid=%d (128 keys x 32-row query tiles, 8 wavefronts, float32 atomic dQ); "
+               "dq_convert<d=%d> grid=%zu",
+               D, (rows + RPB - 1) / RPB, D, a.total_kv, D, (threads + 255) / 256);
+    return hipSuccess;
+  }
   if (a.total_kv > 0) {
     timing_begin(s, "bwd_dkdv");
     if (a.causal)
-      launch_dkdv<D, true>(a, s);
+      launch_dkdv<D, true, false>(a, s);
     else
-      launch_dkdv<D, false>(a, s);
+      launch_dkdv<D, false, false>(a, s);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -1018,13 +1164,15 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(const Problem& p) { return ws_layout(p).total; }
+size_t bwd_workspace_bytes(const Problem& p) { return ws_layout(p).dqacc; }
+size_t bwd_fused_workspace_bytes(const Problem& p) { return ws_layout(p).total; }
 
 hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
-                           hipStream_t s, char* log, size_t log_n) {
+                           bool fused, hipStream_t s, char* log, size_t log_n) {
   const WsLayout w = ws_layout(p);
   BwdArgs a{};
+  a.dqacc = fused ? (float*)((char*)ws + w.dqacc) : nullptr;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
   a.v = (const bf16*)v;
@@ -1071,9 +1219,9 @@ hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tp, int gp, con
   if (gkv > 0) {
     timing_begin(s, "bwd_dkdv");
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SeqTable, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SeqTable, false, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SeqTable, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SeqTable, false, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;

@@ -142,10 +142,14 @@ hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, cons
                           float* o, float* lse, hipStream_t s);
 
 // ---- backward, bf16 ---------------------------------------------------------
+// Workspace of the two-kernel path (lse2/D), and of the fused path (the same
+// lse2/D block followed by the float32 dQ sums).
 size_t bwd_workspace_bytes(const Problem& p);
+size_t bwd_fused_workspace_bytes(const Problem& p);
 hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq,
-                           void* dk, void* dv, void* ws, hipStream_t s, char* log, size_t log_n);
+                           void* dk, void* dv, void* ws, bool fused, hipStream_t s, char* log,
+                           size_t log_n);
 
 // ---- forward, MXFP8 ---------------------------------------------------------
 // Keys of the transposed FP8 V rounded up to the 64-key tile.

@@ -132,6 +132,26 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward in one pass. attn_bwd runs a dK/dV pass and a separate dQ
+ * pass, which rebuilds S and dP a second time, and its results are the same
+ * bits on every run. attn_bwd_fused instead forms dV, dK and dQ in a single
+ * pass over the (key tile, query tile) pairs, adding each pair's dQ share into
+ * float32 sums with atomic adds (the single-pass backward with accumulated dQ
+ * that "Flash Attention FA1->FA4 / pre-training practice", §2.3, describes for
+ * FA4), then rounds the sums into dq. The order of those additions varies
+ * between runs, so dq can differ in its last bits from run to run, and dk/dv
+ * differ from attn_bwd's by rounding (another summation order). On MI355X it
+ * is slower than attn_bwd (float32 atomic adds are the bottleneck); it is kept
+ * for comparison. Same arguments and errors as attn_bwd, with the workspace
+ * of attn_bwd_fused_workspace_bytes: attn_bwd's block followed by the float32
+ * dQ sums (B * Hq * Sq' * d values, rounded up to 256 bytes). */
+size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                                      int causal, int dtype);
+int attn_bwd_fused(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packed variable-length batches ("ragged layout" of the second page,
  * section on interface constraints, where a packed row number and a logical
  * row number are distinct). B sequences of different lengths are stored

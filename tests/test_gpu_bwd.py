@@ -27,12 +27,13 @@ def attn():
     return m
 
 
-def _fwd_bwd(attn, w):
+def _fwd_bwd(attn, w, fused=False):
     import torch
     x = synth.make_inputs(w, backward=True)
     dev = {n: to_device(x[n], w.dtype) for n in ("q", "k", "v", "do")}
     o, lse = attn.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
-    dq, dk, dv = attn.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=w.causal, scale=w.scale)
+    dq, dk, dv = attn.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=w.causal, scale=w.scale,
+                          fused=fused)
     torch.cuda.synchronize()
     out = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
     return x, dev, out
@@ -53,13 +54,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_pass", "fused"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
-def test_bwd_small_all_outputs(attn, shape):
+def test_bwd_small_all_outputs(attn, shape, fused):
     B, Hq, Hkv, Sq, Sk, d, causal = shape
     w = synth.Workload("small_bwd", B, Hq, Hkv, Sq, Sk, d, "bf16", causal, seed=2000 + sum(shape),
                        backward=True)
-    _say("case", shape)
-    x, dev, out = _fwd_bwd(attn, w)
+    _say("case", shape, "fused" if fused else "two-pass")
+    x, dev, out = _fwd_bwd(attn, w, fused)
     f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v", "do")}
     o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal=causal, scale=w.scale)
     check_o(to_host_f64(out["o"]), o_ref, "bf16")
@@ -68,22 +70,32 @@ def test_bwd_small_all_outputs(attn, shape):
     for n in ("dq", "dk", "dv"):
         r = check_grad(n, to_host_f64(out[n]), g[n])
         _say(f"  {n} rel fro {r:.3e}")
-    assert "bwd_dkdv" in attn.last_dispatch()
+    disp = attn.last_dispatch()
+    assert "bwd_dkdv" in disp and (("bwd_dq<" in disp) != fused) and (("fused dQ" in disp) == fused)
 
 
-def test_masked_positions_get_exactly_zero_gradient(attn):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_pass", "fused"])
+def test_masked_positions_get_exactly_zero_gradient(attn, fused):
     # top-left with Sk > Sq: keys >= Sq are seen by no query -> dK = dV = 0 exactly
     w = synth.Workload("zero_keys", 1, 4, 2, 100, 230, 128, "bf16", 1, seed=31, backward=True)
-    x, dev, out = _fwd_bwd(attn, w)
+    x, dev, out = _fwd_bwd(attn, w, fused)
     dk = to_host_f64(out["dk"])
     dv = to_host_f64(out["dv"])
     assert (dk[:, :, 100:] == 0).all() and (dv[:, :, 100:] == 0).all()
     assert np.abs(dk[:, :, :100]).max() > 0
     # bottom-right with Sq > Sk: query rows i < Sq - Sk see no key -> dQ = 0 exactly
     w = synth.Workload("zero_rows", 1, 4, 4, 200, 90, 64, "bf16", 2, seed=32, backward=True)
-    x, dev, out = _fwd_bwd(attn, w)
+    x, dev, out = _fwd_bwd(attn, w, fused)
     dq = to_host_f64(out["dq"])
     assert (dq[:, :, :110] == 0).all() and np.abs(dq[:, :, 110:]).max() > 0
+    # no key at all: dQ = 0 (the fused path's sums stay at the zeros the first pass wrote)
+    import torch
+    q = dev["q"]
+    kv = torch.empty(1, 4, 0, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = attn.fwd(q, kv, kv, causal=0)
+    dq0, _, _ = attn.bwd(q, kv, kv, o, lse, dev["do"], causal=0, fused=fused)
+    torch.cuda.synchronize()
+    assert (dq0.float() == 0).all()
 
 
 def test_train_workload_full_size(attn):
@@ -129,9 +141,23 @@ def test_train_workload_full_size(attn):
 
 
 def test_backward_is_deterministic(attn):
+    """The two-pass backward gives the same bits every run. The fused one gives
+    the same dK and dV bits every run (no atomics there); its dQ is summed
+    atomically in a varying order, and all three agree with the two-pass
+    results to rounding."""
     import torch
     w = synth.Workload("det_bwd", 1, 4, 2, 300, 300, 128, "bf16", 1, seed=33, backward=True)
     x, dev, out = _fwd_bwd(attn, w)
-    dq, dk, dv = attn.bwd(dev["q"], dev["k"], dev["v"], out["o"], out["lse"], dev["do"], causal=1)
+    for _ in range(3):
+        dq, dk, dv = attn.bwd(dev["q"], dev["k"], dev["v"], out["o"], out["lse"], dev["do"], causal=1)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, out["dq"]) and torch.equal(dk, out["dk"]) and torch.equal(dv, out["dv"])
+    fq, fk, fv = attn.bwd(dev["q"], dev["k"], dev["v"], out["o"], out["lse"], dev["do"], causal=1, fused=True)
+    gq, gk, gv = attn.bwd(dev["q"], dev["k"], dev["v"], out["o"], out["lse"], dev["do"], causal=1, fused=True)
     torch.cuda.synchronize()
-    assert torch.equal(dq, out["dq"]) and torch.equal(dk, out["dk"]) and torch.equal(dv, out["dv"])
+    assert torch.equal(fk, gk) and torch.equal(fv, gv)
+    # the same float32 terms summed in another order, then rounded to bf16
+    for x, y in ((fq, out["dq"]), (fk, out["dk"]), (fv, out["dv"])):
+        a, b = x.float(), y.float()
+        assert torch.linalg.norm(a - b) <= 1e-2 * torch.linalg.norm(b)
+        assert (a - b).abs().max() <= 1e-2 * b.abs().max()
