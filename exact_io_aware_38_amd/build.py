@@ -46,21 +46,68 @@ def _hipcc() -> str:
 KERNEL_ONLY = ["-fno-honor-nans"]
 
 
-def _compile(src: str) -> str:
+# Kernels allowed to use per-lane scratch memory (register spills), with the
+# reason; every other kernel must compile without any. Names are the mangled
+# symbols' distinctive parts.
+SCRATCH_ALLOWED = {
+    # d = 128 prefill with dropout or packed-sequence table: a few values live
+    # across the main loop are stored once before it and reloaded once after
+    "fwd_prefill_kernelILi128ENS_7NoTableELb1E": "dropout variant, spill outside the main loop",
+    "fwd_prefill_kernelILi128ENS_8SeqTableELb0E": "packed variant, spill outside the main loop",
+    # the fp32 parity path (one query row per thread) is not tuned
+    "fwd_f32_kernelILi128E": "fp32 parity path",
+}
+RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
+
+
+def _resources(stderr: str):
+    """(kernel, VGPRs, AGPRs, scratch bytes per lane, waves per SIMD) from the
+    compiler's kernel-resource-usage remarks."""
+    out, cur = [], None
+    for line in stderr.splitlines():
+        if "remark:" not in line:
+            continue
+        text = line.split("remark:", 1)[1].split("[-Rpass")[0].strip()
+        key, _, val = text.partition(":")
+        val = val.strip()
+        if key == "Function Name":
+            cur = {"kernel": val}
+            out.append(cur)
+        elif cur is not None and key in ("VGPRs", "AGPRs", "ScratchSize [bytes/lane]", "Occupancy [waves/SIMD]"):
+            cur[key.split()[0]] = int(val)
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     extra = (KERNEL_ONLY if src.endswith(".hip") else []) + PER_SOURCE.get(src, [])
-    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *extra, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libattn.so. Returns its path."""
+    """Compile every source for gfx950 and link libattn.so. Returns its path.
+
+    Also writes the per-kernel register, scratch and occupancy figures to
+    _build/kernel_resources.txt and fails if a kernel outside SCRATCH_ALLOWED
+    spills to scratch memory."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        done = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in done]
+    res = [k for _, ks in done for k in ks]
+    with open(RESOURCES, "w") as f:
+        for k in res:
+            f.write(f"{k['kernel']} VGPRs={k.get('VGPRs')} AGPRs={k.get('AGPRs')} "
+                    f"scratch={k.get('ScratchSize')} waves/SIMD={k.get('Occupancy')}\n")
+    bad = [k["kernel"] for k in res if k.get("ScratchSize", 0) > 0
+           and not any(a in k["kernel"] for a in SCRATCH_ALLOWED)]
+    if bad:
+        raise RuntimeError("kernels spill to scratch memory: " + ", ".join(bad))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -196,19 +196,21 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   // The swizzle of those rows does not change with kc (16 kc adds nothing to
   // the row bits it uses), so kc is an immediate offset too.
   uint32_t kb[DC], vb[MB][2];
+  auto lds_offsets = [&](int ln) __attribute__((always_inline)) {
+    const int r32 = ln & 31, h32 = ln >> 5;
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) kb[dc] = l32 * RB + (((2 * dc + hi) ^ chunk_swizzle<D>(l32)) << 4);
-  {
-    const int L = lane & 15, dhalf = (lane >> 4) & 1;
+    for (int dc = 0; dc < DC; ++dc) kb[dc] = r32 * RB + (((2 * dc + h32) ^ chunk_swizzle<D>(r32)) << 4);
+    const int L = ln & 15, dhalf = (ln >> 4) & 1;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int r = 4 * hi + (L >> 2) + 8 * h;
+        const int r = 4 * h32 + (L >> 2) + 8 * h;
         const int c = 32 * mb + 16 * dhalf + 4 * (L & 3);
         vb[mb][h] = R::TILE + r * RB + (((c >> 3) ^ chunk_swizzle<D>(r)) << 4) + (c & 7) * 2;
       }
-  }
+  };
+  lds_offsets(lane);
 
   // Per-lane DMA geometry (the same for K and V tiles): lane i of instruction
   // n writes LDS chunk P = (wid*INSTR + n)*64 + i of a tile, i.e. row P / CPR,
@@ -391,6 +393,9 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
     full(I3{}, j + 2);
     full(I0{}, j + 3);
   }
+  // the last steps get freshly computed offsets (from the lane index counted
+  // again), so that no offset is held, or spilled, across the main loop
+  lds_offsets((int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
   if (j < ntiles) full(I1{}, j);
   if (j + 1 < ntiles) full(I2{}, j + 1);
   if (j + 2 < ntiles) full(I3{}, j + 2);
@@ -412,8 +417,11 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   float inv = lt > 0.f ? 1.f / lt : 0.f;
   if constexpr (DROP) inv *= a.drop.scale;
   const float lse_v = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : kNegInf;
-  if (!colv) return;
-  bf16* op = a.o + (((size_t)b * a.Hq + head) * a.hsq + pos) * D;
+  // this lane's row, from the lane index counted again (not held across the loop)
+  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int pos_e = p0 + (ln & 31), hi_e = ln >> 5;
+  if (pos_e >= a.Sq) return;
+  bf16* op = a.o + (((size_t)b * a.Hq + head) * a.hsq + pos_e) * D;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -423,9 +431,9 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
       r[1] = (bf16)(acc[mb][4 * q4 + 1] * inv);
       r[2] = (bf16)(acc[mb][4 * q4 + 2] * inv);
       r[3] = (bf16)(acc[mb][4 * q4 + 3] * inv);
-      *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi) = r;
+      *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi_e) = r;
     }
-  if (a.lse != nullptr && hi == 0) a.lse[((size_t)b * a.Hq + head) * a.hsq + pos] = lse_v;
+  if (a.lse != nullptr && hi_e == 0) a.lse[((size_t)b * a.Hq + head) * a.hsq + pos_e] = lse_v;
 }
 
 // ---------------------------------------------------------------------------
