@@ -334,7 +334,10 @@ def bench_fp8(attn, steps, warmup):
             "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
             "roofline": roofline("fwd_fp8", w.with_(name=w.name + "_mxfp8"), kern["fwd_fp8"]),
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
-            "quantise_ms": round(qms, 4), "quantise_kernels_ms": {k: round(v, 4) for k, v in qkern.items()}}
+            "quantise_ms": round(qms, 4), "quantise_kernels_ms": {k: round(v, 4) for k, v in qkern.items()},
+            # from bf16 operands: quantising Q, K and V, then the FP8 forward
+            "with_quantise": {"ms": round(ms + qms, 4), "tflops": round(flops / (ms + qms) / 1e9, 2),
+                              "frac_of_bf16_peak": round(flops / (ms + qms) / 1e9 / PEAK_BF16_TFLOPS, 4)}}
 
 
 def bench_fp8_decode(attn, steps, warmup):
