@@ -457,7 +457,7 @@ def host_description() -> dict:
     return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity": affinity, "blas_threads": blas}
 
 
-def cpu_baseline(w, heads: int = 4) -> dict:
+def cpu_baseline(w, heads: int = 8) -> dict:
     """The FP64 oracle as it stands, on a bounded sample of each measured
     workload: fwd + bwd on a few heads of the training workload (the headline
     figure), the forward on one head of the long-context workload, and the

@@ -19,7 +19,9 @@ error per head, a statistical check: the rounding errors of different keys are
 independent, so it is close to the RMS relative error of E4M3 rounding, which
 for mantissas m spread log-uniformly over [1, 2) is 2^-4 sqrt(E[m^-2] / 3) =
 2^-4 sqrt(0.541 / 3) ~ 2.65 %; the bound is 1.5 times that, 4e-2 (observed
-1.4 % to 2.8 %). lse does not depend on the rounding of P;
+worst heads from 1.3 % to 3.1 % over the cases below; a head averages fewer
+independent roundings when few keys dominate its rows, so its figure spreads
+around the RMS value). lse does not depend on the rounding of P;
 it moves by at most the largest score error, and a score is an fp32 dot
 product of d exact products, which any summation order with directed
 rounding keeps within d 2^-23 sum_c |q_c k_c| (= 2^-16 for d = 128). So
