@@ -54,8 +54,6 @@ SCRATCH_ALLOWED = {
     # across the main loop are stored once before it and reloaded once after
     "fwd_prefill_kernelILi128ENS_7NoTableELb1E": "dropout variant, spill outside the main loop",
     "fwd_prefill_kernelILi128ENS_8SeqTableELb0E": "packed variant, spill outside the main loop",
-    # the fp32 parity path (one query row per thread) is not tuned
-    "fwd_f32_kernelILi128E": "fp32 parity path",
 }
 RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
 
