@@ -584,7 +584,11 @@ def summarize_pmc(workload: str, title: str, dirs, command: str, out_md: str = N
       VALUBusy expression;
     * executed MFMA work: SQ_INSTS_VALU_MFMA_MOPS_BF16 (or _F8) x 512 FLOP;
     * transcendental share: SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_VALU;
-    * LDS bank conflicts: SQ_LDS_BANK_CONFLICT cycles per CU cycle.
+    * LDS bank conflicts: SQ_LDS_BANK_CONFLICT cycles per CU cycle;
+    * with a second pass: the share of MFMA-busy cycles in which the vector
+      ALU co-executes (SQ_VALU_MFMA_COEXEC_CYCLES), LDS activity and FIFO-full
+      cycles per CU cycle, and the share of wave cycles spent waiting to issue
+      an LDS instruction, waiting on anything, or issuing (per SQ_WAVE_CYCLES).
 
     Writes profiles/pmc__<workload>.md (or out_md) and returns its path."""
     per = {}         # short kernel name -> counter -> [values]
@@ -640,6 +644,21 @@ def summarize_pmc(workload: str, title: str, dirs, command: str, out_md: str = N
         b = mean(k, "SQ_LDS_BANK_CONFLICT")
         if b is not None and gui:
             lines.append(f"| LDS bank-conflict cycles per CU cycle | {b / (gui / N_XCD * N_SIMD / 4):.4f} |")
+        co, mb = mean(k, "SQ_VALU_MFMA_COEXEC_CYCLES"), mean(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+        if co is not None and mb:
+            lines.append(f"| VALU co-executing with MFMA (% of MFMA-busy cycles) | {100 * co / mb:.1f} |")
+        cu_cycles = gui / N_XCD * N_SIMD / 4 if gui else None
+        for ctr, label in (("SQ_LDS_IDX_ACTIVE", "LDS active"), ("SQ_LDS_DATA_FIFO_FULL", "LDS data FIFO full"),
+                           ("SQ_LDS_CMD_FIFO_FULL", "LDS command FIFO full")):
+            x = mean(k, ctr)
+            if x is not None and cu_cycles:
+                lines.append(f"| {label} (% of CU cycles) | {100 * x / cu_cycles:.1f} |")
+        wc = mean(k, "SQ_WAVE_CYCLES")
+        for ctr, label in (("SQ_WAIT_INST_LDS", "waiting to issue an LDS instruction"),
+                           ("SQ_WAIT_ANY", "waiting on anything"), ("SQ_ACTIVE_INST_ANY", "issuing")):
+            x = mean(k, ctr)
+            if x is not None and wc:
+                lines.append(f"| wave cycles {label} (%) | {100 * x / wc:.1f} |")
         lines.append("")
     out_md = out_md or os.path.join(PROFILES, f"pmc__{workload}.md")
     with open(out_md, "w") as f:

@@ -12,6 +12,9 @@
 // of the first page), and the rescale is skipped unless some row's max grew
 // by more than RESCALE_T (§2.3 of the first page describes the skip; with a
 // threshold the probabilities stay below 2^RESCALE_T and u / l is unchanged).
+// Without dropout the row max itself is formed only where it can matter: at
+// the first tile, and where a lane's probabilities against the current
+// reference sum to more than 2^RESCALE_T.
 //
 // Mapping to CDNA4:
 //  * a wavefront owns 32 query rows as MFMA columns and computes the transposed
@@ -72,6 +75,7 @@ hipError_t noalloc_scratch(void** ptr) {
 namespace {
 
 constexpr float RESCALE_T = 8.0f;   // log2 units
+constexpr float kRescaleSum = 256.0f;   // 2^RESCALE_T
 constexpr int BC = 64;               // keys per tile
 
 struct FwdArgs {
@@ -308,6 +312,23 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
     });
     __builtin_amdgcn_s_setprio(0);
   };
+  // The reference max m2 (log2 units) of this lane's row moves only when the
+  // row max grew by more than RESCALE_T; the running sum and output are then
+  // rescaled. msub is m2, or 0 while m2 = -inf.
+  float msub = 0.f;
+  auto move_max = [&](const float* v) __attribute__((always_inline)) {
+    const float mx = max_halves(tree_max32(v)) * a.c;
+    const bool grow = mx > m2 + RESCALE_T;
+    if (!wave_any(grow)) return false;
+    const float mnew = grow ? mx : m2;
+    const float alpha = grow ? fast_exp2(m2 - mnew) : 1.f;
+    lsum *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+    m2 = mnew;
+    msub = (m2 == kNegInf) ? 0.f : m2;
+    return true;
+  };
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int key0 = j * BC;
     float v[32];
@@ -323,21 +344,10 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
         if (key > lim) v[i] = kNegInf;
       }
     }
-    const float mx = max_halves(tree_max32(v)) * a.c;
-    // move the reference max only when the row max grew by more than RESCALE_T
-    const bool grow = mx > m2 + RESCALE_T;
-    if (wave_any(grow)) {
-      const float mnew = grow ? mx : m2;
-      const float alpha = grow ? fast_exp2(m2 - mnew) : 1.f;
-      lsum *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
-      m2 = mnew;
-    }
-    const float msub = (m2 == kNegInf) ? 0.f : m2;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = fast_exp2(__builtin_fmaf(v[i], a.c, -msub));
     if constexpr (DROP) {
+      move_max(v);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = fast_exp2(__builtin_fmaf(v[i], a.c, -msub));
       lsum += tree_sum32(v);
       // values 4g .. 4g+3 are keys 4 j4 .. 4 j4 + 3 of this lane's query row:
       // word (pos & 3) of block (pos / 4, j4)
@@ -352,12 +362,36 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
         for (int t = 0; t < 4; ++t)
           if (((word >> (8 * t)) & 0xffu) < a.drop.thr) v[4 * g + t] = 0.f;
       }
-    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      pf[q] = to_bf16x8(v[8 * q + 0], v[8 * q + 1], v[8 * q + 2], v[8 * q + 3], v[8 * q + 4], v[8 * q + 5],
-                        v[8 * q + 6], v[8 * q + 7]);
-    if constexpr (!DROP) lsum += tree_sum32(v);
+      for (int q = 0; q < 4; ++q)
+        pf[q] = to_bf16x8(v[8 * q + 0], v[8 * q + 1], v[8 * q + 2], v[8 * q + 3], v[8 * q + 4], v[8 * q + 5],
+                          v[8 * q + 6], v[8 * q + 7]);
+    } else {
+      // The probabilities are first taken against the current m2. While every
+      // lane's sum of its 32 values stays within 2^RESCALE_T, no score of the
+      // wavefront exceeds m2 + RESCALE_T, so m2 stays and the row max is not
+      // needed; otherwise, and at tile 0 (the first tile of every row that
+      // sees any key), the row max is formed and the rule applied. Either way
+      // the result is the same. Groups of eight values are summed and packed
+      // as they are formed; the four group sums make the same tree as
+      // tree_sum32.
+      auto probs = [&]() __attribute__((always_inline)) {
+        float g[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(v[8 * q + i], a.c, -msub));
+          g[q] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          pf[q] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        }
+        return (g[0] + g[1]) + (g[2] + g[3]);
+      };
+      float ts = probs();
+      if (j == 0 || wave_any(!(ts <= kRescaleSum)))
+        if (move_max(v)) ts = probs();
+      lsum += ts;
+    }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
