@@ -188,6 +188,34 @@ def test_batched_equals_single_head_runs(attn):
             assert torch.equal(o1[0, 0], o[b, h]) and torch.equal(l1[0, 0], lse[b, h])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_scores_growing_across_key_tiles(attn, d, causal):
+    """The reference max moves only when a row max grows by more than 2^8, and
+    the kernel looks for such growth through the per-lane probability sums.
+    Key tiles here get growing norms (each 64-key tile x1.6, a few rows
+    crossing the threshold at every tile) and the last tiles a jump of about
+    2^11 in the scores, so that probabilities against the old reference
+    overflow to inf: every branch of that test runs, and O and lse must still
+    match the oracle."""
+    B, H, S = 1, 4, 520
+    w = synth.Workload("growth", B, H, H, S, S, d, "bf16", causal, seed=4242 + d + causal)
+    _say("growth", d, causal)
+    x = synth.make_inputs(w)
+    kf = synth.f32_from_bf16_bits(x["k"])
+    tile = np.arange(S) // 64
+    factor = 1.6 ** tile
+    factor[tile >= 7] *= 12.0
+    kf = kf * factor[None, None, :, None].astype(np.float32)
+    x["k"] = synth.bf16_bits_from_f32(kf)
+    dev = {n: to_device(x[n], "bf16") for n in ("q", "k", "v")}
+    f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v")}
+    o, lse = _run(attn, w, dev)
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal=causal, scale=w.scale)
+    check_o(o, o_ref, "bf16")
+    check_lse(lse, lse_ref)
+
+
 def test_no_keys_and_fully_masked_rows(attn):
     import torch
     # Sk = 0: every row is empty
