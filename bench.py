@@ -22,6 +22,8 @@ min, max).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration          (a plain copy of known size,
                                                     for counter calibration)
+       python bench.py --only mfma_ceiling         (the chip's sustained bf16 MFMA
+                                                    rate on an MFMA-only loop)
        python bench.py --summarize-counters WORKLOAD FETCH_DIR WRITE_DIR
                        COPY_FETCH_DIR COPY_WRITE_DIR   (turn rocprofv3 --pmc
                        output into per-kernel HBM-traffic summaries in profiles/)
@@ -518,6 +520,41 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
+def mfma_ceiling(reps: int = 5) -> dict:
+    """Sustained bf16 MFMA rate of the whole chip on a loop of independent
+    32x32x16 MFMAs and nothing else (libcalib.so; one workgroup of four
+    wavefronts per CU, 2.3 ms per launch), median of `reps` launches after one
+    warm-up. The published dense peak assumes the top clock, which the chip does
+    not hold under a full matrix load; this figure is what the kernels' MFMA
+    fractions can be read against. Reported next to the published peak, never
+    in place of it."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_38_amd", "libcalib.so"))
+    lib.calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_mfma_bf16.restype = ctypes.c_int
+    blocks, nit = 256, 16384
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flop = blocks * 4 * nit * 8 * (2 * 32 * 32 * 16)
+    times = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.calib_mfma_bf16(out.data_ptr(), blocks, nit, stream.cuda_stream)
+        e1.record(stream)
+        stream.synchronize()
+        if st != 0:
+            raise RuntimeError(f"calib_mfma_bf16 failed with status {st}")
+        if r:
+            times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    tf = flop / ms / 1e9
+    return {"tflops": round(tf, 1), "frac_of_published_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 3),
+            "kernel": "mfma_loop_kernel: 8 independent 32x32x16 bf16 MFMA chains per wavefront, 4 wavefronts per CU",
+            "launches": reps}
+
+
 def _read_counter_csv(d: str):
     rows = []
     for p in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
@@ -722,7 +759,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "step", "step_fused", "fwd", "decode", "varlen", "fp8", "fp8_decode", "f32",
-                                       "d64", "gqa_prefill"], default="all")
+                                       "d64", "gqa_prefill", "mfma_ceiling"], default="all")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
                     help="WORKLOAD TITLE DIR [DIR ...]")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -810,6 +847,12 @@ def main() -> int:
         result["varlen"] = bench_varlen(attn, args.steps, args.warmup)
         print(f"# varlen: {result['varlen']['ms']} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+    if args.only in ("all", "mfma_ceiling"):
+        result["mfma_ceiling"] = mfma_ceiling()
+        print(f"# sustained MFMA loop: {result['mfma_ceiling']['tflops']} TFLOP/s", file=sys.stderr, flush=True)
+    if args.only == "mfma_ceiling":
+        r = result["mfma_ceiling"]
+        result.update({"value": r["tflops"], "ms_per_step": r["ms"], "config": {"workload": "mfma_loop"}})
     if args.only == "varlen":
         result.update({"value": result["varlen"]["tflops"], "ms_per_step": result["varlen"]["ms"],
                        "config": {"workload": result["varlen"]["workload"]},

@@ -19,6 +19,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip", "fwd_fp8.hip"]
+# Measurement aid for the benchmark (sustained MFMA rate), kept out of libattn.so.
+CALIB_LIB = os.path.join(PKG, "libcalib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 arithmetic is switched off for all device code.
@@ -88,15 +91,17 @@ def _compile(src: str):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libattn.so. Returns its path.
+    """Compile every source for gfx950 and link libattn.so (and the
+    benchmark's libcalib.so). Returns the path of libattn.so.
 
     Also writes the per-kernel register, scratch and occupancy figures to
     _build/kernel_resources.txt and fails if a kernel outside SCRATCH_ALLOWED
     spills to scratch memory."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        done = list(ex.map(_compile, SOURCES))
-    objs = [o for o, _ in done]
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(CALIB_SOURCES), 8)) as ex:
+        done = list(ex.map(_compile, SOURCES + CALIB_SOURCES))
+    objs = [o for o, _ in done[:len(SOURCES)]]
+    calib_objs = [o for o, _ in done[len(SOURCES):]]
     res = [k for _, ks in done for k in ks]
     with open(RESOURCES, "w") as f:
         for k in res:
@@ -106,12 +111,13 @@ def build(verbose: bool = False) -> str:
            and not any(a in k["kernel"] for a in SCRATCH_ALLOWED)]
     if bad:
         raise RuntimeError("kernels spill to scratch memory: " + ", ".join(bad))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    for out, o in ((LIB, objs), (CALIB_LIB, calib_objs)):
+        tmp = out + ".tmp"
+        cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *o, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed for {os.path.basename(out)}:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, out)
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -27,3 +27,16 @@ def test_only_listed_kernels_may_spill():
                 and not any(a in k["kernel"] for a in build.SCRATCH_ALLOWED)]
     assert spilling == [r[1]["kernel"]]                 # the split kernel is not on the list
     assert not any(a in r[0]["kernel"] for a in build.SCRATCH_ALLOWED)   # the benchmarked prefill is not either
+
+
+def test_calibration_library_is_separate_and_exports_its_entry():
+    """The benchmark's MFMA calibration kernel lives in its own library, so
+    libattn.so exports only the attention entry points."""
+    import ctypes
+    import os
+    import subprocess
+    assert os.path.exists(build.CALIB_LIB), "run __graft_entry__.build() first"
+    lib = ctypes.CDLL(build.CALIB_LIB)
+    assert hasattr(lib, "calib_mfma_bf16")
+    syms = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True).stdout
+    assert "calib_mfma_bf16" not in syms
