@@ -103,26 +103,6 @@ struct BwdArgs {
   DropParams drop;
 };
 
-// Workgroup order: the 8 XCDs each receive a contiguous range of logical ids
-// (xcd_logical_id), i.e. whole heads, whose tiles then share that XCD's L2.
-// Inside the range, when it holds whole heads, the tile index varies slowest
-// so that the longest causal tiles of all its heads start first.
-__device__ __forceinline__ void wg_coords(int total, int tiles, int& tile, int& head) {
-  const int W = xcd_logical_id(blockIdx.x, total);
-  if ((total & 7) == 0) {
-    const int R = total >> 3;
-    if (R % tiles == 0) {
-      const int nh = R / tiles;
-      const int x = W / R, s = W % R;
-      tile = s / nh;
-      head = x * nh + s % nh;
-      return;
-    }
-  }
-  tile = W % tiles;
-  head = W / tiles;
-}
-
 // Sequence s of a packed launch as a problem of batch 1: lengths, data
 // pointers and its lse2/D block from the table (the head strides stay the
 // packed totals).
@@ -261,7 +241,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
     b = 0;
   } else {
     int bh;
-    wg_coords(a.total_kv, a.n_ktiles, kt, bh);
+    xcd_tile_order(a.total_kv, a.n_ktiles, kt, bh);
     hkv = bh % a.Hkv;
     b = bh / a.Hkv;
   }
@@ -727,7 +707,7 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
     b = 0;
   } else {
     int bh;
-    wg_coords(a.total_q, a.n_qtiles, qtile, bh);
+    xcd_tile_order(a.total_q, a.n_qtiles, qtile, bh);
     hq = bh % a.Hq;
     b = bh / a.Hq;
   }

@@ -120,6 +120,29 @@ __device__ __forceinline__ int xcd_logical_id(int linear, int total) {
   return (linear & 7) * (total >> 3) + (linear >> 3);
 }
 
+// Workgroup -> (tile, unit) for grids of `tiles` tiles per unit (a unit being
+// a head, or a group of heads) whose tiles differ in length, tile 0 the
+// longest. Each XCD receives a contiguous range of logical ids (whole units
+// when the range holds whole units, so the units' K/V lines stay in that XCD's
+// L2), and inside the range the tile index varies slowest: the XCD starts the
+// longest tiles of all its units first, which keeps the short ones for the
+// end of the launch.
+__device__ __forceinline__ void xcd_tile_order(int total, int tiles, int& tile, int& unit) {
+  const int W = xcd_logical_id(blockIdx.x, total);
+  if ((total & 7) == 0) {
+    const int R = total >> 3;
+    if (R % tiles == 0) {
+      const int nu = R / tiles;
+      const int x = W / R, s = W % R;
+      tile = s / nu;
+      unit = x * nu + s % nu;
+      return;
+    }
+  }
+  tile = W % tiles;
+  unit = W / tiles;
+}
+
 // Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw
 // ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds of two
 // 32x32->64-bit products whose halves are mixed with the other two counter

@@ -153,9 +153,9 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
     hkv = c.unit / a.n_hgroups;
     b = 0;
   } else {
-    const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
-    ptile = a.n_ptiles - 1 - (W % a.n_ptiles);
-    int rest = W / a.n_ptiles;
+    int t, rest;
+    xcd_tile_order(a.total_wgs, a.n_ptiles, t, rest);
+    ptile = a.n_ptiles - 1 - t;
     hgrp = rest % a.n_hgroups;
     rest /= a.n_hgroups;
     hkv = rest % a.Hkv;

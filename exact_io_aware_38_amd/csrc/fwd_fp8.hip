@@ -135,9 +135,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
   const int hi = lane >> 5;
   const bool phase_b = wid >= 4;
 
-  const int W = xcd_logical_id(blockIdx.x, a.total_wgs);
-  const int ptile = a.n_ptiles - 1 - (W % a.n_ptiles);     // longest causal tiles first
-  int rest = W / a.n_ptiles;
+  int t, rest;
+  xcd_tile_order(a.total_wgs, a.n_ptiles, t, rest);
+  const int ptile = a.n_ptiles - 1 - t;                    // longest causal tiles first
   const int hgrp = rest % a.n_hgroups;
   rest /= a.n_hgroups;
   const int hkv = rest % a.Hkv;
