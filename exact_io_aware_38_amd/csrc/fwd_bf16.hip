@@ -30,7 +30,9 @@
 //  * two wavefronts share each SIMD and run the per-tile steps in opposite
 //    orders so that one's softmax (vector ALU) overlaps the other's MFMAs;
 //  * exp2 with log2(e) folded into the score scale: one FMA and one v_exp_f32
-//    per score.
+//    per score;
+//  * each XCD takes whole heads and starts the longest causal query tiles of
+//    all of them first (xcd_tile_order), so the launch ends on short tiles.
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
