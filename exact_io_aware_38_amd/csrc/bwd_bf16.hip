@@ -10,21 +10,24 @@
 // probabilities are exactly zero, so their gradients are too.
 //
 // Kernels, all on the caller's stream:
-//  1. bwd_pre:   D_i = dO_i . O_i and lse2_i = lse_i * log2(e) (+inf for rows
+//  1. bwd_dq:    one workgroup per (query head, 128-row tile); forms its rows'
+//                D_i = dO_i . O_i and lse2_i = lse_i * log2(e) (+inf for rows
 //                that see no key and for padding rows, which makes every
-//                rebuilt probability 0), packed per 32 rows;
+//                rebuilt probability 0), writes them packed per 32 rows for
+//                the next pass, then loops over 32-key tiles, accumulating
+//                dQ^T in registers;
 //  2. bwd_dkdv:  one workgroup per (KV head, 128-key tile); loops over the
 //                query heads that share the KV head and over 32-row query
-//                tiles, accumulating dK^T and dV^T in registers (no atomics);
-//  3. bwd_dq:    one workgroup per (query head, 128-row tile); loops over
-//                32-key tiles, accumulating dQ^T in registers.
+//                tiles, accumulating dK^T and dV^T in registers (no atomics).
 // The dK/dV and dQ passes both rebuild S and dP, which costs two GEMMs more
-// than a single pass with atomic dQ but keeps the result deterministic.
+// than a single pass with atomic dQ but keeps the result deterministic. (A
+// separate pass computing the row terms first measured 1 % slower on the
+// whole training step than forming them in the dQ pass.)
 //
-// Fused path (attn_bwd_fused): the dK/dV pass also forms dQ = dS K for its
-// 128 keys and adds it into a float32 workspace with vector atomic adds, so S
-// and dP are rebuilt once; bwd_pre clears the workspace first and dq_convert
-// scales and rounds it into dq afterwards. The order in which workgroups add
+// Fused path (attn_bwd_fused): a first pass, bwd_pre, forms the row terms and
+// clears a float32 dQ workspace; the dK/dV pass also forms dQ = dS K for its
+// 128 keys and adds it into that workspace with vector atomic adds, so S and
+// dP are rebuilt once; dq_convert scales and rounds it into dq afterwards. The order in which workgroups add
 // into a dQ row varies from run to run, so the float32 sums (and at times the
 // bf16 result) do too. On this chip it is the slower form: every (128-key
 // tile, query row) pair costs d float32 atomic adds, about 1.1e9 for the
@@ -741,12 +744,27 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
         df[cb][dc] = qf[cb][dc];
       }
     }
-    l2[cb] = __builtin_huge_valf();
-    dl[cb] = 0.f;
+    // The row terms of this lane's query row, formed here rather than by a
+    // preprocessing pass: D = dO . O over the row's channels (this lane's
+    // half, then its partner lane's) and lse2 = lse log2(e), +inf where the
+    // row sees no key or lies past Sq (every rebuilt probability is then 0).
+    // They also go to the row's lse2/D block for the dK/dV pass that follows.
+    float dpart = 0.f, l = kNegInf;
     if (valid[cb]) {
-      const float* blk = a.ld + (hrow * (a.sqp / BT) + pos[cb] / BT) * (2 * BT);
-      l2[cb] = blk[pos[cb] % BT];
-      dl[cb] = blk[BT + pos[cb] % BT];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 ov = *(const bf16x8*)(a.o + qrow * D + 16 * dc + 8 * hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)ov[e], (float)df[cb][dc][e], dpart);
+      }
+      l = a.lse[qrow];
+    }
+    dl[cb] = sum_halves(dpart);
+    l2[cb] = (l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+    if (hi == 0 && pos[cb] < a.sqp) {
+      float* blk = a.ld + (hrow * (a.sqp / BT) + pos[cb] / BT) * (2 * BT);
+      blk[pos[cb] % BT] = l2[cb];
+      blk[BT + pos[cb] % BT] = dl[cb];
     }
   }
 #pragma unroll
@@ -1079,7 +1097,7 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
   constexpr int RPB = 256 / (D / 8);
   const bool fused = a.dqacc != nullptr;
   hipError_t e = hipSuccess;
-  if (rows > 0) {
+  if (fused && rows > 0) {
     timing_begin(s, "bwd_pre");
     hipLaunchKernelGGL((bwd_pre_kernel<D, NoTable>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
                        a, NoTable{});
@@ -1113,16 +1131,7 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
                D, (rows + RPB - 1) / RPB, D, a.total_kv, D, (threads + 255) / 256);
     return hipSuccess;
   }
-  if (a.total_kv > 0) {
-    timing_begin(s, "bwd_dkdv");
-    if (a.causal)
-      launch_dkdv<D, true, false>(a, s);
-    else
-      launch_dkdv<D, false, false>(a, s);
-    e = hipGetLastError();
-    timing_end(s);
-    if (e != hipSuccess) return e;
-  }
+  // dQ first: it also writes the row terms (lse2, D) that the dK/dV pass reads
   if (a.total_q > 0) {
     timing_begin(s, "bwd_dq");
     if (a.causal)
@@ -1133,12 +1142,21 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t s, char* log, size_t log_n) {
     timing_end(s);
     if (e != hipSuccess) return e;
   }
+  if (a.total_kv > 0) {
+    timing_begin(s, "bwd_dkdv");
+    if (a.causal)
+      launch_dkdv<D, true, false>(a, s);
+    else
+      launch_dkdv<D, false, false>(a, s);
+    e = hipGetLastError();
+    timing_end(s);
+    if (e != hipSuccess) return e;
+  }
   if (log != nullptr && log_n > 0)
     snprintf(log, log_n,
-             "attn_bwd: bwd_pre<d=%d> grid=%zu; "
-             "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles, 8 wavefronts); "
-             "bwd_dq<d=%d> grid=%d (%d rows x 32-key tiles)",
-             D, (rows + RPB - 1) / RPB, D, a.total_kv, D, a.total_q, Q_WG);
+             "attn_bwd: bwd_dq<d=%d> grid=%d (%d rows x 32-key tiles; also the rows' lse2 and D); "
+             "bwd_dkdv<d=%d> grid=%d (128 keys x 32-row query tiles, 8 wavefronts)",
+             D, a.total_q, Q_WG, D, a.total_kv);
   return hipSuccess;
 }
 
@@ -1186,12 +1204,16 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
 namespace {
 
 template <int D>
-hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tp, int gp, const SeqTable& Tkv, int gkv,
-                               const SeqTable& Tq, int gq, hipStream_t s) {
+hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tkv, int gkv, const SeqTable& Tq, int gq,
+                               hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (gp > 0) {
-    timing_begin(s, "bwd_pre");
-    hipLaunchKernelGGL((bwd_pre_kernel<D, SeqTable>), dim3(gp), dim3(256), 0, s, a, Tp);
+  // dQ first: it also writes the row terms (lse2, D) that the dK/dV pass reads
+  if (gq > 0) {
+    timing_begin(s, "bwd_dq");
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, SeqTable, false>), dim3(gq), dim3(256), 0, s, a, Tq);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, SeqTable, false>), dim3(gq), dim3(256), 0, s, a, Tq);
     e = hipGetLastError();
     timing_end(s);
     if (e != hipSuccess) return e;
@@ -1202,16 +1224,6 @@ hipError_t launch_bwd_packed_d(const BwdArgs& a, const SeqTable& Tp, int gp, con
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SeqTable, false, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SeqTable, false, false>), dim3(gkv), dim3(512), 0, s, a, Tkv);
-    e = hipGetLastError();
-    timing_end(s);
-    if (e != hipSuccess) return e;
-  }
-  if (gq > 0) {
-    timing_begin(s, "bwd_dq");
-    if (a.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true, SeqTable, false>), dim3(gq), dim3(256), 0, s, a, Tq);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false, SeqTable, false>), dim3(gq), dim3(256), 0, s, a, Tq);
     e = hipGetLastError();
     timing_end(s);
   }
@@ -1249,29 +1261,25 @@ hipError_t launch_bwd_bf16_packed(const Problem& p, const SeqSpan* seqs, int n, 
   a.causal = p.causal;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
-  const int rpb = 256 / (p.d / 8);              // bwd_pre rows per block
-  int np[SEQ_MAX], nkv[SEQ_MAX], nq[SEQ_MAX], ld0[SEQ_MAX];
+  int nkv[SEQ_MAX], nq[SEQ_MAX], ld0[SEQ_MAX];
   int rows = 0;
   for (int i = 0; i < n; ++i) {
     const int sqp = (seqs[i].sq + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
-    np[i] = p.Hq * (sqp / rpb);
     nkv[i] = (seqs[i].sk + KV_WG - 1) / KV_WG;
     nq[i] = (seqs[i].sq + Q_WG - 1) / Q_WG;
     ld0[i] = rows;
     rows += sqp;
   }
-  SeqTable Tp, Tkv, Tq;
-  const int gp = build_seq_table(Tp, seqs, n, 1, np, ld0);
+  SeqTable Tkv, Tq;
   const int gkv = build_seq_table(Tkv, seqs, n, p.Hkv, nkv, ld0);
   const int gq = build_seq_table(Tq, seqs, n, p.Hq, nq, ld0);
   if (log != nullptr && log_n > 0)
     snprintf(log, log_n,
-             "bwd_pre<d=%d, packed> grid=%d; bwd_dkdv<d=%d, packed> %d sequences grid=%d%s; "
-             "bwd_dq<d=%d, packed> %d sequences grid=%d%s",
-             p.d, gp, p.d, Tkv.n, gkv, Tkv.split8 ? " (per-XCD head split)" : "", p.d, Tq.n, gq,
-             Tq.split8 ? " (per-XCD head split)" : "");
-  return p.d == 64 ? launch_bwd_packed_d<64>(a, Tp, gp, Tkv, gkv, Tq, gq, s)
-                   : launch_bwd_packed_d<128>(a, Tp, gp, Tkv, gkv, Tq, gq, s);
+             "bwd_dq<d=%d, packed> %d sequences grid=%d%s (also the rows' lse2 and D); "
+             "bwd_dkdv<d=%d, packed> %d sequences grid=%d%s",
+             p.d, Tq.n, gq, Tq.split8 ? " (per-XCD head split)" : "", p.d, Tkv.n, gkv,
+             Tkv.split8 ? " (per-XCD head split)" : "");
+  return p.d == 64 ? launch_bwd_packed_d<64>(a, Tkv, gkv, Tq, gq, s) : launch_bwd_packed_d<128>(a, Tkv, gkv, Tq, gq, s);
 }
 
 }  // namespace attn

@@ -174,7 +174,7 @@ int attn_bwd_fused(const void* q, const void* k, const void* v, const void* o,
  * sequence in batch order, each reusing the start of the one workspace; the
  * remaining bf16 sequences then run as packed grids of up to 64 sequences
  * each (largest work first), which need no workspace. Backward: packed grids
- * of up to 64 sequences (bwd_pre, dK/dV, dQ kernels per grid) over every
+ * of up to 64 sequences (dQ, then dK/dV kernels per grid) over every
  * sequence with queries or keys, in the same order; the workspace holds the
  * lse2/D rows of every sequence at once. So one workspace of the size the
  * query returns serves the whole call. */
