@@ -857,6 +857,15 @@ def main() -> int:
     if args.only in ("all", "mfma_ceiling"):
         result["mfma_ceiling"] = mfma_ceiling()
         print(f"# sustained MFMA loop: {result['mfma_ceiling']['tflops']} TFLOP/s", file=sys.stderr, flush=True)
+        # the bf16 MFMA-bound rooflines of this run read against the sustained rate as well
+        ceil = result["mfma_ceiling"]["tflops"]
+        against = {}
+        for key, sub in (("step", result), ("fwd", result.get("fwd")), ("gqa_prefill", result.get("gqa_prefill")),
+                         ("varlen", result.get("varlen"))):
+            rl = (sub or {}).get("roofline")
+            if rl and rl.get("bound") == "mfma" and rl.get("peak") == PEAK_BF16_TFLOPS and ceil:
+                against[f"{key}:{rl['kernel']}"] = round(rl["achieved"] / ceil, 4)
+        result["mfma_ceiling"]["dominant_kernels_over_sustained"] = against
     if args.only == "mfma_ceiling":
         r = result["mfma_ceiling"]
         result.update({"value": r["tflops"], "ms_per_step": r["random_operands"]["ms"],
