@@ -22,6 +22,8 @@ min, max).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration          (a plain copy of known size,
                                                     for counter calibration)
+       python bench.py --only coissue              (matrix pipe and vector ALU shared
+                                                    by two wavefronts of one SIMD)
        python bench.py --only mfma_ceiling         (the chip's sustained bf16 MFMA
                                                     rate on an MFMA-only loop)
        python bench.py --summarize-counters WORKLOAD FETCH_DIR WRITE_DIR
@@ -561,6 +563,50 @@ def mfma_ceiling(reps: int = 5) -> dict:
     return res
 
 
+def coissue(nit: int = 512) -> dict:
+    """How one SIMD shares its matrix pipe and vector ALU between two
+    wavefronts (libcalib.so calib_coissue, one workgroup of 8 wavefronts per
+    CU, shader-clock cycles per wavefront, medians over the chip): the
+    forward's matrix stream (one MFMA per KB of LDS operand reads) alone and
+    beside a softmax-shaped vector stream on the same SIMD, and the vector
+    stream alone with one and with two wavefronts per SIMD, and the matrix
+    stream on both wavefronts of every SIMD (both reading LDS)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_38_amd", "libcalib.so"))
+    lib.calib_coissue.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.calib_coissue.restype = ctypes.c_int
+    blocks = 256
+    cyc = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ideal = nit * 64 * 32                         # 64 MFMAs of 32 cycles per round
+    scores = 96 * nit                             # per vector wavefront (lane)
+    res = {}
+    for mode in range(5):
+        for warm in (True, False):
+            st = lib.calib_coissue(cyc.data_ptr(), out.data_ptr(), blocks, max(1, nit // 8) if warm else nit, mode,
+                                   stream.cuda_stream)
+            stream.synchronize()
+            if st != 0:
+                raise RuntimeError(f"calib_coissue failed with status {st}")
+        c = cyc.view(blocks, 8).cpu()
+        mat = sorted(c[:, :4].flatten().tolist()) if mode <= 1 else sorted(c.flatten().tolist()) if mode == 4 else []
+        vec = sorted(c[:, 4:].flatten().tolist() if mode in (1, 2) else c.flatten().tolist()) if 1 <= mode <= 3 else []
+        r = {}
+        if mat:                                   # mode 4: two matrix wavefronts share each pipe
+            r["matrix_pipe_frac"] = round(ideal * (2 if mode == 4 else 1) / mat[len(mat) // 2], 4)
+        if vec:
+            r["vector_cycles_per_score"] = round(vec[len(vec) // 2] / scores, 2)
+        res[("matrix_alone", "matrix_with_vector", "vector_one_wave_per_simd", "vector_two_waves_per_simd",
+             "matrix_two_waves_per_simd")[mode]] = r
+    res["note"] = ("matrix stream: per MFMA pair one ds_read_b128 K fragment and two ds_read_b64_tr_b16 V halves, "
+                   "two pairs ahead; vector stream per score: fma, exp2, sum-tree add, half a bf16 pack, fma; "
+                   "32 cycles per 32x32x16 bf16 MFMA at the published peak")
+    return res
+
+
 def _read_counter_csv(d: str):
     rows = []
     for p in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
@@ -766,7 +812,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "step", "step_fused", "fwd", "decode", "varlen", "fp8", "fp8_decode", "f32",
-                                       "d64", "gqa_prefill", "mfma_ceiling"], default="all")
+                                       "d64", "gqa_prefill", "mfma_ceiling", "coissue"], default="all")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
                     help="WORKLOAD TITLE DIR [DIR ...]")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -866,6 +912,11 @@ def main() -> int:
             if rl and rl.get("bound") == "mfma" and rl.get("peak") == PEAK_BF16_TFLOPS and ceil:
                 against[f"{key}:{rl['kernel']}"] = round(rl["achieved"] / ceil, 4)
         result["mfma_ceiling"]["dominant_kernels_over_sustained"] = against
+    if args.only == "coissue":
+        result["coissue"] = coissue()
+        r = result["coissue"]
+        result.update({"value": r["matrix_with_vector"]["matrix_pipe_frac"], "unit": "fraction", "ms_per_step": None,
+                       "config": {"workload": "coissue"}})
     if args.only == "mfma_ceiling":
         r = result["mfma_ceiling"]
         result.update({"value": r["tflops"], "ms_per_step": r["random_operands"]["ms"],

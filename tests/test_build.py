@@ -30,13 +30,15 @@ def test_only_listed_kernels_may_spill():
 
 
 def test_calibration_library_is_separate_and_exports_its_entry():
-    """The benchmark's MFMA calibration kernel lives in its own library, so
-    libattn.so exports only the attention entry points."""
+    """The benchmark's calibration kernels (MFMA ceiling, matrix/vector
+    co-issue) live in their own library, so libattn.so exports only the
+    attention entry points."""
     import ctypes
     import os
     import subprocess
     assert os.path.exists(build.CALIB_LIB), "run __graft_entry__.build() first"
     lib = ctypes.CDLL(build.CALIB_LIB)
-    assert hasattr(lib, "calib_mfma_bf16")
+    for name in ("calib_mfma_bf16", "calib_coissue"):
+        assert hasattr(lib, name)
     syms = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True).stdout
-    assert "calib_mfma_bf16" not in syms
+    assert "calib_" not in syms
