@@ -25,6 +25,11 @@
 //  * the ring has 8 stages and the DMA runs three tiles ahead, so the
 //    workgroup needs a barrier only every other step (the barrier held the
 //    eight wavefronts in lockstep around the softmax; halving it saves 3 %);
+//  * the main loop is compiled once per phase, so that each phase keeps its
+//    scores in the registers its MFMAs write: with one loop for both, every
+//    step copied the 32 score registers after the MFMAs (16 v_mov_b64), and
+//    this kernel is bound by its vector instruction issue (11 % faster
+//    without the copies, bit-identical output);
 //  * operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured with an
 //    in-bounds probe of the builtin): lane l holds row (A) or column (B)
 //    l % 32; its operand bytes 0..15 lie in k-block 0 (k 0..31), bytes 16..31
@@ -348,46 +353,52 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
     if (scale_dma) asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
   };
-  auto full = [&](auto pos_, int j) __attribute__((always_inline)) {
-    if constexpr (decltype(pos_)::value % 2 == 0) sync();
-    if (phase_b) softmax(j - 1);
-    mma(pos_, T_{}, T_{}, j);
-    if (!phase_b) softmax(j);
-  };
+  // one copy of the loop per phase (see the header)
+  auto run = [&](auto pb_) __attribute__((always_inline)) {
+    constexpr bool PB = decltype(pb_)::value;
+    auto full = [&](auto pos_, int j) __attribute__((always_inline)) {
+      if constexpr (decltype(pos_)::value % 2 == 0) sync();
+      if constexpr (PB) softmax(j - 1);
+      mma(pos_, T_{}, T_{}, j);
+      if constexpr (!PB) softmax(j);
+    };
 
-  if (ntiles > 0) {
-    const Dma d0 = dma_for(0), d1 = dma_for(1), d2 = dma_for(2);
-    static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I0{}, qi, d0); });
-    static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I1{}, qi, d1); });
-    static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I2{}, qi, d2); });
-    sync();
-    mma(I0{}, T_{}, F_{}, 0);
-    if (!phase_b) softmax(0);
-  }
-  int j = 1;
-  for (; j + 7 < ntiles; j += 8) {
-    static_for<8>([&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      full(std::integral_constant<int, (k + 1) % 8>{}, j + k);
-    });
-  }
-  static_for<7>([&](auto kc) __attribute__((always_inline)) {
-    constexpr int k = decltype(kc)::value;
-    if (j + k < ntiles) full(std::integral_constant<int, k + 1>{}, j + k);
-  });
-  if (ntiles > 0) {
-    if (phase_b) softmax(ntiles - 1);
-    switch (ntiles & 7) {
-      case 0: mma(I0{}, F_{}, T_{}, ntiles); break;
-      case 1: mma(I1{}, F_{}, T_{}, ntiles); break;
-      case 2: mma(I2{}, F_{}, T_{}, ntiles); break;
-      case 3: mma(I3{}, F_{}, T_{}, ntiles); break;
-      case 4: mma(std::integral_constant<int, 4>{}, F_{}, T_{}, ntiles); break;
-      case 5: mma(std::integral_constant<int, 5>{}, F_{}, T_{}, ntiles); break;
-      case 6: mma(std::integral_constant<int, 6>{}, F_{}, T_{}, ntiles); break;
-      default: mma(std::integral_constant<int, 7>{}, F_{}, T_{}, ntiles); break;
+    if (ntiles > 0) {
+      const Dma d0 = dma_for(0), d1 = dma_for(1), d2 = dma_for(2);
+      static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I0{}, qi, d0); });
+      static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I1{}, qi, d1); });
+      static_for<3>([&](auto qi) __attribute__((always_inline)) { issue_one(I2{}, qi, d2); });
+      sync();
+      mma(I0{}, T_{}, F_{}, 0);
+      if constexpr (!PB) softmax(0);
     }
-  }
+    int j = 1;
+    for (; j + 7 < ntiles; j += 8) {
+      static_for<8>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        full(std::integral_constant<int, (k + 1) % 8>{}, j + k);
+      });
+    }
+    static_for<7>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      if (j + k < ntiles) full(std::integral_constant<int, k + 1>{}, j + k);
+    });
+    if (ntiles > 0) {
+      if constexpr (PB) softmax(ntiles - 1);
+      switch (ntiles & 7) {
+        case 0: mma(I0{}, F_{}, T_{}, ntiles); break;
+        case 1: mma(I1{}, F_{}, T_{}, ntiles); break;
+        case 2: mma(I2{}, F_{}, T_{}, ntiles); break;
+        case 3: mma(I3{}, F_{}, T_{}, ntiles); break;
+        case 4: mma(std::integral_constant<int, 4>{}, F_{}, T_{}, ntiles); break;
+        case 5: mma(std::integral_constant<int, 5>{}, F_{}, T_{}, ntiles); break;
+        case 6: mma(std::integral_constant<int, 6>{}, F_{}, T_{}, ntiles); break;
+        default: mma(std::integral_constant<int, 7>{}, F_{}, T_{}, ntiles); break;
+      }
+    }
+  };
+  if (phase_b) run(T_{});
+  else run(F_{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float lt = sum_halves(lsum);
