@@ -53,10 +53,9 @@ KERNEL_ONLY = ["-fno-honor-nans"]
 # reason; every other kernel must compile without any. Names are the mangled
 # symbols' distinctive parts.
 SCRATCH_ALLOWED = {
-    # d = 128 prefill with dropout or packed-sequence table: a few values live
-    # across the main loop are stored once before it and reloaded once after
+    # d = 128 prefill with dropout: two values live across the main loop are
+    # stored once before it and reloaded once after
     "fwd_prefill_kernelILi128ENS_7NoTableELb1E": "dropout variant, spill outside the main loop",
-    "fwd_prefill_kernelILi128ENS_8SeqTableELb0E": "packed variant, spill outside the main loop",
 }
 RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
 

@@ -167,6 +167,9 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   // the two phases take alternating 32-row blocks, which keeps their causal work equal
   const int slot = (wid & 3) * 2 + (wid >> 2);
   const int head = hkv * a.g + hgrp * a.hw + slot % a.hw;
+  // (batch, query head) index, wave-uniform: one scalar register carries it
+  // from the Q load to the epilogue
+  const int bh = __builtin_amdgcn_readfirstlane(b * a.Hq + head);
   const int p0 = ptile * a.rows_per_wg + 32 * (slot / a.hw);
   const int pos = p0 + l32;
   const bool colv = pos < a.Sq;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
 
   bf16x8 qf[DC];
   {
-    const bf16* qp = a.q + (((size_t)b * a.Hq + head) * a.hsq + (colv ? pos : 0)) * D;
+    const bf16* qp = a.q + ((size_t)bh * a.hsq + (colv ? pos : 0)) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = colv ? *(const bf16x8*)(qp + 16 * dc + 8 * hi) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -353,11 +356,10 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
       lsum += tree_sum32(v);
       // values 4g .. 4g+3 are keys 4 j4 .. 4 j4 + 3 of this lane's query row:
       // word (pos & 3) of block (pos / 4, j4)
-      const uint32_t bh = (uint32_t)(b * a.Hq + head);
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const uint32_t j4 = (uint32_t)(key0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * hi) >> 2;
-        const u32x4 x = dropout_block(a.drop, (uint32_t)pos >> 2, j4, bh);
+        const u32x4 x = dropout_block(a.drop, (uint32_t)pos >> 2, j4, (uint32_t)bh);
         const int w = pos & 3;
         const uint32_t word = w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3];
 #pragma unroll
@@ -407,11 +409,11 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory"); };
   // Wavefronts whose rows see no key of a tile still run it (their scores are
   // all masked, so P = 0): the step sequence is the same for the whole workgroup.
-  // The steps of one wavefront, for its phase pb_: a bool, or at d = 64 a
-  // compile-time constant, so that each phase gets its own copy of the loop
-  // and keeps its scores in the registers its MFMAs write (measured 4 %
-  // faster at d = 64; at d = 128 the two copies no longer fit in the
-  // registers without spills).
+  // The steps of one wavefront for its phase pb_, a compile-time constant:
+  // each phase gets its own copy of the loop and keeps its scores in the
+  // registers its MFMAs write (one loop for both copied them after every
+  // MFMA block; the copies cost 3-5 % at d = 128 and 5-9 % at d = 64, with
+  // bit-identical output).
   auto run = [&](auto pb_) __attribute__((always_inline)) {
     const bool pb = pb_;
     auto full = [&](auto pos_, int j) __attribute__((always_inline)) {
@@ -453,12 +455,8 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
       }
     }
   };
-  if constexpr (D == 64) {
-    if (phase_b) run(T_{});
-    else run(F_{});
-  } else {
-    run(phase_b);
-  }
+  if (phase_b) run(T_{});
+  else run(F_{});
   // no LDS DMA may still be in flight when the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -470,7 +468,8 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int pos_e = p0 + (ln & 31), hi_e = ln >> 5;
   if (pos_e >= a.Sq) return;
-  bf16* op = a.o + (((size_t)b * a.Hq + head) * a.hsq + pos_e) * D;
+  const size_t hbase = (size_t)bh * a.hsq;
+  bf16* op = a.o + (hbase + pos_e) * D;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -482,7 +481,7 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
       r[3] = (bf16)(acc[mb][4 * q4 + 3] * inv);
       *(bf16x4*)(op + 32 * mb + 8 * q4 + 4 * hi_e) = r;
     }
-  if (a.lse != nullptr && hi_e == 0) a.lse[((size_t)b * a.Hq + head) * a.hsq + pos_e] = lse_v;
+  if (a.lse != nullptr && hi_e == 0) a.lse[hbase + pos_e] = lse_v;
 }
 
 // ---------------------------------------------------------------------------
