@@ -170,9 +170,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
       l2 = (l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
       dl = acc;
     }
-    float* blk = a.ld + (head * (a.sqp / BT) + pos / BT) * (2 * BT);
-    blk[pos % BT] = l2;
-    blk[BT + pos % BT] = dl;
+    float* ldb = a.ld + (head * (a.sqp / BT) + pos / BT) * (2 * BT);
+    ldb[pos % BT] = l2;
+    ldb[BT + pos % BT] = dl;
   }
 }
 

@@ -695,7 +695,7 @@ __global__ __launch_bounds__(64) void combine_split_kernel(const float* __restri
   float m = kNegInf;
   for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, part_lse[(size_t)s * rows + row]);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh));
   constexpr int PER = D / 64;
   float accv[PER];
 #pragma unroll
