@@ -29,6 +29,8 @@
 //    tile, which the swizzle keeps free of bank conflicts;
 //  * two wavefronts share each SIMD and run the per-tile steps in opposite
 //    orders so that one's softmax (vector ALU) overlaps the other's MFMAs;
+//    the main loop is compiled once per order, so each keeps its scores in
+//    the registers its MFMAs write;
 //  * exp2 with log2(e) folded into the score scale: one FMA and one v_exp_f32
 //    per score;
 //  * each XCD takes whole heads and starts the longest causal query tiles of
