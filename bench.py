@@ -41,6 +41,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -98,11 +99,22 @@ def kernel_matches(kernel: str, name: str) -> bool:
     return True
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that an
+    edit of comments alone does not mark stored counters as stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel: str) -> str:
+    """Hash of the code (comments and layout ignored) of the files that define
+    a kernel; stored with its counters, which bench reports only while it
+    still matches."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(kernel, []):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

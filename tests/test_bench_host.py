@@ -108,3 +108,15 @@ def test_shader_counter_summary(tmp_path):
     assert "| MFMA busy (%) | 50.0 |" in text
     assert "| TRANS share of VALU instructions (%) | 25.0 |" in text
     assert "| executed MFMA work, bf16 (TFLOP) | 1.0240 |" in text
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """Counters stay valid across comment edits and go stale on code edits."""
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    for f in bench.KERNEL_SOURCES["fwd_f32"]:
+        (tmp_path / f).write_text("int x = 1; // note\n")
+    h0 = bench.source_hash("fwd_f32")
+    (tmp_path / "fwd_f32.hip").write_text("/* a block\n   comment */ int  x = 1;   // another note\n")
+    assert bench.source_hash("fwd_f32") == h0
+    (tmp_path / "fwd_f32.hip").write_text("int x = 2; // note\n")
+    assert bench.source_hash("fwd_f32") != h0
