@@ -195,8 +195,8 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
     for (int dc = 0; dc < DC; ++dc) qf[dc] = settle(qf[dc]);
   }
   const size_t kvh = ((size_t)b * a.Hkv + hkv) * (size_t)a.hsk * D;
-  const bf16* kg = a.k + kvh;
-  const bf16* vg = a.v + kvh;
+  const bf16* kg = wave_uniform(a.k + kvh);
+  const bf16* vg = wave_uniform(a.v + kvh);
 
   // Per-lane LDS read offsets (the ring slot and the constant parts of each
   // fragment's address are immediate offsets of the reads). K: row l32 (+32

@@ -181,10 +181,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Args a) {
     qsc = settle(qsc);
   }
   const size_t kvh = (size_t)b * a.Hkv + hkv;
-  const u8* kg = a.k + kvh * (size_t)a.Sk * D;
-  const u8* ksg = a.ks + kvh * (size_t)a.Sk * NSB;
-  const u8* vtg = a.vt + kvh * (size_t)D * a.Skp;
-  const u8* vsg = a.vs + kvh * (size_t)(a.Skp / F8_BC) * (2 * D);
+  const u8* kg = wave_uniform(a.k + kvh * (size_t)a.Sk * D);
+  const u8* ksg = wave_uniform(a.ks + kvh * (size_t)a.Sk * NSB);
+  const u8* vtg = wave_uniform(a.vt + kvh * (size_t)D * a.Skp);
+  const u8* vsg = wave_uniform(a.vs + kvh * (size_t)(a.Skp / F8_BC) * (2 * D));
 
   // LDS read offsets. K: block c, d-chunk dc, k-block hh (bytes 16 hh .. of
   // the lane's 32): row kappa_c(l32), logical chunk 4 dc + 2 hh + hi. V^T:

@@ -16,6 +16,20 @@ constexpr int TILE_ROWS = 64;        // the backward pads Sq to a multiple of th
 // Buffer resource for raw loads with range checking: a lane whose byte
 // offset is >= num_bytes reads zeros. Word 3 selects the 32-bit data format
 // (format 0 would read zeros everywhere); stride 0 gives a raw buffer.
+// A wave-uniform pointer moved into scalar registers once, so that address
+// arithmetic on it stays scalar (the compiler can keep uniform values in
+// vector registers, and every buffer descriptor built from one then needs a
+// vector add and two readfirstlane per use).
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  // readfirstlane returns int: widen each half as unsigned (a sign-extended
+  // low half would corrupt the high word)
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)((hi << 32) | lo);
+}
+
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t num_bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   u32x4 r;
