@@ -14,7 +14,7 @@
 //                D_i = dO_i . O_i and lse2_i = lse_i * log2(e) (+inf for rows
 //                that see no key and for padding rows, which makes every
 //                rebuilt probability 0), writes them packed per 32 rows for
-//                the next pass, then loops over 32-key tiles, accumulating
+//                the next pass (lse2 and -D), then loops over 32-key tiles, accumulating
 //                dQ^T in registers;
 //  2. bwd_dkdv:  one workgroup per (KV head, 128-key tile); loops over the
 //                query heads that share the KV head and over 32-row query
@@ -94,7 +94,7 @@ struct BwdArgs {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  float* ld;      // [B, Hq, sqp / 32][64]: lse2 of 32 rows, then D of the same rows
+  float* ld;      // [B, Hq, sqp / 32][64]: lse2 of 32 rows, then -D of the same rows
   float* dqacc;   // fused path: [B, Hq, sqp, D] float32 sums of dS K (NULL on the two-kernel path)
   int B, Hq, Hkv, Sq, Sk, g, causal;
   int hsq, hsk;   // head strides in rows (see Problem)
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
     }
     float* ldb = a.ld + (head * (a.sqp / BT) + pos / BT) * (2 * BT);
     ldb[pos % BT] = l2;
-    ldb[BT + pos % BT] = dl;
+    ldb[BT + pos % BT] = -dl;
   }
 }
 
@@ -184,7 +184,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
 //  * the score wavefront (w < 4) computes S = Q K^T and dP = dO V^T (rows =
 //    queries) with K and V held in registers, then P = 2^(S c - lse2) and
 //    dS = P (dP - D), and hands the bf16 fragments of P and dS to its partner
-//    through LDS, one lane to the same lane;
+//    through LDS, one lane to the same lane; without dropout the dP
+//    accumulator starts at -D (stored negated for this), so that it ends as
+//    dP - D and dS is one multiply per score (1 % on the training step);
 //  * the gradient wavefront (w >= 4) accumulates dV^T += dO^T P and
 //    dK^T += Q^T dS (rows = d) one step later, reading dO^T and Q^T with
 //    transposing LDS reads of the row-major tiles the score wavefront used,
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, Tab T) {
 // does its vector work.
 //
 // LDS: a 4-slot ring of [Q | dO] row tiles (tile t loaded at the start of
-// step t-1, read in steps t and t+1) with its lse2/D blocks, and a 2-slot
+// step t-1, read in steps t and t+1) with its lse2/-D blocks, and a 2-slot
 // exchange buffer of P and dS fragments (written in step t, read in step t+1).
 // ---------------------------------------------------------------------------
 // DROP (here and in the dQ kernel): dropout with the forward's mask, so that
@@ -344,15 +346,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
       bf16x8 f[3];
       f[0] = frag(0);
       f[1] = frag(1);
+      // the dP accumulator starts at -D of its rows, so that it ends as dP - D
+      if constexpr (!DROP)
+        dp = __builtin_shufflevector(__builtin_shufflevector(dlv[0], dlv[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                     __builtin_shufflevector(dlv[2], dlv[3], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5,
+                                     6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       static_for<2 * DC>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k + 2 < 2 * DC) f[(k + 2) % 3] = frag(k + 2);
         __builtin_amdgcn_sched_barrier(0);      // keep the reads two MFMAs ahead of their use
         if constexpr (k < 2) {
-          if constexpr (k & 1)
-            mfma_first(dp, f[k % 3], vf[k >> 1]);
-          else
+          if constexpr (k & 1) {
+            if constexpr (DROP)
+              mfma_first(dp, f[k % 3], vf[k >> 1]);
+            else
+              mfma_next(dp, f[k % 3], vf[k >> 1]);
+          } else {
             mfma_first(s, f[k % 3], kf[k >> 1]);
+          }
         } else {
           if constexpr (k & 1)
             mfma_next(dp, f[k % 3], vf[k >> 1]);
@@ -377,10 +388,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Tab T) {
                                (uint32_t)(b * a.Hq + hq));
           const float z = ((dx[v & 3] >> (8 * (key & 3))) & 0xffu) >= a.drop.thr ? a.drop.scale : 0.f;
           p[v] = pv * z;
-          ds[v] = pv * (z * dp[v] - dlv[v >> 2][v & 3]);
+          ds[v] = pv * (z * dp[v] + dlv[v >> 2][v & 3]);
         } else {
           p[v] = pv;
-          ds[v] = pv * (dp[v] - dlv[v >> 2][v & 3]);
+          ds[v] = pv * dp[v];
         }
       }
       char* xs = smem + xw + (POS & 1) * XSLOT;
@@ -748,7 +759,7 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
     // preprocessing pass: D = dO . O over the row's channels (this lane's
     // half, then its partner lane's) and lse2 = lse log2(e), +inf where the
     // row sees no key or lies past Sq (every rebuilt probability is then 0).
-    // They also go to the row's lse2/D block for the dK/dV pass that follows.
+    // They also go to the row's lse2/D block (D negated) for the dK/dV pass that follows.
     float dpart = 0.f, l = kNegInf;
     if (valid[cb]) {
 #pragma unroll
@@ -764,7 +775,7 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
     if (hi == 0 && pos[cb] < a.sqp) {
       float* blk = a.ld + (hrow * (a.sqp / BT) + pos[cb] / BT) * (2 * BT);
       blk[pos[cb] % BT] = l2[cb];
-      blk[BT + pos[cb] % BT] = dl[cb];
+      blk[BT + pos[cb] % BT] = -dl[cb];
     }
   }
 #pragma unroll
