@@ -788,6 +788,13 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
     l2[cb] = settle(l2[cb]);
     dl[cb] = settle(dl[cb]);
   }
+  // without dropout the dP^T accumulators start at -D of the lane's row, so
+  // that they end as dP - D (a register tuple of its own, kept for the kernel)
+  f32x16 ndl[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndl[cb][i] = DROP ? 0.f : -dl[cb];
 
   const size_t kvh = (size_t)b * a.Hkv + hkv;
   const bf16* kg = a.k + kvh * (size_t)a.hsk * D;
@@ -932,7 +939,7 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
             const float z = ((dword[cb] >> (8 * (v & 3))) & 0xffu) >= a.drop.thr ? a.drop.scale : 0.f;
             dt[cb][v & 7] = p * (z * dp_[cb][v] - dl[cb]);
           } else {
-            dt[cb][v & 7] = p * (dp_[cb][v] - dl[cb]);
+            dt[cb][v & 7] = p * dp_[cb][v];
           }
           pin(dt[cb][v & 7]);
           if ((v & 7) == 7) {
@@ -949,7 +956,7 @@ __global__ __launch_bounds__(256, (DQ_NCB == 1 && !DROP) ? 2 : 1) void bwd_dq_ke
         if constexpr (u + 1 < NU) fv[(u + 1) & 1] = vfr(u + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) dp_[cb] = mfma32(fv[u & 1], df[cb][u], u == 0 ? f32x16{} : dp_[cb]);
+        for (int cb = 0; cb < NCB; ++cb) dp_[cb] = mfma32(fv[u & 1], df[cb][u], u == 0 ? (DROP ? f32x16{} : ndl[cb]) : dp_[cb]);
       });
     }
   };
