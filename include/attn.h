@@ -117,7 +117,7 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float
 
 /* Bytes of device workspace attn_bwd needs: the per-row terms D_i = dO_i . O_i
  * and lse_i * log2(e) (float32, 2 * B * Hq * Sq' values with Sq' = Sq rounded
- * up to 64, stored per 32 rows as [lse2 x 32 | D x 32]), rounded up to 256
+ * up to 64, stored per 32 rows as [lse2 x 32 | -D x 32]), rounded up to 256
  * bytes. The contents are scratch: nothing is kept between calls. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                 int causal, int dtype);
