@@ -242,6 +242,29 @@ def test_fwd_fp8_matches_oracle(attn, B, Hq, Hkv, Sq, Sk, causal, seed):
     _say(f"  relative Frobenius error (worst head) {fro:.3e}, lse max err {le:.3e}")
 
 
+def _random_fwd_shapes(n=8, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        Sq = 1 if i % 4 == 2 else int(rng.integers(2, 500))
+        out.append((int(rng.integers(1, 3)), Hkv * g, Hkv, Sq, int(rng.integers(1, 900)), int(rng.integers(0, 3)),
+                    600 + i))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal,seed", _random_fwd_shapes())
+def test_fwd_fp8_random_shapes(attn, B, Hq, Hkv, Sq, Sk, causal, seed):
+    """Seeded random shapes (fixed seed: the same ones every run), prefill and
+    split-key decode, all mask modes, against the oracle's MXFP8 forward."""
+    _say(f"fwd_fp8 random B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} causal={causal}")
+    o, lse, o_ref, lse_ref, tol, ltol = _fwd_case(attn, B, Hq, Hkv, Sq, Sk, causal, seed)
+    fro = _check_fp8_o(o, o_ref, tol)
+    le = _check_fp8_lse(lse, lse_ref, ltol)
+    _say(f"  relative Frobenius error (worst head) {fro:.3e}, lse max err {le:.3e}")
+
+
 def test_fwd_fp8_outlier_rows(attn):
     """Rows scaled x30 push the scores far past exp's range; the per-block
     scales absorb the magnitude and the recurrence stays finite."""
