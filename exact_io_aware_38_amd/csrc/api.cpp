@@ -187,8 +187,11 @@ hipError_t fwd_launch(const attn::Problem& p, int dtype, const void* q, const vo
   }
   const attn::PrefillPlan pl = attn::plan_prefill(p);
   e = attn::launch_fwd_prefill_bf16(p, pl, q, k, v, o, lse, workspace, s);
-  std::snprintf(text, text_n, "fwd_prefill_bf16<d=%d> grid=%d block=512 heads/wg=%d rows/wg=%d key_tile=64 causal=%d",
-                p.d, pl.total_wgs, pl.hw, pl.rows_per_wg, p.causal);
+  const int poly = p.d == 128 ? attn::exp2_poly_every() : 0;
+  std::snprintf(text, text_n,
+                "fwd_prefill_bf16<d=%d> grid=%d block=512 heads/wg=%d rows/wg=%d key_tile=64 causal=%d%s",
+                p.d, pl.total_wgs, pl.hw, pl.rows_per_wg, p.causal,
+                poly == 4 ? " exp2=poly every 4th" : poly == 2 ? " exp2=poly every 2nd" : "");
   return e;
 }
 

@@ -40,6 +40,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // 2^x on the transcendental unit; 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the FMA pipe, the software exponential of "Flash Attention FA1->FA4 /
+// pre-training practice" section 2.3: 2^x = 2^n 2^f, n = floor(x), f in
+// [0, 1), 2^f by a cubic fitted to it on [0, 1) (relative error at most
+// 8.6e-5, below a bf16 rounding step), 2^n by an exponent add. Arguments
+// below -127 give 0, as exp2 does in the range the softmax uses.
+__device__ __forceinline__ float poly_exp2(float x) {
+  x = fmaxf(x, -127.f);
+  const float n = __builtin_floorf(x);
+  const float f = x - n;
+  float p = __builtin_fmaf(f, 0.07706520f, 0.22764701f);
+  p = __builtin_fmaf(f, p, 0.69511634f);
+  p = __builtin_fmaf(f, p, 1.0f);
+  const float r = __builtin_ldexpf(p, (int)n);
+  return x <= -127.f ? 0.f : r;
+}
+
 // max of x over lanes l and l^32.
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -41,6 +41,8 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <type_traits>
 
@@ -127,8 +129,10 @@ __device__ __forceinline__ void rebase(FwdArgs& a, const SeqTable& T, int s) {
 
 // Tab: NoTable for one dense [B, H, S, d] problem, SeqTable for a packed launch.
 // DROP: dropout on the probabilities that multiply V (the denominator counts
-// every visible key, as without dropout).
-template <int D, typename Tab, bool DROP>
+// every visible key, as without dropout). POLY > 0: every POLY-th probability
+// of a lane is formed by poly_exp2 on the FMA pipe instead of v_exp_f32 (an
+// opt-in variant, ATTN_EXP2_POLY; slower on this chip, kept to measure it).
+template <int D, typename Tab, bool DROP, int POLY = 0>
 __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
   using R = Ring<D>;
   constexpr int MB = D / 32;
@@ -449,7 +453,10 @@ __global__ __launch_bounds__(512) void fwd_prefill_kernel(FwdArgs a, Tab T) {
         for (int q = 0; q < 4; ++q) {
           float p[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(v[8 * q + i], a.c, -msub));
+          for (int i = 0; i < 8; ++i) {
+            const float x = __builtin_fmaf(v[8 * q + i], a.c, -msub);
+            p[i] = (POLY > 0 && i % POLY == POLY - 1) ? poly_exp2(x) : fast_exp2(x);
+          }
           g[q] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
           pf[q] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
         }
@@ -812,11 +819,30 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(DropParams dp, unsign
   }
 }
 
+}  // namespace
+
+// ATTN_EXP2_POLY=2 or 4: the dense d = 128 prefill without dropout forms every
+// second or fourth probability with poly_exp2 (read at every call).
+int exp2_poly_every() {
+  const char* e = std::getenv("ATTN_EXP2_POLY");
+  if (e == nullptr) return 0;
+  if (std::strcmp(e, "2") == 0) return 2;
+  if (std::strcmp(e, "4") == 0) return 4;
+  return 0;
+}
+
+namespace {
+
 template <int D>
 hipError_t launch_prefill_d(const FwdArgs& a, hipStream_t s) {
   timing_begin(s, "fwd_prefill_bf16");
+  const int poly = exp2_poly_every();
   if (a.drop.thr != 0)
     hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable, true>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
+  else if (D == 128 && poly == 4)
+    hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable, false, 4>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
+  else if (D == 128 && poly == 2)
+    hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable, false, 2>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
   else
     hipLaunchKernelGGL((fwd_prefill_kernel<D, NoTable, false>), dim3(a.total_wgs), dim3(512), 0, s, a, NoTable{});
   const hipError_t e = hipGetLastError();

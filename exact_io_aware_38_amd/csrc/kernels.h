@@ -37,6 +37,10 @@ struct Problem {
   DropParams drop;
 };
 
+// 0, or 2 / 4 when ATTN_EXP2_POLY asks the dense d = 128 bf16 prefill to form
+// every second / fourth probability with the FMA-pipe exponential.
+int exp2_poly_every();
+
 // keep[B, Hq, Sq, Sk] (1 = kept) of the dropout mask the kernels regenerate.
 hipError_t launch_dropout_mask(const Problem& p, unsigned char* keep, hipStream_t s);
 

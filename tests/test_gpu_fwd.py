@@ -249,3 +249,31 @@ def test_bf16_output_bounds_invariant(attn):
     vmin = f["v"].min(axis=2, keepdims=True)
     vmax = f["v"].max(axis=2, keepdims=True)
     assert (o >= vmin - 1e-2).all() and (o <= vmax + 1e-2).all()
+
+
+@pytest.mark.parametrize("every", ["2", "4"])
+@pytest.mark.parametrize("shape", [(2, 4, 2, 257, 333, 128, 2), (1, 4, 1, 600, 600, 128, 1),
+                                   (1, 2, 2, 300, 700, 128, 0)], ids=lambda s: "x".join(map(str, s)))
+def test_poly_exp2_variant(attn, shape, every, monkeypatch):
+    """The opt-in FMA-pipe exponential (ATTN_EXP2_POLY) in the d = 128 prefill:
+    the same tolerances against the oracle, the dispatch log names it, and its
+    O stays within a bf16 rounding step or two of the v_exp_f32 kernel's."""
+    B, Hq, Hkv, Sq, Sk, d, causal = shape
+    w = synth.Workload("poly_exp2", B, Hq, Hkv, Sq, Sk, d, "bf16", causal, seed=4000 + sum(shape),
+                       outlier_frac=0.02, outlier_scale=30.0)
+    _say("case", shape, "poly every", every)
+    x, dev, f = _inputs(w)
+    o0, lse0 = _run(attn, w, dev)
+    monkeypatch.setenv("ATTN_EXP2_POLY", every)
+    o, lse = _run(attn, w, dev)
+    assert f"exp2=poly every {'2nd' if every == '2' else '4th'}" in attn.last_dispatch()
+    monkeypatch.delenv("ATTN_EXP2_POLY")
+    o_ref, lse_ref = oracle.attention_forward(f["q"], f["k"], f["v"], causal=causal, scale=w.scale)
+    check_o(o, o_ref, "bf16")
+    check_lse(lse, lse_ref)
+    fin = np.isfinite(lse0)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse - lse0)[fin].max() <= 1e-4
+    assert np.abs(o - o0).max() <= 2 ** -6 * max(1.0, np.abs(o0).max())
+    _run(attn, w, dev)
+    assert "exp2=poly" not in attn.last_dispatch()
